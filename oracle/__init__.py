@@ -1,0 +1,16 @@
+"""Float64 CPU oracle for differential attention -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library.
+"""
+
+from .diffattn_oracle import (  # noqa: F401
+    diff_attention,
+    diff_attention_decode,
+    diff_attention_rows,
+    head_rmsnorm,
+    lambda_init_schedule,
+    reparam_lambda,
+    score_maps,
+    signed_map,
+)

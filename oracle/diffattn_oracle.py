@@ -1,0 +1,249 @@
+"""Float64 CPU oracle for multi-head differential attention (forward only).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+in ``__graft_entry__.smoke`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call anything in this package.  The GPU path never routes through
+it, and it shares no code, tables or helpers with the HIP library.
+
+What it computes is the plain definition, written out step by step in float64,
+with every attention map materialised row by row (no streaming softmax, no
+tiling of the key axis, no fusion):
+
+    S1 = Q1 K1^T / sqrt(D) + M,   S2 = Q2 K2^T / sqrt(D) + M
+    A1 = softmax_rows(S1),        A2 = softmax_rows(S2)
+    O  = (A1 - lam * A2) V
+
+  - paperleet "Differential Transformer Attention", the displayed equation for
+    A1, A2 and O, and the sentence defining the causal mask M (0 on allowed
+    keys, -inf on future keys, applied to both branches, softmax over keys).
+  - aifetchly "Differential Transformer: Canceling LLM Attention Noise",
+    section 1 (DiffAttn formulation) and the numerically stable softmax of its
+    "Step 1" code (subtract the row maximum, exponentiate, divide by the sum).
+
+lam = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init
+  - aifetchly page, section 3 (re-parameterisation of lambda); paperleet page,
+    the scalar parameterisation equation and "Formula and conventions".
+
+lambda_init(l) = 0.8 - 0.6 exp(-0.3 (l - 1)), layers counted from 1
+  - aifetchly page, section 3; paperleet page, "Formula and conventions".
+
+Optional per-head norm: RMS over the 2D output channels of each token, then a
+constant x (1 - lambda_init).
+  - aifetchly page, section 4 (per-head normalisation, then the (1 - lambda_init)
+    multiplier); the French lesson page, "Le problème" and "V1 contre V2", names
+    the per-head norm of V1 as RMSNorm.  Reading taken: RMSNorm without mean
+    subtraction and without an affine weight (identity at initialisation), with
+    an explicit eps, and the (1 - lambda_init) factor applied only together
+    with the norm (the paperleet page returns the aggregate *before* the norm
+    and its fixed multiplier).
+
+Decode: one query row per (batch, head) against all L cached keys, no mask;
+the same steps as above with T_q = 1.
+
+Readings where the pages are loose (all recorded in the design notes):
+  - softmax scale is 1/sqrt(D) with D the width of Q1/K1 (not 2D);
+  - lambda is not clamped and may be negative or exceed 1;
+  - lambda may differ per head (the French page: "par tête"); a per-layer
+    scalar is the case of all heads equal.
+
+Query rows may be processed in blocks purely to bound memory; every row's
+two score rows and softmax rows are materialised whole, so blocking changes no
+arithmetic.
+
+Pins: every function here is pinned by tests that do not re-type its formula
+(see ``tests/test_oracle_pins.py``): the page's printed worked example, the
+lambda = 0 reduction to a library attention routine, cancellation of identical
+maps at lambda = 1, row sums of 1 - lambda, the exact (1 - lambda) response to a
+value offset, the causal first row, the lambda_init values, a library RMS norm,
+and an independent pure-Python scalar implementation on tiny inputs.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "lambda_init_schedule",
+    "reparam_lambda",
+    "score_maps",
+    "signed_map",
+    "diff_attention",
+    "diff_attention_rows",
+    "head_rmsnorm",
+    "diff_attention_decode",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast of a numpy array or torch tensor (fp32/bf16) to float64."""
+    if hasattr(x, "detach"):  # torch tensor: go through float32 (exact for bf16)
+        x = x.detach().to("cpu")
+        if str(x.dtype) == "torch.bfloat16":
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def lambda_init_schedule(layer: int) -> float:
+    """lambda_init(l) = 0.8 - 0.6 exp(-0.3 (l - 1)), l = 1, 2, ...
+
+    aifetchly page, section 3 (depth-dependent initialisation); paperleet page,
+    "Formula and conventions" (layers start at 1).
+    """
+    if layer < 1:
+        raise ValueError("layers are counted from 1")
+    return 0.8 - 0.6 * math.exp(-0.3 * (layer - 1))
+
+
+def reparam_lambda(lq1, lk1, lq2, lk2, lambda_init: float) -> np.ndarray:
+    """lam = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init, in float64.
+
+    aifetchly page, section 3; paperleet page, scalar parameterisation.
+    Vectors of shape [Dl] give a 0-d result; shape [H, Dl] gives one lambda per
+    head (the French page: lambda is a learnable scalar per head).
+    """
+    a, b, c, d = (_f64(t) for t in (lq1, lk1, lq2, lk2))
+    dot1 = np.sum(a * b, axis=-1)
+    dot2 = np.sum(c * d, axis=-1)
+    return np.exp(dot1) - np.exp(dot2) + float(lambda_init)
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax over the last axis: subtract the row max, exp, normalise.
+
+    aifetchly page, "Step 1" (stable softmax); the French page, "Étape 1".
+    Entries equal to -inf (masked keys) become exactly 0.
+    """
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _scores(q: np.ndarray, k: np.ndarray, rows: np.ndarray | None, causal: bool) -> np.ndarray:
+    """S = Q K^T / sqrt(D) for the given query rows, with the causal mask.
+
+    paperleet page: scaled scores, M = -inf on keys j > i (future positions).
+    q: [Tq_all, D], k: [Tk, D]; rows: indices into q (None = all rows, which are
+    then positions 0..Tq-1).
+    """
+    d = q.shape[-1]
+    if rows is None:
+        rows = np.arange(q.shape[0])
+    s = (q[rows] @ k.T) / math.sqrt(d)
+    if causal:
+        keys = np.arange(k.shape[0])
+        s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+    return s
+
+
+def score_maps(q1, k1, q2, k2, causal: bool):
+    """Return the two materialised softmax maps A1, A2 (float64).
+
+    Shapes: q*, k* are [..., T, D]; returns [..., T, T] each.  Only meant for
+    small T (the maps are T x T).
+    """
+    q1, k1, q2, k2 = (_f64(t) for t in (q1, k1, q2, k2))
+    lead = q1.shape[:-2]
+    t = q1.shape[-2]
+    a1 = np.empty(lead + (t, k1.shape[-2]))
+    a2 = np.empty_like(a1)
+    for idx in np.ndindex(*lead):
+        a1[idx] = _softmax_rows(_scores(q1[idx], k1[idx], None, causal))
+        a2[idx] = _softmax_rows(_scores(q2[idx], k2[idx], None, causal))
+    return a1, a2
+
+
+def signed_map(a1: np.ndarray, a2: np.ndarray, lam) -> np.ndarray:
+    """A = A1 - lam * A2 (paperleet page equation for O; aifetchly section 2).
+
+    ``lam`` broadcasts over the leading axes: a scalar, or one value per head
+    for maps shaped [B, H, T, T].
+    """
+    lam = _f64(lam)
+    if lam.ndim == 1:
+        lam = lam[:, None, None]
+    return a1 - lam * a2
+
+
+def _lam_per_head(lam, h: int) -> np.ndarray:
+    lam = _f64(lam)
+    if lam.ndim == 0:
+        return np.full(h, float(lam))
+    if lam.shape != (h,):
+        raise ValueError(f"lambda must be a scalar or have shape [{h}]")
+    return lam
+
+
+def diff_attention_rows(q1, k1, q2, k2, v, lam, causal: bool, rows, row_block: int = 512):
+    """O rows (A1 - lam A2) V for the selected query rows of one (b, h) slice.
+
+    q*, k*: [T, D]; v: [T, 2D]; lam: python/0-d scalar; rows: 1-D int array of
+    query positions.  Returns [len(rows), 2D] float64.  Each selected row's two
+    score rows over all keys are materialised whole; ``row_block`` only bounds
+    how many rows are held at once.
+    """
+    q1, k1, q2, k2, v = (_f64(t) for t in (q1, k1, q2, k2, v))
+    lam = float(_f64(lam))
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], v.shape[-1]))
+    for s in range(0, rows.shape[0], row_block):
+        r = rows[s:s + row_block]
+        a1 = _softmax_rows(_scores(q1, k1, r, causal))
+        a2 = _softmax_rows(_scores(q2, k2, r, causal))
+        out[s:s + row_block] = (a1 - lam * a2) @ v
+    return out
+
+
+def diff_attention(q1, k1, q2, k2, v, lam, causal: bool = True, row_block: int = 512):
+    """O = (softmax(Q1K1^T/sqrt(D)+M) - lam softmax(Q2K2^T/sqrt(D)+M)) V.
+
+    paperleet page: q*, k* are [B, H, T, D], v is [B, H, T, 2D], result
+    [B, H, T, 2D] (the value aggregate before any head normalisation).
+    ``lam`` is a scalar or one value per head [H].  float64 result.
+    """
+    q1, k1, q2, k2, v = (_f64(t) for t in (q1, k1, q2, k2, v))
+    b, h, t, _ = q1.shape
+    lam_h = _lam_per_head(lam, h)
+    out = np.empty((b, h, t, v.shape[-1]))
+    rows = np.arange(t)
+    for bi in range(b):
+        for hi in range(h):
+            out[bi, hi] = diff_attention_rows(
+                q1[bi, hi], k1[bi, hi], q2[bi, hi], k2[bi, hi], v[bi, hi],
+                lam_h[hi], causal, rows, row_block)
+    return out
+
+
+def head_rmsnorm(o, lambda_init: float, eps: float) -> np.ndarray:
+    """Y_t = O_t / sqrt(mean_c O_t,c^2 + eps) * (1 - lambda_init).
+
+    Per token, over the 2D channels of one head (aifetchly page, section 4:
+    normalise each head separately, then the constant (1 - lambda_init)
+    multiplier; the French page names V1's per-head norm as RMSNorm).
+    """
+    o = _f64(o)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    return o / np.sqrt(ms + float(eps)) * (1.0 - float(lambda_init))
+
+
+def diff_attention_decode(q1, k1, q2, k2, v, lam):
+    """Decode: one query per (b, h) against all L cached keys, no mask.
+
+    q*: [B, H, D]; k*: [B, H, L, D]; v: [B, H, L, 2D]; lam scalar or [H].
+    Returns [B, H, 2D] float64.  Same definition as ``diff_attention`` with a
+    single query row that sees every cached key (the French page, "V1 contre
+    V2": decoding reads the value cache; one read of V serves both maps).
+    """
+    q1, q2 = _f64(q1), _f64(q2)
+    b, h, _ = q1.shape
+    lam_h = _lam_per_head(lam, h)
+    out = np.empty((b, h, v.shape[-1]))
+    for bi in range(b):
+        for hi in range(h):
+            k1s, k2s, vs = _f64(k1[bi, hi]), _f64(k2[bi, hi]), _f64(v[bi, hi])
+            out[bi, hi] = diff_attention_rows(
+                q1[bi, hi][None, :], k1s, q2[bi, hi][None, :], k2s, vs,
+                lam_h[hi], False, np.array([0]))[0]
+    return out

@@ -1,0 +1,183 @@
+"""Checks that pin the float64 oracle to facts outside itself.
+
+Each ``check_*`` raises AssertionError on failure.  They are run as tests on
+the real oracle (``test_oracle_pins.py``) and against deliberately broken
+copies of it (``test_oracle_mutants.py``), which shows that a plausible mistake
+anywhere in the oracle trips at least one of them.
+
+What pins what:
+  worked example   the glossary page's printed output: with its seed-0 inputs
+                   (n=6, d=8, lambda=0.8, no mask) row 0 of the signed map sums
+                   to 0.20 and 13 of 36 weights are negative -> scores, scale,
+                   softmax, sign of lambda
+  library attn     lambda = 0 is ordinary attention (paperleet page), and by
+                   linearity O = SDPA(Q1,K1,V) - lam SDPA(Q2,K2,V) for every
+                   lambda; torch's float64 scaled_dot_product_attention is the
+                   library routine -> scale, mask, operand order, V width 2D
+  cancellation     identical maps cancel exactly at lambda = 1 (paperleet page)
+  row sums         each signed-map row sums to 1 - lambda (paperleet page;
+                   glossary page)
+  value offset     a value offset shared by every token comes out as exactly
+                   (1 - lambda) times the offset (paperleet page, toy
+                   experiment)
+  first row        under the causal mask row 0 sees only key 0: O_0 = (1-lam) V_0
+  lambda           zero vectors give lambda_init (vectors start at zero,
+                   aifetchly section 3); a closed form with exp(ln 2) = 2
+  lambda_init      l = 1 gives 0.2 and deep layers approach 0.8 (aifetchly
+                   section 3), increasing in l
+  head norm        torch.nn.functional.rms_norm (no weight), times
+                   (1 - lambda_init)
+  brute force      an independent pure-Python scalar implementation on T <= 8
+  decode           one query against the cache equals the last row of the
+                   causal forward (that row sees every key)
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float64)
+
+
+def _case(b, h, t, d, seed):
+    return [_rand((b, h, t, d), seed + i) for i in range(4)] + [_rand((b, h, t, 2 * d), seed + 9)]
+
+
+def check_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example_glossary.json")) as f:
+        gold = json.load(f)
+    rec = gold["recipe"]
+    torch.manual_seed(0)
+    n, d = rec["n_tokens"], rec["head_width_d"]
+    q1, k1, q2, k2 = torch.randn(4, n, d)
+    torch.randn(n, 2 * d)  # v: drawn by the recipe; not needed for the maps
+    a1, a2 = oracle.score_maps(q1, k1, q2, k2, causal=False)
+    a = oracle.signed_map(a1, a2, rec["lambda"])
+    printed = gold["printed"]
+    assert f"{a[0].sum():.2f}" == printed["row0_sum_2dp"], a[0].sum()
+    assert int((a < 0).sum()) == printed["negative_weights"], int((a < 0).sum())
+    assert a.size == printed["total_weights"]
+
+
+def _sdpa(q, k, v, causal):
+    return F.scaled_dot_product_attention(q, k, v, is_causal=causal).numpy()
+
+
+def check_library_attention():
+    for causal in (True, False):
+        q1, k1, q2, k2, v = _case(2, 3, 37, 16, seed=11)
+        ref1 = _sdpa(q1, k1, v, causal)
+        ref2 = _sdpa(q2, k2, v, causal)
+        o0 = oracle.diff_attention(q1, k1, q2, k2, v, 0.0, causal)
+        assert np.max(np.abs(o0 - ref1)) < 1e-12
+        lam = np.array([-0.3, 0.8, 1.5])
+        o = oracle.diff_attention(q1, k1, q2, k2, v, lam, causal)
+        ref = ref1 - lam[None, :, None, None] * ref2
+        assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def check_cancellation():
+    q1, k1, _, _, v = _case(1, 2, 23, 8, seed=21)
+    for causal in (True, False):
+        o = oracle.diff_attention(q1, k1, q1, k1, v, 1.0, causal)
+        assert np.all(o == 0.0)
+
+
+def check_row_sums():
+    q1, k1, q2, k2, _ = _case(2, 2, 19, 8, seed=31)
+    lam = np.array([0.35, -0.4])
+    for causal in (True, False):
+        a1, a2 = oracle.score_maps(q1, k1, q2, k2, causal)
+        a = oracle.signed_map(a1, a2, lam)
+        sums = a.sum(-1)
+        assert np.max(np.abs(sums - (1.0 - lam)[None, :, None])) < 1e-13
+        if causal:  # future keys carry no weight in either map
+            upper = np.triu(np.ones((19, 19), dtype=bool), 1)
+            assert np.all(a1[..., upper] == 0) and np.all(a2[..., upper] == 0)
+
+
+def check_value_offset():
+    q1, k1, q2, k2, v = _case(1, 2, 4, 8, seed=41)
+    c = _rand((16,), 42)
+    for lam in (0.0, 0.25, 0.5, 1.0):
+        for causal in (True, False):
+            base = oracle.diff_attention(q1, k1, q2, k2, v, lam, causal)
+            shifted = oracle.diff_attention(q1, k1, q2, k2, v + c, lam, causal)
+            assert np.max(np.abs(shifted - base - (1.0 - lam) * c.numpy())) < 1e-12
+
+
+def check_first_row():
+    q1, k1, q2, k2, v = _case(1, 2, 9, 8, seed=51)
+    lam = 0.7
+    o = oracle.diff_attention(q1, k1, q2, k2, v, lam, causal=True)
+    assert np.max(np.abs(o[:, :, 0, :] - (1.0 - lam) * v[:, :, 0, :].numpy())) < 1e-15
+
+
+def check_lambda():
+    z = np.zeros((3, 5))
+    li = 0.6123
+    lam = oracle.reparam_lambda(z, z, z, z, li)
+    assert lam.shape == (3,) and np.all(lam == li)
+    one = np.zeros(4)
+    one[2] = 1.0
+    ln2 = np.zeros(4)
+    ln2[2] = math.log(2.0)
+    lam = oracle.reparam_lambda(ln2, one, 0.5 * one, np.zeros(4), 0.3)
+    assert np.ndim(lam) == 0 and abs(float(lam) - (2.0 - 1.0 + 0.3)) < 1e-15
+    lam = oracle.reparam_lambda(np.zeros(4), np.zeros(4), ln2, one, 0.3)
+    assert abs(float(lam) - (1.0 - 2.0 + 0.3)) < 1e-15
+
+
+def check_lambda_init():
+    assert abs(oracle.lambda_init_schedule(1) - 0.2) < 1e-15
+    vals = [oracle.lambda_init_schedule(l) for l in range(1, 200)]
+    assert all(b > a for a, b in zip(vals[:60], vals[1:60]))
+    assert all(b >= a for a, b in zip(vals, vals[1:]))
+    assert abs(vals[-1] - 0.8) < 1e-12
+
+
+def check_head_norm():
+    o = _rand((2, 3, 7, 32), 61) * 0.01
+    for li, eps in ((0.2, 1e-5), (0.8, 1e-6)):
+        y = oracle.head_rmsnorm(o, li, eps)
+        ref = F.rms_norm(o, (32,), eps=eps).numpy() * (1.0 - li)
+        assert np.max(np.abs(y - ref)) < 1e-12
+
+
+def check_brute_force():
+    for t, causal, seed in ((1, True, 71), (5, True, 72), (8, False, 73), (7, False, 74)):
+        q1, k1, q2, k2, v = _case(1, 2, t, 4, seed)
+        lam = np.array([0.42, 1.3])
+        o = oracle.diff_attention(q1, k1, q2, k2, v, lam, causal)
+        for h in range(2):
+            ref = brute.diff_attention_head(
+                q1[0, h].tolist(), k1[0, h].tolist(), q2[0, h].tolist(), k2[0, h].tolist(),
+                v[0, h].tolist(), float(lam[h]), causal)
+            assert np.max(np.abs(o[0, h] - np.array(ref))) < 1e-12
+
+
+def check_decode():
+    q1, k1, q2, k2, v = _case(2, 3, 33, 8, seed=81)
+    lam = np.array([0.1, 0.5, 0.9])
+    full = oracle.diff_attention(q1, k1, q2, k2, v, lam, causal=True)
+    dec = oracle.diff_attention_decode(q1[:, :, -1], k1, q2[:, :, -1], k2, v, lam)
+    assert np.max(np.abs(dec - full[:, :, -1])) < 1e-13
+
+
+ALL_CHECKS = [
+    check_worked_example, check_library_attention, check_cancellation, check_row_sums,
+    check_value_offset, check_first_row, check_lambda, check_lambda_init, check_head_norm,
+    check_brute_force, check_decode,
+]
