@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of the differential-attention forward on one MI355X.
+
+One "step" is one pass of the path over one batch of synthetic input that is
+already resident in HBM:
+  prefill workloads   lambda kernel (when the workload derives lambda from its
+                      four vectors) + the prefill forward kernel
+  decode workload     lambda kernel + split-K partial kernel + reduce kernel
+
+The printed JSON line reports the primary workload (default: the causal T=4096
+bf16 prefill, B2 H16 D64, head norm on) as TFLOP/s counted as
+8 * T_eff * T * D * B * H per forward (T_eff = (T+1)/2 causal, T full), and
+the other workloads (causal T=32768, full T=8192 D=128, decode L=65536) under
+"also".  "roofline" gives the dominant kernel's algorithmic rate (from HIP
+events around each launch on the launch stream) against the MI355X peak
+(bf16 dense MFMA 2.5 PFLOP/s, fp32 MFMA 157.3 TFLOP/s, HBM 8 TB/s).
+"cpu_baseline" times the float64 oracle on the host cores on a bounded sample
+of the primary workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DiffAttn fwd TFLOP/s (bf16 causal T=4k/32k) & % MFMA peak; decode HBM GB/s"
+PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
+PRIMARY = "prefill_t4k_causal"
+OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k"]
+CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
+KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip"}
+KERNEL_NAME = {"prefill": "fwd_kernel", "decode": "decode_partial_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for f in (KERNEL_FILE[kind], "common.h", "kernels.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{KERNEL_NAME[kind]}:{workload}")
+    if not rec or rec.get("source_hash") != source_hash(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def prefill_flops(w):
+    t_eff = (w.T + 1) / 2.0 if w.causal else float(w.T)
+    return 8.0 * t_eff * w.T * w.D * w.B * w.H
+
+
+def decode_bytes(w):
+    es = 2 if w.dtype == "bf16" else 4
+    return float(w.B * w.H * w.T * 4 * w.D * es)
+
+
+def time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_kernel(torch, launch, steps):
+    """Average duration of one launch, from events recorded around each launch
+    on the current (launch) stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        launch()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def bench_workload(torch, da, name, steps, warmup):
+    from workloads import WORKLOADS, make_workload
+
+    w = WORKLOADS[name]
+    log(f"[bench] {name}: generating inputs")
+    x = make_workload(name, "cuda")
+    torch.cuda.synchronize()
+    li = w.lambda_init if w.lambda_init is not None else da.diffattn_lambda_init(w.layer)
+    lam = x.get("lam")
+    lam_buf = torch.empty(w.H, device="cuda", dtype=torch.float32)
+    if w.kind == "prefill":
+        out = torch.empty_like(x["v"])
+
+        def kernel():
+            da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"],
+                            lam if lam is not None else lam_buf, causal=w.causal,
+                            headnorm=w.headnorm, lambda_init=li, eps=w.eps, out=out)
+    else:
+        out = torch.empty((w.B, w.H, 2 * w.D), device="cuda", dtype=x["v"].dtype)
+        ws = torch.empty(da.diffattn_decode_workspace_bytes(w.B, w.H, w.T, w.D, w.num_splits) // 4,
+                         device="cuda", dtype=torch.float32)
+
+        def kernel():
+            da.diffattn_decode(x["q1"], x["k1"], x["q2"], x["k2"], x["v"],
+                               lam if lam is not None else lam_buf, headnorm=w.headnorm,
+                               lambda_init=li, eps=w.eps, num_splits=w.num_splits,
+                               workspace=ws, out=out)
+
+    def step():
+        if lam is None:
+            da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], li, out=lam_buf)
+        kernel()
+
+    log(f"[bench] {name}: {warmup} warmup + {steps} timed steps")
+    ms, wall = time_steps(torch, step, steps, warmup)
+    kern_ms = time_kernel(torch, kernel, steps)
+    log(f"[bench] {name}: {ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
+    if w.kind == "prefill":
+        work = prefill_flops(w)
+        value = work / (ms * 1e-3) / 1e12
+        achieved = work / (kern_ms * 1e-3) / 1e12
+        peak = PEAK["bf16_mfma_tflops"] if w.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic("prefill", name), "kernel": KERNEL_NAME["prefill"],
+                "algorithmic_per_launch": work}
+        unit = "TFLOP/s"
+    else:
+        work = decode_bytes(w)
+        value = work / (ms * 1e-3) / 1e9
+        achieved = work / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"],
+                "unit": "GB/s", "frac": round(achieved / PEAK["hbm_gbs"], 4),
+                "traffic": measured_traffic("decode", name), "kernel": KERNEL_NAME["decode"],
+                "algorithmic_per_launch": work}
+        unit = "GB/s"
+    res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
+           "kernel_ms": round(kern_ms, 5), "wall_s": round(wall, 4), "roofline": roof,
+           "shape": {"B": w.B, "H": w.H, ("T" if w.kind == "prefill" else "L"): w.T, "D": w.D,
+                     "causal": w.causal if w.kind == "prefill" else False,
+                     "headnorm": w.headnorm, "dtype": w.dtype}}
+    del x, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(torch, name, budget_s=12.0):
+    """The float64 oracle, as it stands, on the host cores: whole heads of the
+    workload (every query row of each sampled (b, h)) until ~budget_s seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import WORKLOADS, make_workload
+
+    w = WORKLOADS[name]
+    x = make_workload(name, "cuda")
+    lam = 0.8
+    heads, t0 = 0, time.perf_counter()
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for (b, h) in pairs:
+        sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
+        o = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], lam,
+                                       w.causal, np.arange(w.T))
+        if w.headnorm:
+            oracle.head_rmsnorm(o, 0.8, w.eps)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = prefill_flops(w) / (w.B * w.H) * heads
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    del x
+    torch.cuda.empty_cache()
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (b,h) heads of {name}, all {w.T} query rows, "
+                      f"float64 numpy, {dt:.1f} s wall, host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--primary-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, head) with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import differential_attention_forward_amd as da
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    da.lib()
+    primary = bench_workload(torch, da, args.workload, args.steps, args.warmup)
+    also = {}
+    if not args.primary_only:
+        for name in OTHERS + [PRIMARY]:
+            if name != args.workload and name not in also:
+                also[name] = bench_workload(torch, da, name, args.steps, args.warmup)
+    cpu = None
+    w = WORKLOADS[args.workload]
+    if not args.no_cpu_baseline and w.kind == "prefill":
+        log("[bench] cpu baseline (float64 oracle)")
+        cpu = cpu_baseline(torch, args.workload)
+    line = {
+        "metric": METRIC, "value": primary["value"], "unit": primary["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": primary["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, **primary["shape"]},
+        "roofline": primary["roofline"], "cpu_baseline": cpu,
+        "also": also,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

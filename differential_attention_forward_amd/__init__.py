@@ -1,0 +1,210 @@
+"""Python binding of the gfx950 differential-attention library (libdiffattn.so).
+
+Argument marshalling only: every function below forwards to the C entry point
+of the same name (declared in ``include/diffattn.h``) with device pointers
+taken from torch tensors and the current HIP stream.  All arithmetic of the
+path runs in the HIP kernels.  Importing works without the library; the first
+call raises ``RuntimeError`` if ``libdiffattn.so`` has not been built (there is
+no CPU fallback).
+
+The method (paperleet "Differential Transformer Attention", equation for A1,
+A2 and O):  O = (softmax(Q1 K1^T/sqrt(D) + M) - lambda softmax(Q2 K2^T/sqrt(D) + M)) V
+with Q/K [B, H, T, D] and V, O [B, H, T, 2D].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "DIFFATTN_F32", "DIFFATTN_BF16", "library_path", "lib",
+    "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
+    "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
+]
+
+DIFFATTN_F32 = 0
+DIFFATTN_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libdiffattn.so"
+_lib = None
+
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SIGS = {
+    "diffattn_status_string": (ctypes.c_char_p, [_I]),
+    "diffattn_lambda_init": (_F, [_I]),
+    "diffattn_lambda": (_I, [_VP, _VP, _VP, _VP, _I, _I, _F, _VP, _VP]),
+    "diffattn_fwd": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
+                          _VP, _VP]),
+    "diffattn_decode_default_splits": (_I, [_I, _I, _I]),
+    "diffattn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "diffattn_decode": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F, _I,
+                             _VP, ctypes.c_size_t, _VP, _VP]),
+}
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (loaded on first use; raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m differential_attention_forward_amd.build`"
+                " (there is no CPU fallback)")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/diffattn.h (for symbol checks)."""
+    hdr = os.path.join(os.path.dirname(_HERE), "include", "diffattn.h")
+    with open(hdr) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(diffattn_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RuntimeError(f"diffattn: {diffattn_status_string(status)} (status {status})")
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DIFFATTN_F32
+    if t.dtype == torch.bfloat16:
+        return DIFFATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on a HIP device")
+    return t.contiguous()
+
+
+def _lambda_vec(lam, h: int, device) -> torch.Tensor:
+    """A per-head fp32 device vector [H] from a scalar, 0-d or [H] lambda."""
+    if isinstance(lam, torch.Tensor):
+        lam = lam.to(device=device, dtype=torch.float32)
+        if lam.dim() == 0 or lam.numel() == 1:
+            return lam.reshape(1).expand(h).contiguous()
+        if lam.shape != (h,):
+            raise ValueError(f"lambda must be a scalar or have shape [{h}]")
+        return lam.contiguous()
+    return torch.full((h,), float(lam), device=device, dtype=torch.float32)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def diffattn_status_string(status: int) -> str:
+    return lib().diffattn_status_string(int(status)).decode()
+
+
+def diffattn_lambda_init(layer: int) -> float:
+    return float(lib().diffattn_lambda_init(int(layer)))
+
+
+def diffattn_lambda(lq1, lk1, lq2, lk2, lambda_init: float, out=None, stream=None):
+    """lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init, per head.
+
+    Vectors of shape [Dl] give a 0-d tensor, [H, Dl] give [H] (fp32, device).
+    """
+    vecs = [_dev(t, n).float() for t, n in ((lq1, "lq1"), (lk1, "lk1"), (lq2, "lq2"), (lk2, "lk2"))]
+    one_d = vecs[0].dim() == 1
+    vecs = [v.reshape(1, -1) if one_d else v for v in vecs]
+    h, dl = vecs[0].shape
+    for v in vecs:
+        if v.shape != (h, dl):
+            raise ValueError("the four lambda vectors must have the same shape")
+    if out is None:
+        out = torch.empty((h,), device=vecs[0].device, dtype=torch.float32)
+    _check(lib().diffattn_lambda(*map(_ptr, vecs), h, dl, float(lambda_init), _ptr(out),
+                                 _stream(stream)))
+    return out.reshape(()) if one_d else out
+
+
+def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
+                 lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
+    """Prefill forward; q*, k* [B,H,T,D], v [B,H,T,2D] -> out [B,H,T,2D]."""
+    q1, k1, q2, k2, v = (_dev(t, n) for t, n in
+                         ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")))
+    if q1.dim() != 4:
+        raise ValueError("q1 must be [B, H, T, D]")
+    b, h, t, d = q1.shape
+    for x, n in ((k1, "k1"), (q2, "q2"), (k2, "k2")):
+        if x.shape != q1.shape or x.dtype != q1.dtype:
+            raise ValueError(f"{n} must match q1 in shape and dtype")
+    if v.shape != (b, h, t, 2 * d) or v.dtype != q1.dtype:
+        raise ValueError("v must be [B, H, T, 2D] with the dtype of q1")
+    lamv = _lambda_vec(lam, h, q1.device)
+    if out is None:
+        out = torch.empty_like(v)
+    _check(lib().diffattn_fwd(_dtype_code(q1), b, h, t, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                              _ptr(k2), _ptr(v), _ptr(lamv), int(bool(causal)),
+                              int(bool(headnorm)), float(lambda_init), float(eps), _ptr(out),
+                              _stream(stream)))
+    return out
+
+
+def diffattn_decode_default_splits(B: int, H: int, L: int) -> int:
+    return int(lib().diffattn_decode_default_splits(B, H, L))
+
+
+def diffattn_decode_workspace_bytes(B: int, H: int, L: int, D: int, num_splits: int = 0) -> int:
+    return int(lib().diffattn_decode_workspace_bytes(B, H, L, D, num_splits))
+
+
+def diffattn_decode(q1, k1, q2, k2, v, lam, headnorm: bool = False, lambda_init: float = 0.8,
+                    eps: float = 1e-5, num_splits: int = 0, workspace=None, out=None,
+                    stream=None):
+    """Decode; q* [B,H,D], caches k* [B,H,L,D] and v [B,H,L,2D] -> out [B,H,2D]."""
+    q1, k1, q2, k2, v = (_dev(t, n) for t, n in
+                         ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")))
+    if k1.dim() != 4:
+        raise ValueError("k1 must be [B, H, L, D]")
+    b, h, l, d = k1.shape
+    if q1.shape != (b, h, d) or q2.shape != (b, h, d):
+        raise ValueError("q1, q2 must be [B, H, D]")
+    if k2.shape != k1.shape or v.shape != (b, h, l, 2 * d):
+        raise ValueError("k2 must match k1 and v must be [B, H, L, 2D]")
+    for x in (q2, k1, k2, v):
+        if x.dtype != q1.dtype:
+            raise ValueError("all inputs must share one dtype")
+    lamv = _lambda_vec(lam, h, q1.device)
+    need = diffattn_decode_workspace_bytes(b, h, l, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, device=q1.device, dtype=torch.float32)
+    if out is None:
+        out = torch.empty((b, h, 2 * d), device=q1.device, dtype=q1.dtype)
+    _check(lib().diffattn_decode(_dtype_code(q1), b, h, l, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                                 _ptr(k2), _ptr(v), _ptr(lamv), int(bool(headnorm)),
+                                 float(lambda_init), float(eps), int(num_splits),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _ptr(out), _stream(stream)))
+    return out

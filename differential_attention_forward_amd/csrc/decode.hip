@@ -1,0 +1,326 @@
+// Differential-attention decode for gfx950: one new query per (batch, head)
+// against a KV cache of L rows, no mask.
+//
+// It computes the same O = (softmax(q1 K1^T / sqrt(D)) - lam softmax(q2 K2^T /
+// sqrt(D))) V as the prefill path for a single query row (paperleet
+// "Differential Transformer Attention", equation for A1, A2, O), with the
+// optional RMS head norm and x (1 - lambda_init) (aifetchly "Differential
+// Transformer: Canceling LLM Attention Noise", section 4).  The French lesson
+// page ("Le problème", "V1 contre V2") names the decode cost of the first
+// version: the value cache was loaded twice per step.  Here each cache byte is
+// read once: K1 and K2 once for the two score vectors, V once for both
+// weighted sums.
+//
+// Split-K: the cache is cut into S chunks; decode_partial_kernel turns each
+// (b, h, chunk) into two partial softmax states (running max m, sum l and the
+// 2D-wide weighted sum of V rows, one state per map), written to an fp32
+// workspace; decode_reduce_kernel then merges the S states of each (b, h) in
+// a fixed order (deterministic), combines the two maps, applies the optional
+// norm and stores the output row.  Stream order between the two launches is
+// the cross-workgroup barrier.
+//
+// Inside a chunk a workgroup walks sub-chunks of kSub keys: first all scores
+// of the sub-chunk (8-lane groups each own one key row, 16-byte coalesced
+// loads, dot products reduced across the group), then one block-wide max per
+// map, the exponentials, and finally the V pass (each lane owns 8 channels of
+// a V row).  Partial state is rescaled only when a sub-chunk raises the max.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kSub = 512;  // keys per sub-chunk (scores kept in LDS)
+constexpr int kUnroll = 4;
+
+template <bool F32>
+using Elem = typename std::conditional<F32, float, bf16>::type;
+
+// 16-byte chunk -> fp32 values
+template <bool F32>
+__device__ inline void unpack16(const u32x4& w, float* f) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16lo(w[i]);
+      f[2 * i + 1] = bf16hi(w[i]);
+    }
+  }
+}
+
+__device__ inline float block_reduce_max(float v, float* red) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) {
+  using E = Elem<F32>;
+  constexpr int DV = 2 * D;
+  constexpr int EPC = F32 ? 4 : 8;    // elements per 16-byte chunk
+  constexpr int LPK = D / EPC;        // lanes per K row
+  constexpr int KPR = kThreads / LPK; // key rows per pass (score phase)
+  constexpr int LPV = DV / EPC;       // lanes per V row
+  constexpr int VPR = kThreads / LPV; // V rows per pass
+  constexpr int RS = 2 * (DV + 2);    // floats per (b, h, split) record
+  static_assert(LPK <= 64 && LPV <= 64, "row must fit in one wave");
+
+  __shared__ float2 sp[kSub];         // per key: (s1, s2) then (p1, p2)
+  __shared__ float red[kWaves];
+  __shared__ float accred[kWaves][2][DV];
+
+  const int tid = threadIdx.x;
+  const int S = a.S;
+  const int split = blockIdx.x % S;
+  const int bh = blockIdx.x / S;
+  const int L = a.L;
+  const int chunk = (L + S - 1) / S;
+  const int kb = min(L, split * chunk);
+  const int ke = min(L, kb + chunk);
+
+  const E* __restrict__ K1 = (const E*)a.k1 + (size_t)bh * L * D;
+  const E* __restrict__ K2 = (const E*)a.k2 + (size_t)bh * L * D;
+  const E* __restrict__ V = (const E*)a.v + (size_t)bh * L * DV;
+  const float sc = a.score_scale;
+
+  // this lane's slice of q1 and q2 (score phase layout)
+  const int ksub = tid % LPK;
+  float q1f[EPC], q2f[EPC];
+  {
+    const E* q1p = (const E*)a.q1 + (size_t)bh * D + ksub * EPC;
+    const E* q2p = (const E*)a.q2 + (size_t)bh * D + ksub * EPC;
+    unpack16<F32>(*(const u32x4*)q1p, q1f);
+    unpack16<F32>(*(const u32x4*)q2p, q2f);
+  }
+  const int vsub = tid % LPV;
+
+  float m1 = kNegInf, m2 = kNegInf;  // running maxima (log2 units)
+  float l1 = 0.0f, l2 = 0.0f;        // this thread's share of the sums
+  float acc1[EPC], acc2[EPC];        // this thread's channels vsub*EPC ..
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc1[e] = acc2[e] = 0.0f;
+
+  for (int base = kb; base < ke; base += kSub) {
+    const int n = min(kSub, ke - base);
+
+    // ---- scores: s = q . k * log2(e)/sqrt(D) -----------------------------------
+    for (int k0 = tid / LPK; k0 < n; k0 += KPR * kUnroll) {
+      u32x4 w1[kUnroll], w2[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = min(k0 + u * KPR, n - 1);  // clamped: always in bounds
+        const size_t off = (size_t)(base + kk) * D + ksub * EPC;
+        w1[u] = *(const u32x4*)(K1 + off);
+        w2[u] = *(const u32x4*)(K2 + off);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float k1f[EPC], k2f[EPC];
+        unpack16<F32>(w1[u], k1f);
+        unpack16<F32>(w2[u], k2f);
+        float d1 = 0.0f, d2 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          d1 = fmaf(q1f[e], k1f[e], d1);
+          d2 = fmaf(q2f[e], k2f[e], d2);
+        }
+#pragma unroll
+        for (int o = 1; o < LPK; o <<= 1) {
+          d1 += __shfl_xor(d1, o);
+          d2 += __shfl_xor(d2, o);
+        }
+        const int kk = k0 + u * KPR;
+        if (ksub == 0 && kk < n) sp[kk] = make_float2(d1 * sc, d2 * sc);
+      }
+    }
+    __syncthreads();
+
+    // ---- block max per map, rescale the running state --------------------------
+    float bm1 = kNegInf, bm2 = kNegInf;
+    for (int kk = tid; kk < n; kk += kThreads) {
+      bm1 = fmaxf(bm1, sp[kk].x);
+      bm2 = fmaxf(bm2, sp[kk].y);
+    }
+    bm1 = block_reduce_max(bm1, red);
+    bm2 = block_reduce_max(bm2, red);
+    const float n1 = fmaxf(m1, bm1), n2 = fmaxf(m2, bm2);
+    const float al1 = __builtin_amdgcn_exp2f(m1 - n1);  // m = -inf -> 0
+    const float al2 = __builtin_amdgcn_exp2f(m2 - n2);
+    m1 = n1;
+    m2 = n2;
+    l1 *= al1;
+    l2 *= al2;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      acc1[e] *= al1;
+      acc2[e] *= al2;
+    }
+    for (int kk = tid; kk < n; kk += kThreads) {
+      const float2 s = sp[kk];
+      const float p1 = __builtin_amdgcn_exp2f(s.x - m1);
+      const float p2 = __builtin_amdgcn_exp2f(s.y - m2);
+      l1 += p1;
+      l2 += p2;
+      sp[kk] = make_float2(p1, p2);
+    }
+    __syncthreads();
+
+    // ---- V pass: both weighted sums from one read of each V row ----------------
+    for (int k0 = tid / LPV; k0 < n; k0 += VPR * kUnroll) {
+      u32x4 wv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = min(k0 + u * VPR, n - 1);
+        wv[u] = *(const u32x4*)(V + (size_t)(base + kk) * DV + vsub * EPC);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = k0 + u * VPR;
+        if (kk < n) {
+          const float2 p = sp[kk];
+          float vf[EPC];
+          unpack16<F32>(wv[u], vf);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            acc1[e] = fmaf(p.x, vf[e], acc1[e]);
+            acc2[e] = fmaf(p.y, vf[e], acc2[e]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // sp is rewritten by the next sub-chunk
+  }
+
+  // ---- reduce the per-thread shares and write the partial record ---------------
+  l1 = wave_sum(l1);
+  l2 = wave_sum(l2);
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) {
+#pragma unroll
+    for (int o = LPV; o < 64; o <<= 1) {
+      acc1[e] += __shfl_xor(acc1[e], o);
+      acc2[e] += __shfl_xor(acc2[e], o);
+    }
+  }
+  if (lane < LPV) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      accred[wave][0][vsub * EPC + e] = acc1[e];
+      accred[wave][1][vsub * EPC + e] = acc2[e];
+    }
+  }
+  __shared__ float lred[kWaves][2];
+  if (lane == 0) {
+    lred[wave][0] = l1;
+    lred[wave][1] = l2;
+  }
+  __syncthreads();
+  float* rec = a.ws + ((size_t)bh * S + split) * RS;
+  for (int i = tid; i < 2 * DV; i += kThreads) {
+    const int br = i / DV, c = i % DV;
+    float t = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) t += accred[wv][br][c];
+    rec[br * (DV + 2) + 2 + c] = t;
+  }
+  if (tid < 2) {
+    float t = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) t += lred[wv][tid];
+    rec[tid * (DV + 2)] = tid == 0 ? m1 : m2;
+    rec[tid * (DV + 2) + 1] = t;
+  }
+}
+
+template <int D, bool F32, bool HEADNORM>
+__global__ __launch_bounds__(2 * D) void decode_reduce_kernel(DecodeArgs a) {
+  using E = Elem<F32>;
+  constexpr int DV = 2 * D;
+  constexpr int RS = 2 * (DV + 2);
+  constexpr int NWV = (DV + 63) / 64;
+  __shared__ float red[NWV];
+
+  const int bh = blockIdx.x;
+  const int c = threadIdx.x;
+  const int S = a.S;
+  const float* __restrict__ rec = a.ws + (size_t)bh * S * RS;
+
+  float M1 = kNegInf, M2 = kNegInf;
+  for (int s = 0; s < S; ++s) {
+    M1 = fmaxf(M1, rec[s * RS]);
+    M2 = fmaxf(M2, rec[s * RS + DV + 2]);
+  }
+  float L1 = 0.0f, L2 = 0.0f, A1 = 0.0f, A2 = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float* r = rec + s * RS;
+    const float f1 = __builtin_amdgcn_exp2f(r[0] - M1);  // empty chunk: m = -inf -> 0
+    const float f2 = __builtin_amdgcn_exp2f(r[DV + 2] - M2);
+    L1 = fmaf(f1, r[1], L1);
+    A1 = fmaf(f1, r[2 + c], A1);
+    L2 = fmaf(f2, r[DV + 3], L2);
+    A2 = fmaf(f2, r[DV + 4 + c], A2);
+  }
+  const float t1 = A1 * (1.0f / L1);
+  const float t2 = A2 * (1.0f / L2);
+  const float lt2 = a.lam[bh % a.H] * t2;
+  float o = t1 - lt2;
+  if constexpr (HEADNORM) {
+    float ss = wave_sum(o * o);
+    if ((c & 63) == 0) red[c >> 6] = ss;
+    __syncthreads();
+    ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) ss += red[i];
+    o *= rsqrtf(ss * (1.0f / DV) + a.eps) * a.out_scale;
+  }
+  ((E*)a.out)[(size_t)bh * DV + c] = (E)o;
+}
+
+template <int D, bool F32>
+hipError_t launch_d(const DecodeArgs& a, bool headnorm, hipStream_t stream) {
+  const long nblk = (long)a.B * a.H * a.S;
+  if (nblk > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  decode_partial_kernel<D, F32><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g((unsigned)(a.B * a.H)), b(2 * D);
+  if (headnorm) decode_reduce_kernel<D, F32, true><<<g, b, 0, stream>>>(a);
+  else decode_reduce_kernel<D, F32, false><<<g, b, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, bool headnorm, hipStream_t stream) {
+  if (dtype == 1) {
+    switch (D) {
+      case 32: return launch_d<32, false>(a, headnorm, stream);
+      case 64: return launch_d<64, false>(a, headnorm, stream);
+      case 128: return launch_d<128, false>(a, headnorm, stream);
+    }
+  } else {
+    switch (D) {
+      case 32: return launch_d<32, true>(a, headnorm, stream);
+      case 64: return launch_d<64, true>(a, headnorm, stream);
+      case 128: return launch_d<128, true>(a, headnorm, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn

@@ -1,0 +1,43 @@
+// lambda_h = exp(lq1_h . lk1_h) - exp(lq2_h . lk2_h) + lambda_init
+// (aifetchly "Differential Transformer: Canceling LLM Attention Noise",
+// section 3; paperleet "Differential Transformer Attention", the scalar
+// parameterisation).  One wave per head: strided fp32 products, a fixed-order
+// wavefront reduction, two exp.  The result stays on the device so the
+// forward call can consume it without a host round trip.
+#include "common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+__global__ __launch_bounds__(64) void lambda_kernel(const float* __restrict__ lq1,
+                                                    const float* __restrict__ lk1,
+                                                    const float* __restrict__ lq2,
+                                                    const float* __restrict__ lk2, int Dl,
+                                                    float lambda_init, float* __restrict__ out) {
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x;
+  const size_t base = (size_t)h * Dl;
+  float d1 = 0.0f, d2 = 0.0f;
+  for (int i = lane; i < Dl; i += 64) {
+    d1 = fmaf(lq1[base + i], lk1[base + i], d1);
+    d2 = fmaf(lq2[base + i], lk2[base + i], d2);
+  }
+  d1 = wave_sum(d1);
+  d2 = wave_sum(d2);
+  if (lane == 0) {
+    const float e1 = expf(d1);
+    const float e2 = expf(d2);
+    out[h] = (e1 - e2) + lambda_init;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
+                         int H, int Dl, float lambda_init, float* out, hipStream_t stream) {
+  lambda_kernel<<<dim3(H), dim3(64), 0, stream>>>(lq1, lk1, lq2, lk2, Dl, lambda_init, out);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

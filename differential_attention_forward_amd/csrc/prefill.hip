@@ -1,0 +1,499 @@
+// Differential-attention prefill forward for gfx950 (CDNA4).
+//
+// Computes, per (batch, head),
+//   O = (softmax(Q1 K1^T / sqrt(D) + M) - lam_h softmax(Q2 K2^T / sqrt(D) + M)) V
+// (paperleet "Differential Transformer Attention", equation for A1, A2, O; the
+// causal mask M is -inf on future keys in both branches), optionally followed
+// by an RMS norm over the 2D output channels of each token and a constant
+// x (1 - lambda_init) (aifetchly "Differential Transformer: Canceling LLM
+// Attention Noise", section 4).
+//
+// Design (one pass over K/V, both maps at once):
+//  * One workgroup = NW waves = BR query rows of one (b, h); each wave owns
+//    32*NQB queries.  Q1/Q2 fragments stay in VGPRs for the whole kernel.
+//  * K1, K2 and V tiles of BC keys are staged global -> VGPR -> LDS, double
+//    buffered: the global loads of tile t+1 are in flight while tile t is
+//    computed, one barrier per tile.  V is written to LDS transposed
+//    ([channel][key]) so that it can be the A operand of the P.V MFMA.
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: lane l then holds 16 keys of query l%32, so the
+//    row max is an in-lane reduction plus one exchange with lane l^32, and
+//    the probabilities P^T land in exactly the register layout the P.V MFMA
+//    wants as its B operand (no data movement).
+//  * Two independent online-softmax states per query row (one per map) with
+//    lazy rescaling: the running max only moves (and the accumulators are
+//    only rescaled) when a block max exceeds it by more than kTau (log2
+//    units), so steady-state blocks do no rescale work.
+//  * The row sums are taken over the bf16-rounded probabilities actually fed
+//    to the MFMA (v_dot2_f32_bf16 against 1.0), so a value offset shared by
+//    all keys passes through with weights that sum exactly to one.
+//  * Both P1.V and P2.V are fed from one V tile in LDS: each V fragment read
+//    serves both branches (V is read from memory once, not once per map).
+//  * Causal: key blocks above a wave's last query are skipped; only blocks
+//    that straddle the diagonal evaluate the mask.  Query tiles are issued
+//    heaviest first and workgroups are remapped so that each XCD works
+//    through consecutive tiles of the same heads (K/V reuse in its L2).
+//  * fp32 inputs use the same structure with v_mfma_f32_32x32x2_f32 and
+//    fp32 probabilities (V kept row-major in LDS).
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 2^8
+
+template <int D, int NQB, int NW, int BC, bool F32>
+struct Cfg {
+  static constexpr int DV = 2 * D;
+  static constexpr int QPW = 32 * NQB;
+  static constexpr int BR = NW * QPW;
+  static constexpr int NT = NW * 64;
+  static constexpr int ES = F32 ? 4 : 2;
+  static constexpr int EPC = 16 / ES;               // elements per 16-byte chunk
+  static constexpr int KP = F32 ? D + 4 : D + 8;    // K row pitch (elements)
+  // V in LDS: fp32 row-major [BC][DV]; bf16 transposed [DV][BC]
+  static constexpr int VP = F32 ? DV + 4 : BC + 8;
+  static constexpr int KTILE = BC * KP;
+  static constexpr int VTILE = F32 ? BC * VP : DV * VP;
+  static constexpr int STAGE = 2 * KTILE + VTILE;   // elements per LDS stage
+  static constexpr int NKC = BC * D / EPC;          // 16-B chunks per K tile
+  static constexpr int NKPT = (NKC + NT - 1) / NT;
+  // V staging units: fp32 plain 16-B chunks; bf16 blocks of 4 keys x 8 channels
+  static constexpr int NVU = F32 ? BC * DV / EPC : (BC / 4) * (DV / 8);
+  static constexpr int NVPT = (NVU + NT - 1) / NT;
+  static constexpr int VREG = F32 ? 1 : 4;
+  static constexpr int NKB = BC / 32;               // 32-key blocks per tile
+  static constexpr int CB = DV / 32;                // 32-channel output blocks
+  static constexpr int KSTEPS = F32 ? D / 2 : D / 16;
+  static_assert(BC % 32 == 0, "key tile must hold whole 32-key blocks");
+  static_assert(STAGE * ES * 2 <= 160 * 1024, "LDS budget exceeded");
+};
+
+// Position of key quad kq inside the transposed V row: within every group of
+// 4 quads (16 keys) the middle two are swapped, which is the key order in
+// which one lane's 8 probabilities reach the MFMA (keys 0-3 and 8-11 in the
+// lower lane half, 4-7 and 12-15 in the upper half).
+__device__ inline int vt_quad_pos(int kq) { return kq ^ ((((kq >> 1) ^ kq) & 1) * 3); }
+
+template <bool F32>
+using QFrag = typename std::conditional<F32, float, bf16x8>::type;
+template <bool F32>
+using Elem = typename std::conditional<F32, float, bf16>::type;
+
+template <int D, int NQB, int NW, int BC, bool F32, bool CAUSAL, bool HEADNORM>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
+  using C = Cfg<D, NQB, NW, BC, F32>;
+  using E = Elem<F32>;
+  __shared__ __attribute__((aligned(16))) E smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int T = a.T;
+
+  const int nqt = (T + C::BR - 1) / C::BR;
+  const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
+  const int bh = w / nqt;
+  const int qi = w % nqt;
+  const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
+  const int h = bh % a.H;
+
+  const size_t qk_off = (size_t)bh * T * D;
+  const size_t v_off = (size_t)bh * T * C::DV;
+  const E* __restrict__ Q1 = (const E*)a.q1 + qk_off;
+  const E* __restrict__ Q2 = (const E*)a.q2 + qk_off;
+  const E* __restrict__ K1 = (const E*)a.k1 + qk_off;
+  const E* __restrict__ K2 = (const E*)a.k2 + qk_off;
+  const E* __restrict__ V = (const E*)a.v + v_off;
+
+  const int q_tile0 = qt * C::BR;
+  const int q0 = q_tile0 + wave * C::QPW;
+  const int q_last = min(q0 + C::QPW, T) - 1;
+  const bool wave_active = q0 < T;
+  const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
+  const int ntiles = (k_end + BC - 1) / BC;
+  const float sc = a.score_scale;
+  const float lamv = a.lam[h];
+
+  // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
+  QFrag<F32> qf[2][NQB][C::KSTEPS];
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      // rows past the end read row T-1 (always in bounds) and are zeroed
+      const int query = q0 + qb * 32 + l32;
+      const bool ok = query < T;
+      const E* src = (br ? Q2 : Q1) + (size_t)min(query, T - 1) * D;
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        if constexpr (F32) {
+          const float x = src[2 * ks + hi];
+          qf[br][qb][ks] = ok ? x : 0.0f;
+        } else {
+          u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
+          raw = ok ? raw : u32x4{0u, 0u, 0u, 0u};
+          qf[br][qb][ks] = __builtin_bit_cast(bf16x8, raw);
+        }
+      }
+    }
+  }
+
+  floatx16 acc[2][NQB][C::CB];
+  float mu[2][NQB];
+  float lsum[2][NQB];
+#pragma unroll
+  for (int br = 0; br < 2; ++br)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      mu[br][qb] = kNegInf;
+      lsum[br][qb] = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[br][qb][cb][r] = 0.0f;
+    }
+
+  // ---- staging registers ------------------------------------------------------
+  u32x4 rk[2][C::NKPT];
+  u32x4 rv[C::NVPT][C::VREG];
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // Global -> register staging of one key tile.  Keys past the end load row
+  // T-1 (always in bounds) and are replaced by zeros, so there is no branch.
+  auto load_tile = [&](int kt) {
+    const int kbase = kt * BC;
+#pragma unroll
+    for (int i = 0; i < C::NKPT; ++i) {
+      const int c = (C::NKC % C::NT == 0) ? tid + i * C::NT : min(tid + i * C::NT, C::NKC - 1);
+      const int row = c / (D / C::EPC);
+      const int col = c % (D / C::EPC);
+      const int key = kbase + row;
+      const size_t off = (size_t)min(key, T - 1) * D + col * C::EPC;
+      const u32x4 x1 = *(const u32x4*)(K1 + off);
+      const u32x4 x2 = *(const u32x4*)(K2 + off);
+      rk[0][i] = key < T ? x1 : zero4;
+      rk[1][i] = key < T ? x2 : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < C::NVPT; ++i) {
+      const int u = (C::NVU % C::NT == 0) ? tid + i * C::NT : min(tid + i * C::NT, C::NVU - 1);
+      if constexpr (F32) {
+        const int row = u / (C::DV / 4);
+        const int col = u % (C::DV / 4);
+        const int key = kbase + row;
+        const u32x4 x = *(const u32x4*)(V + (size_t)min(key, T - 1) * C::DV + col * 4);
+        rv[i][0] = key < T ? x : zero4;
+      } else {
+        const int kq = u % (BC / 4);
+        const int cc = u / (BC / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kbase + kq * 4 + r;
+          const u32x4 x = *(const u32x4*)(V + (size_t)min(key, T - 1) * C::DV + cc * 8);
+          rv[i][r] = key < T ? x : zero4;
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    E* Ks1 = smem + buf * C::STAGE;
+    E* Ks2 = Ks1 + C::KTILE;
+    E* Vs = Ks2 + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::NKPT; ++i) {
+      const int c = tid + i * C::NT;
+      if (C::NKC % C::NT == 0 || c < C::NKC) {
+        const int row = c / (D / C::EPC);
+        const int col = c % (D / C::EPC);
+        *(u32x4*)(Ks1 + row * C::KP + col * C::EPC) = rk[0][i];
+        *(u32x4*)(Ks2 + row * C::KP + col * C::EPC) = rk[1][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::NVPT; ++i) {
+      const int u = tid + i * C::NT;
+      if (C::NVU % C::NT == 0 || u < C::NVU) {
+        if constexpr (F32) {
+          const int row = u / (C::DV / 4);
+          const int col = u % (C::DV / 4);
+          *(u32x4*)(Vs + row * C::VP + col * 4) = rv[i][0];
+        } else {
+          // 4 keys x 8 channels -> 8 channel rows of 4 keys each
+          const int kq = u % (BC / 4);
+          const int cc = u / (BC / 4);
+          const int pos = vt_quad_pos(kq) * 4;
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            const uint32_t a0 = rv[i][0][wd], a1 = rv[i][1][wd];
+            const uint32_t a2 = rv[i][2][wd], a3 = rv[i][3][wd];
+            const u32x2 even = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+            const u32x2 odd = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+            *(u32x2*)(Vs + (cc * 8 + 2 * wd) * C::VP + pos) = even;
+            *(u32x2*)(Vs + (cc * 8 + 2 * wd + 1) * C::VP + pos) = odd;
+          }
+        }
+      }
+    }
+  };
+
+  auto compute_tile = [&](int kt, int buf) {
+    const E* Ks1 = smem + buf * C::STAGE;
+    const E* Ks2 = Ks1 + C::KTILE;
+    const E* Vs = Ks2 + C::KTILE;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      const int key0 = kt * BC + kb * 32;
+      if (key0 >= T) break;
+      if (CAUSAL && key0 > q_last) break;
+
+      // S^T = K Q^T for both maps
+      floatx16 s[2][NQB];
+#pragma unroll
+      for (int br = 0; br < 2; ++br)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[br][qb][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        if constexpr (F32) {
+          const float a1 = Ks1[(kb * 32 + l32) * C::KP + 2 * ks + hi];
+          const float a2 = Ks2[(kb * 32 + l32) * C::KP + 2 * ks + hi];
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            s[0][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, qf[0][qb][ks], s[0][qb], 0, 0, 0);
+            s[1][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a2, qf[1][qb][ks], s[1][qb], 0, 0, 0);
+          }
+        } else {
+          const bf16x8 a1 = *(const bf16x8*)(Ks1 + (kb * 32 + l32) * C::KP + ks * 16 + hi * 8);
+          const bf16x8 a2 = *(const bf16x8*)(Ks2 + (kb * 32 + l32) * C::KP + ks * 16 + hi * 8);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            s[0][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[0][qb][ks], s[0][qb], 0, 0, 0);
+            s[1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, qf[1][qb][ks], s[1][qb], 0, 0, 0);
+          }
+        }
+      }
+
+      // mask: causal blocks that reach past the wave's first query, or the
+      // ragged end of the key axis for full attention
+      const bool need_mask = CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int query = q0 + qb * 32 + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool masked = CAUSAL ? (key > query) : (key >= T);
+            if (masked) {
+              s[0][qb][r] = kNegInf;
+              s[1][qb][r] = kNegInf;
+            }
+          }
+        }
+      }
+
+      // online softmax, two independent states per query row
+      float mx[2][NQB];
+      bool need = false;
+#pragma unroll
+      for (int br = 0; br < 2; ++br)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float m = s[br][qb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][qb][r]);
+          m = fmaxf(m, __shfl_xor(m, 32));
+          m *= sc;
+          mx[br][qb] = m;
+          need |= m > mu[br][qb] + kTau;
+        }
+      if (__any(need)) {
+#pragma unroll
+        for (int br = 0; br < 2; ++br)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float mn = fmaxf(mu[br][qb], mx[br][qb]);
+            const float alpha = (mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(mu[br][qb] - mn);
+            mu[br][qb] = mn;
+            lsum[br][qb] *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[br][qb][cb][r] *= alpha;
+          }
+      }
+
+      if constexpr (F32) {
+        float p[2][NQB][16];
+#pragma unroll
+        for (int br = 0; br < 2; ++br)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              p[br][qb][r] = __builtin_amdgcn_exp2f(fmaf(s[br][qb][r], sc, -msub));
+              lsum[br][qb] += p[br][qb][r];
+            }
+          }
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int krow = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const float av = Vs[krow * C::VP + cb * 32 + l32];
+#pragma unroll
+            for (int br = 0; br < 2; ++br)
+#pragma unroll
+              for (int qb = 0; qb < NQB; ++qb)
+                acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, p[br][qb][r], acc[br][qb][cb], 0, 0, 0);
+          }
+      } else {
+        bf16x8 pk[2][NQB][2];
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int br = 0; br < 2; ++br)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float pa = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j], sc, -msub));
+                const float pb = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j + 1], sc, -msub));
+                const bf16x2 pw = {(bf16)pa, (bf16)pb};
+                lsum[br][qb] = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, lsum[br][qb], false);
+                pk[br][qb][ks][2 * j] = pw[0];
+                pk[br][qb][ks][2 * j + 1] = pw[1];
+              }
+            }
+          }
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 av = *(const bf16x8*)(Vs + (cb * 32 + l32) * C::VP + kb * 32 + ks * 16 + hi * 8);
+#pragma unroll
+            for (int br = 0; br < 2; ++br)
+#pragma unroll
+              for (int qb = 0; qb < NQB; ++qb)
+                acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[br][qb][ks], acc[br][qb][cb], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  // ---- main loop over key tiles ----------------------------------------------
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const bool more = kt + 1 < ntiles;
+    if (more) load_tile(kt + 1);
+    if (wave_active) compute_tile(kt, kt & 1);
+    if (more) store_tile((kt + 1) & 1);
+    __syncthreads();
+  }
+  if (!wave_active) return;
+
+  // ---- epilogue: combine the maps, optional head norm, store -----------------
+  E* __restrict__ O = (E*)a.out + v_off;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int query = q0 + qb * 32 + l32;
+    const float l1 = lsum[0][qb] + __shfl_xor(lsum[0][qb], 32);
+    const float l2 = lsum[1][qb] + __shfl_xor(lsum[1][qb], 32);
+    const float inv1 = 1.0f / l1;
+    const float inv2 = 1.0f / l2;
+    float o[C::CB][16];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // t1 - lam * t2 with both branches rounded identically (no contraction)
+        const float t1 = acc[0][qb][cb][r] * inv1;
+        const float t2 = acc[1][qb][cb][r] * inv2;
+        const float lt2 = lamv * t2;
+        o[cb][r] = t1 - lt2;
+      }
+    if constexpr (HEADNORM) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss = fmaf(o[cb][r], o[cb][r], ss);
+      ss += __shfl_xor(ss, 32);
+      const float f = rsqrtf(ss * (1.0f / C::DV) + a.eps) * a.out_scale;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= f;
+    }
+    if (query < T) {
+      E* dst = O + (size_t)query * C::DV;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ch = cb * 32 + 8 * g + 4 * hi;
+          if constexpr (F32) {
+            const floatx4 v4 = {o[cb][4 * g], o[cb][4 * g + 1], o[cb][4 * g + 2], o[cb][4 * g + 3]};
+            *(floatx4*)(dst + ch) = v4;
+          } else {
+            const bf16x4 v4 = {(bf16)o[cb][4 * g], (bf16)o[cb][4 * g + 1], (bf16)o[cb][4 * g + 2],
+                               (bf16)o[cb][4 * g + 3]};
+            *(bf16x4*)(dst + ch) = v4;
+          }
+        }
+    }
+  }
+}
+
+template <int D, int NQB, int NW, int BC, bool F32>
+hipError_t launch_cfg(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
+  using C = Cfg<D, NQB, NW, BC, F32>;
+  const long nqt = (a.T + C::BR - 1) / C::BR;
+  const long grid = (long)a.B * a.H * nqt;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), b(C::NT);
+  if (causal) {
+    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, true, true><<<g, b, 0, stream>>>(a);
+    else fwd_kernel<D, NQB, NW, BC, F32, true, false><<<g, b, 0, stream>>>(a);
+  } else {
+    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, false, true><<<g, b, 0, stream>>>(a);
+    else fwd_kernel<D, NQB, NW, BC, F32, false, false><<<g, b, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool headnorm,
+                      hipStream_t stream) {
+  if (dtype == 1) {  // bf16
+    switch (D) {
+      case 32: return launch_cfg<32, 1, 8, 64, false>(a, causal, headnorm, stream);
+      case 64: return launch_cfg<64, 1, 8, 64, false>(a, causal, headnorm, stream);
+      case 128: return launch_cfg<128, 1, 4, 64, false>(a, causal, headnorm, stream);
+    }
+  } else {  // fp32
+    switch (D) {
+      case 32: return launch_cfg<32, 1, 4, 32, true>(a, causal, headnorm, stream);
+      case 64: return launch_cfg<64, 1, 4, 32, true>(a, causal, headnorm, stream);
+      case 128: return launch_cfg<128, 1, 4, 32, true>(a, causal, headnorm, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn

@@ -1,0 +1,146 @@
+/*
+ * diffattn.h -- C ABI of the MI355X (gfx950) differential-attention library.
+ *
+ * The library computes multi-head differential attention, forward only:
+ *
+ *   O = (softmax(Q1 K1^T / sqrt(D) + M) - lambda * softmax(Q2 K2^T / sqrt(D) + M)) V
+ *
+ * as defined on the paperleet page "Differential Transformer Attention"
+ * (equation for A1, A2 and O; M is 0 on allowed keys and -inf on future keys
+ * under the causal mask, in both branches; softmax runs over keys), with
+ * Q1, Q2, K1, K2 of shape [B, H, T, D] and V, O of shape [B, H, T, 2D].
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP device memory) owned by the
+ *     caller.  The library allocates nothing and keeps no state; every entry
+ *     point is thread-safe.
+ *   - Tensors are dense, contiguous and row-major in the shapes given.  Every
+ *     tensor pointer must be 16-byte aligned.
+ *   - Inputs are never written.  Outputs must not overlap any input.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising.  Argument checks run on the
+ *     host before any HIP call, so an invalid call launches nothing.
+ *   - Element type `dtype`: DIFFATTN_F32 (float) or DIFFATTN_BF16 (bfloat16).
+ *     The output has the input dtype.  Accumulation is fp32 in both cases; in
+ *     bf16 mode the probabilities are rounded to bf16 before they multiply V.
+ *   - Head width D must be 32, 64 or 128 (V and O rows are 2D wide).
+ *   - lambda is a per-head fp32 device array [H]; a per-layer scalar is the
+ *     case of all heads equal.  It is not clamped: negative values and values
+ *     above 1 are allowed (paperleet page, "Return requirements").
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIFFATTN_OK = 0,
+  DIFFATTN_ERR_INVALID = 1,     /* null pointer, size < 1, eps <= 0 with head norm,
+                                   overlapping output, bad split count */
+  DIFFATTN_ERR_UNSUPPORTED = 2, /* unknown dtype, D not in {32,64,128}, misaligned pointer,
+                                   sizes beyond the 32-bit grid limits */
+  DIFFATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  DIFFATTN_ERR_HIP = 4          /* the kernel launch itself failed */
+} diffattn_status;
+
+typedef enum { DIFFATTN_F32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* diffattn_status_string(int status);
+
+/*
+ * lambda_init(l) = 0.8 - 0.6 * exp(-0.3 * (l - 1)) for layer l = 1, 2, ...
+ * (aifetchly "Differential Transformer: Canceling LLM Attention Noise",
+ * section 3; paperleet page, "Formula and conventions").  Host-only; returns
+ * NaN for layer < 1.
+ */
+float diffattn_lambda_init(int layer);
+
+/*
+ * lambda_out[h] = exp(lq1[h] . lk1[h]) - exp(lq2[h] . lk2[h]) + lambda_init
+ * (aifetchly page, section 3; paperleet page, scalar parameterisation).
+ *
+ *   lq1, lk1, lq2, lk2  device fp32 [H, Dl], row h = the four vectors of head h
+ *   lambda_out          device fp32 [H]; may be passed straight to diffattn_fwd
+ *                       or diffattn_decode on the same stream
+ * Errors: ERR_INVALID for a null pointer, H < 1 or Dl < 1, or lambda_out
+ * overlapping an input; ERR_UNSUPPORTED for a misaligned pointer (4 bytes
+ * suffices here) or H beyond the grid limit.
+ */
+diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float* lq2,
+                                const float* lk2, int H, int Dl, float lambda_init,
+                                float* lambda_out, hipStream_t stream);
+
+/*
+ * Prefill forward (paperleet page, equation for A1, A2, O).
+ *
+ *   q1, k1, q2, k2  [B, H, T, D]   dtype elements
+ *   v               [B, H, T, 2D]  dtype elements
+ *   lambda          [H] fp32 (device)
+ *   causal          non-zero: key j is visible to query i iff j <= i (top-left
+ *                   aligned, both maps); zero: every key is visible
+ *   headnorm        non-zero: each output row is divided by
+ *                   sqrt(mean over its 2D channels of o^2 + eps) and multiplied
+ *                   by (1 - lambda_init) (aifetchly page, section 4: per-head
+ *                   normalisation then the (1 - lambda_init) multiplier; RMS
+ *                   form, no affine weight).  zero: raw (A1 - lambda A2) V,
+ *                   lambda_init and eps unused.
+ *   out             [B, H, T, 2D]  dtype elements
+ * Errors: ERR_INVALID (null pointer, B/H/T < 1, headnorm with eps <= 0 or NaN,
+ * out overlapping an input), ERR_UNSUPPORTED (dtype, D, alignment, grid size),
+ * ERR_HIP (launch failure).
+ */
+diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* q1,
+                             const void* k1, const void* q2, const void* k2, const void* v,
+                             const float* lambda, int causal, int headnorm, float lambda_init,
+                             float eps, void* out, hipStream_t stream);
+
+/*
+ * Number of key splits decode uses for (B, H, L) when num_splits = 0.
+ */
+int diffattn_decode_default_splits(int B, int H, int L);
+
+/*
+ * Bytes of fp32 workspace diffattn_decode needs: B*H*S*2*(2D+2)*4 with
+ * S = num_splits, or the default split count when num_splits = 0.
+ * Returns 0 for invalid sizes.
+ */
+size_t diffattn_decode_workspace_bytes(int B, int H, int L, int D, int num_splits);
+
+/*
+ * Decode: one new query per (b, h) against a KV cache of L rows, no mask
+ * (the French lesson page "Attention différentielle (V2)", "V1 contre V2":
+ * the value cache is read once per step for both maps).
+ *
+ *   q1, q2          [B, H, D]
+ *   k1, k2          [B, H, L, D]   caches
+ *   v               [B, H, L, 2D]  cache
+ *   lambda          [H] fp32 (device)
+ *   headnorm, lambda_init, eps   as for diffattn_fwd
+ *   num_splits      number of key chunks (split-K), 1..L; 0 = default
+ *   workspace       device scratch of at least
+ *                   diffattn_decode_workspace_bytes(B, H, L, D, num_splits)
+ *                   bytes, 16-byte aligned; its contents on entry are ignored
+ *                   and calls on one stream may reuse it (calls that run
+ *                   concurrently need separate workspaces)
+ *   out             [B, H, 2D]
+ * Errors: as diffattn_fwd, plus ERR_INVALID for num_splits < 0 or > L and
+ * ERR_WORKSPACE for a null or too small workspace.
+ */
+diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const void* q1,
+                                const void* k1, const void* q2, const void* k2, const void* v,
+                                const float* lambda, int headnorm, float lambda_init, float eps,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

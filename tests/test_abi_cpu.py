@@ -1,0 +1,131 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+and rejects invalid arguments before any HIP call (no GPU needed).
+
+Pointers passed here are fake addresses; validation only compares them and
+returns before anything dereferences or launches.
+"""
+
+import ctypes
+import math
+
+import pytest
+
+import differential_attention_forward_amd as da
+import oracle
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = da.DIFFATTN_F32, da.DIFFATTN_BF16
+
+
+@pytest.fixture(scope="module")
+def L():
+    return da.lib()
+
+
+def test_header_symbols_exported(L):
+    names = da.header_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert da.diffattn_status_string(s)
+    assert da.diffattn_status_string(99) == "unknown status"
+
+
+def test_lambda_init_matches_oracle(L):
+    for layer in (1, 2, 3, 12, 13, 24, 100):
+        got = da.diffattn_lambda_init(layer)
+        assert abs(got - oracle.lambda_init_schedule(layer)) <= 6e-8
+    assert math.isnan(da.diffattn_lambda_init(0))
+
+
+def test_decode_split_helpers(L):
+    assert da.diffattn_decode_default_splits(32, 16, 65536) >= 1
+    assert da.diffattn_decode_default_splits(1, 1, 100) == 1
+    assert da.diffattn_decode_default_splits(0, 1, 1) == 0
+    assert da.diffattn_decode_workspace_bytes(32, 16, 65536, 64, 64) == 32 * 16 * 64 * 2 * 130 * 4
+    s = da.diffattn_decode_default_splits(2, 3, 5000)
+    assert da.diffattn_decode_workspace_bytes(2, 3, 5000, 32, 0) == 2 * 3 * s * 2 * 66 * 4
+    assert da.diffattn_decode_workspace_bytes(1, 1, 10, 64, 11) == 0
+    assert da.diffattn_decode_workspace_bytes(1, 1, 10, 64, -1) == 0
+
+
+# fake, well-separated, 256-byte aligned device addresses
+BASE = 1 << 40
+def P(i, off=0):
+    return ctypes.c_void_p(BASE + i * (1 << 32) + off)
+
+
+def fwd(L, dtype=BF16, B=1, H=2, T=8, D=64, ptrs=None, causal=1, headnorm=0, eps=1e-5):
+    p = ptrs or [P(i) for i in range(7)]
+    return L.diffattn_fwd(dtype, B, H, T, D, p[0], p[1], p[2], p[3], p[4], p[5], causal,
+                          headnorm, ctypes.c_float(0.8), ctypes.c_float(eps), p[6], None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, ptrs=[P(0), None, P(2), P(3), P(4), P(5), P(6)]) == INVALID
+    assert fwd(L, ptrs=[P(i) for i in range(6)] + [None]) == INVALID
+    assert fwd(L, B=0) == INVALID
+    assert fwd(L, H=0) == INVALID
+    assert fwd(L, T=0) == INVALID
+    assert fwd(L, headnorm=1, eps=0.0) == INVALID
+    assert fwd(L, headnorm=1, eps=-1.0) == INVALID
+    assert fwd(L, headnorm=1, eps=float("nan")) == INVALID
+    assert fwd(L, dtype=7) == UNSUPPORTED
+    for d in (16, 48, 96, 256):
+        assert fwd(L, D=d) == UNSUPPORTED
+    bad = [P(i) for i in range(7)]
+    bad[2] = P(2, 8)
+    assert fwd(L, ptrs=bad) == UNSUPPORTED
+    bad = [P(i) for i in range(7)]
+    bad[6] = P(6, 4)
+    assert fwd(L, ptrs=bad) == UNSUPPORTED
+    # out overlapping an input
+    alias = [P(i) for i in range(7)]
+    alias[6] = P(4, 256)
+    assert fwd(L, ptrs=alias) == INVALID
+    alias[6] = P(0)
+    assert fwd(L, ptrs=alias) == INVALID
+
+
+def dec(L, dtype=BF16, B=1, H=2, Lk=64, D=64, splits=0, ws=None, wsb=1 << 20, ptrs=None):
+    p = ptrs or [P(i) for i in range(7)]
+    return L.diffattn_decode(dtype, B, H, Lk, D, p[0], p[1], p[2], p[3], p[4], p[5], 0,
+                             ctypes.c_float(0.8), ctypes.c_float(1e-5), splits,
+                             ws if ws is not None else P(8), wsb, p[6], None)
+
+
+def test_decode_validation(L):
+    assert dec(L, Lk=0) == INVALID
+    assert dec(L, splits=-1) == INVALID
+    assert dec(L, Lk=10, splits=11) == INVALID
+    assert dec(L, D=80) == UNSUPPORTED
+    assert dec(L, ws=ctypes.c_void_p(0)) == WORKSPACE
+    need = da.diffattn_decode_workspace_bytes(1, 2, 64, 64, 4)
+    assert dec(L, splits=4, wsb=need - 1) == WORKSPACE
+    bad = [P(i) for i in range(7)]
+    bad[1] = P(1, 2)
+    assert dec(L, ptrs=bad) == UNSUPPORTED
+    assert dec(L, ws=P(8, 8)) == UNSUPPORTED
+    # workspace overlapping the value cache
+    assert dec(L, ws=P(4, 64)) == INVALID
+
+
+def test_lambda_validation(L):
+    p = [P(i) for i in range(5)]
+    f = ctypes.c_float(0.2)
+    assert L.diffattn_lambda(p[0], p[1], p[2], p[3], 0, 8, f, p[4], None) == INVALID
+    assert L.diffattn_lambda(p[0], p[1], p[2], p[3], 2, 0, f, p[4], None) == INVALID
+    assert L.diffattn_lambda(None, p[1], p[2], p[3], 2, 8, f, p[4], None) == INVALID
+    assert L.diffattn_lambda(p[0], p[1], p[2], p[3], 2, 8, f, P(0, 4), None) == INVALID
+    assert L.diffattn_lambda(p[0], p[1], p[2], p[3], 2, 8, f, P(4, 2), None) == UNSUPPORTED
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(TypeError):
+        da.diffattn_fwd(x, x, x, x, torch.zeros(1, 1, 4, 64), 0.5)

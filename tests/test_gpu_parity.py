@@ -1,0 +1,294 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Tolerances (max |GPU - oracle| over the compared elements): 1e-4 for fp32
+inputs, 2e-2 for bf16 inputs, both with fp32 accumulation.  Inputs are the
+same seeded tensors on both sides (bf16 values upcast exactly for the oracle).
+Full-size workloads are compared on sampled output rows, which the oracle
+computes one by one from the complete key range.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import differential_attention_forward_amd as da
+import oracle
+from workloads import WORKLOADS, decode_inputs, make_workload, prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    da.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(d):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) and k != "needle_pos" else v)
+            for k, v in d.items()}
+
+
+def maxerr(gpu_out, ref):
+    return float(np.max(np.abs(gpu_out.detach().float().cpu().numpy().astype(np.float64) - ref)))
+
+
+def run_fwd(x, lam, causal, headnorm, lambda_init=0.8, eps=1e-5):
+    out = da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, causal=causal,
+                          headnorm=headnorm, lambda_init=lambda_init, eps=eps)
+    torch.cuda.synchronize()
+    return out
+
+
+def ref_fwd(x, lam, causal, headnorm, lambda_init=0.8, eps=1e-5):
+    o = oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, causal)
+    return oracle.head_rmsnorm(o, lambda_init, eps) if headnorm else o
+
+
+# ---- sweep: dtype x head width x mask x head norm, ragged lengths -------------
+
+SWEEP_T = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 257, 1000]
+
+
+@pytest.mark.parametrize("headnorm", [False, True])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fwd_sweep(dtype, D, causal, headnorm):
+    lam = torch.tensor([0.35, 1.3], dtype=torch.float32)
+    worst = 0.0
+    for i, T in enumerate(SWEEP_T):
+        x = prefill_inputs(1, 2, T, D, dtype, seed=1000 + 17 * D + i)
+        say(f"fwd {dtype} D={D} T={T} causal={causal} headnorm={headnorm}")
+        out = run_fwd(to_dev(x), lam.to(DEV), causal, headnorm)
+        err = maxerr(out, ref_fwd(x, lam, causal, headnorm))
+        worst = max(worst, err)
+        assert err <= TOL[dtype], (T, err)
+    say(f"  worst {worst:.3e}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_lambda_range(dtype):
+    # lambda is not clamped: negative and > 1 values included
+    for lamv in (-0.3, 0.0, 0.2, 0.8, 1.0, 1.5):
+        x = prefill_inputs(2, 3, 300, 64, dtype, seed=77)
+        out = run_fwd(to_dev(x), lamv, True, False)
+        assert maxerr(out, ref_fwd(x, lamv, True, False)) <= TOL[dtype], lamv
+
+
+@pytest.mark.parametrize("headnorm", [False, True])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_identical_maps_cancel_exactly(dtype, causal, headnorm):
+    # paperleet page: identical maps cancel at lambda = 1
+    for D in (32, 64, 128):
+        x = to_dev(prefill_inputs(1, 2, 200, D, dtype, seed=5))
+        out = da.diffattn_fwd(x["q1"], x["k1"], x["q1"], x["k1"], x["v"], 1.0, causal=causal,
+                              headnorm=headnorm)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0, D
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_causal_first_row(dtype):
+    # row 0 sees only key 0 in both maps: O_0 = (1 - lambda) V_0
+    x = prefill_inputs(1, 2, 100, 64, dtype, seed=9)
+    out = run_fwd(to_dev(x), 0.6, True, False)
+    ref = 0.4 * x["v"][:, :, 0].double().numpy()
+    tol = 1e-6 if dtype == "fp32" else 2 ** -8 * np.abs(ref).max() + 1e-6
+    assert maxerr(out[:, :, 0], ref) <= tol
+
+
+def test_value_offset_property_fp32():
+    # a value offset shared by every token comes out as (1 - lambda) * offset
+    x = to_dev(prefill_inputs(1, 2, 2048, 64, "fp32", seed=13))
+    c = torch.randn(128, device=DEV)
+    lam = 0.3
+    base = run_fwd(x, lam, True, False)
+    x2 = dict(x, v=x["v"] + c)
+    shifted = run_fwd(x2, lam, True, False)
+    diff = (shifted - base - (1 - lam) * c).abs().max().item()
+    assert diff <= 1e-4, diff
+
+
+def test_repeatable_bitwise():
+    x = to_dev(prefill_inputs(2, 4, 1500, 64, "bf16", seed=21))
+    a = run_fwd(x, 0.7, True, True)
+    b = run_fwd(x, 0.7, True, True)
+    assert torch.equal(a, b)
+
+
+def test_fwd_rejects_empty():
+    x = to_dev(prefill_inputs(1, 1, 4, 32, "bf16", seed=1))
+    e = {k: v[:, :, :0] for k, v in x.items() if k in ("q1", "k1", "q2", "k2", "v")}
+    with pytest.raises(RuntimeError):
+        da.diffattn_fwd(e["q1"], e["k1"], e["q2"], e["k2"], e["v"], 0.5)
+
+
+# ---- lambda --------------------------------------------------------------------
+
+def test_lambda_kernel():
+    g = torch.Generator().manual_seed(3)
+    vecs = [torch.randn(16, 64, generator=g) * 0.1 for _ in range(4)]
+    li = oracle.lambda_init_schedule(12)
+    got = da.diffattn_lambda(*[v.to(DEV) for v in vecs], li)
+    ref = oracle.reparam_lambda(*vecs, li)
+    assert got.shape == (16,)
+    assert np.max(np.abs(got.cpu().double().numpy() - ref)) <= 1e-6
+    one = da.diffattn_lambda(*[v[0].to(DEV) for v in vecs], li)
+    assert one.shape == () and abs(one.item() - ref[0]) <= 1e-6
+    z = torch.zeros(16, 64, device=DEV)
+    lz = da.diffattn_lambda(z, z, z, z, 0.7993953)
+    assert torch.all(lz == torch.tensor(0.7993953, dtype=torch.float32))
+
+
+def test_lambda_chain_into_fwd():
+    w = WORKLOADS["tiny_fp32_causal"]
+    x = make_workload(w.name, "cpu")
+    xd = to_dev(x)
+    li_gpu = da.diffattn_lambda_init(w.layer)
+    lam_gpu = da.diffattn_lambda(xd["lq1"], xd["lk1"], xd["lq2"], xd["lk2"], li_gpu)
+    out = da.diffattn_fwd(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam_gpu,
+                          causal=w.causal, headnorm=w.headnorm)
+    torch.cuda.synchronize()
+    lam_ref = oracle.reparam_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"],
+                                    oracle.lambda_init_schedule(w.layer))
+    ref = oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_ref, w.causal)
+    err = maxerr(out, ref)
+    say(f"tiny fp32 workload: max err {err:.3e}")
+    assert err <= TOL["fp32"]
+
+
+# ---- decode --------------------------------------------------------------------
+
+@pytest.mark.parametrize("headnorm", [False, True])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_sweep(dtype, D, headnorm):
+    lam = torch.tensor([0.8, -0.2, 1.1], dtype=torch.float32)
+    for L, splits in ((1, 0), (1, 1), (7, 3), (300, 0), (1000, 8), (4097, 0), (4097, 64), (10, 8)):
+        x = decode_inputs(2, 3, L, D, dtype, seed=300 + L + D)
+        say(f"decode {dtype} D={D} L={L} splits={splits} headnorm={headnorm}")
+        xd = to_dev(x)
+        out = da.diffattn_decode(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV),
+                                 headnorm=headnorm, lambda_init=0.8, eps=1e-5, num_splits=splits)
+        torch.cuda.synchronize()
+        ref = oracle.diff_attention_decode(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam)
+        if headnorm:
+            ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+        err = maxerr(out, ref)
+        assert err <= TOL[dtype], (L, splits, err)
+
+
+def test_decode_split_invariance_and_last_row():
+    x = to_dev(prefill_inputs(2, 2, 777, 64, "fp32", seed=44))
+    fwd = run_fwd(x, 0.45, True, False)[:, :, -1]
+    outs = []
+    for s in (1, 2, 5, 16, 64, 777):
+        o = da.diffattn_decode(x["q1"][:, :, -1], x["k1"], x["q2"][:, :, -1], x["k2"], x["v"],
+                               0.45, num_splits=s)
+        torch.cuda.synchronize()
+        outs.append(o)
+        assert (o - fwd).abs().max().item() <= 1e-5, s
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() <= 1e-5
+
+
+# ---- the named workloads at full size (sampled rows) --------------------------
+
+def _sample_rows(T, rng, extra=()):
+    rows = set(range(min(T, 24))) | set(range(max(0, T - 16), T))
+    rows |= set(rng.choice(T, size=min(T, 64), replace=False).tolist())
+    rows |= {r for r in extra if 0 <= r < T}
+    return np.array(sorted(rows))
+
+
+def _check_prefill_workload(name, heads):
+    w = WORKLOADS[name]
+    x = make_workload(name, DEV)
+    if "lam" in x:
+        lam = x["lam"]
+        lam_ref = x["lam"].cpu().double().numpy()
+    else:
+        lam = da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], da.diffattn_lambda_init(w.layer))
+        lam_ref = oracle.reparam_lambda(x["lq1"].cpu(), x["lk1"].cpu(), x["lq2"].cpu(), x["lk2"].cpu(),
+                                        oracle.lambda_init_schedule(w.layer))
+    li = w.lambda_init if w.lambda_init is not None else oracle.lambda_init_schedule(w.layer)
+    say(f"workload {name}: launching")
+    out = da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, causal=w.causal,
+                          headnorm=w.headnorm, lambda_init=li, eps=w.eps)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(w.seed)
+    worst = 0.0
+    for (b, h) in heads:
+        extra = []
+        if "needle_pos" in x:
+            for j in x["needle_pos"][b, h].tolist():
+                extra += [j, j + 1, j + 100]
+        rows = _sample_rows(w.T, rng, extra)
+        sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
+        ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"],
+                                         lam_ref[h], w.causal, rows)
+        if w.headnorm:
+            ref = oracle.head_rmsnorm(ref, li, w.eps)
+        err = maxerr(out[b, h, rows], ref)
+        worst = max(worst, err)
+    say(f"workload {name}: max err {worst:.3e} over {len(heads)} heads")
+    del x, out
+    torch.cuda.empty_cache()
+    assert worst <= TOL[w.dtype]
+
+
+def test_workload_prefill_t4k():
+    _check_prefill_workload("prefill_t4k_causal", [(0, 0), (0, 7), (1, 3), (1, 15)])
+
+
+def test_workload_prefill_t32k_needles():
+    _check_prefill_workload("prefill_t32k_needles", [(0, 0), (0, 5), (0, 15)])
+
+
+def test_workload_full_t8k_d128():
+    _check_prefill_workload("full_t8k_d128", [(0, 0), (1, 4), (3, 7)])
+
+
+def test_workload_tiny_fp32():
+    w = WORKLOADS["tiny_fp32_causal"]
+    x = make_workload(w.name, "cpu")
+    xd = to_dev(x)
+    lam = da.diffattn_lambda(xd["lq1"], xd["lk1"], xd["lq2"], xd["lk2"], da.diffattn_lambda_init(1))
+    out = da.diffattn_fwd(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam, causal=True)
+    torch.cuda.synchronize()
+    lam_ref = oracle.reparam_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], oracle.lambda_init_schedule(1))
+    assert maxerr(out, oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_ref, True)) <= 1e-4
+
+
+def test_workload_decode_l64k():
+    w = WORKLOADS["decode_l64k"]
+    say("workload decode_l64k: generating 16 GiB cache")
+    x = make_workload(w.name, DEV)
+    li = da.diffattn_lambda_init(w.layer)
+    lam = da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], li)
+    out = da.diffattn_decode(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam,
+                             num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    lam_ref = oracle.lambda_init_schedule(w.layer)  # zero vectors: lambda = lambda_init
+    worst = 0.0
+    for (b, h) in ((0, 0), (5, 3), (17, 9), (31, 15)):
+        ref = oracle.diff_attention_decode(x["q1"][b:b + 1, h:h + 1].cpu(), x["k1"][b:b + 1, h:h + 1].cpu(),
+                                           x["q2"][b:b + 1, h:h + 1].cpu(), x["k2"][b:b + 1, h:h + 1].cpu(),
+                                           x["v"][b:b + 1, h:h + 1].cpu(), lam_ref)
+        worst = max(worst, maxerr(out[b:b + 1, h:h + 1], ref))
+    say(f"workload decode_l64k: max err {worst:.3e}")
+    del x
+    torch.cuda.empty_cache()
+    assert worst <= TOL["bf16"]
