@@ -212,6 +212,9 @@ def main():
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--primary-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times): the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -227,6 +230,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.ones(n // 4, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
     da.lib()
     primary = bench_workload(torch, da, args.workload, args.steps, args.warmup)
     also = {}
