@@ -45,11 +45,13 @@ namespace {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 2^8
 
-template <int D, int NQB, int NW, int BC, bool F32>
+template <int D, int NQB, int NW, int BC, bool F32, bool SPLIT>
 struct Cfg {
   static constexpr int DV = 2 * D;
   static constexpr int QPW = 32 * NQB;
-  static constexpr int BR = NW * QPW;
+  static constexpr int NBR = SPLIT ? 1 : 2;         // maps handled by one wave
+  static constexpr int NWQ = SPLIT ? NW / 2 : NW;   // waves per map
+  static constexpr int BR = NWQ * QPW;              // query rows per workgroup
   static constexpr int NT = NW * 64;
   static constexpr int ES = F32 ? 4 : 2;
   static constexpr int EPC = 16 / ES;               // elements per 16-byte chunk
@@ -68,8 +70,14 @@ struct Cfg {
   static constexpr int NKB = BC / 32;               // 32-key blocks per tile
   static constexpr int CB = DV / 32;                // 32-channel output blocks
   static constexpr int KSTEPS = F32 ? D / 2 : D / 16;
+  // split mode: map-2 waves hand acc2/l2 to their map-1 partners through LDS
+  static constexpr int XP = DV + 4;                 // exchange row pitch (floats)
+  static constexpr int XBYTES = SPLIT ? NWQ * QPW * XP * 4 : 0;
+  static constexpr int RBYTES = 2 * STAGE * ES;
+  static constexpr int SMEM = RBYTES > XBYTES ? RBYTES : XBYTES;
   static_assert(BC % 32 == 0, "key tile must hold whole 32-key blocks");
-  static_assert(STAGE * ES * 2 <= 160 * 1024, "LDS budget exceeded");
+  static_assert(!SPLIT || NW % 2 == 0, "split mode pairs waves");
+  static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
 // Position of key quad kq inside the transposed V row: within every group of
@@ -83,11 +91,12 @@ using QFrag = typename std::conditional<F32, float, bf16x8>::type;
 template <bool F32>
 using Elem = typename std::conditional<F32, float, bf16>::type;
 
-template <int D, int NQB, int NW, int BC, bool F32, bool CAUSAL, bool HEADNORM>
+template <int D, int NQB, int NW, int BC, bool F32, bool SPLIT, bool CAUSAL, bool HEADNORM>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
-  using C = Cfg<D, NQB, NW, BC, F32>;
+  using C = Cfg<D, NQB, NW, BC, F32, SPLIT>;
   using E = Elem<F32>;
-  __shared__ __attribute__((aligned(16))) E smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::SMEM];
+  E* const smem = (E*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,8 +120,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   const E* __restrict__ K2 = (const E*)a.k2 + qk_off;
   const E* __restrict__ V = (const E*)a.v + v_off;
 
+  // split mode: waves [0, NWQ) run map 1 and [NWQ, 2 NWQ) map 2 on the same rows
+  const int wbr = SPLIT ? wave / C::NWQ : 0;
+  const int wq = SPLIT ? wave % C::NWQ : wave;
   const int q_tile0 = qt * C::BR;
-  const int q0 = q_tile0 + wave * C::QPW;
+  const int q0 = q_tile0 + wq * C::QPW;
   const int q_last = min(q0 + C::QPW, T) - 1;
   const bool wave_active = q0 < T;
   const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
@@ -121,15 +133,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   const float lamv = a.lam[h];
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
-  QFrag<F32> qf[2][NQB][C::KSTEPS];
+  QFrag<F32> qf[C::NBR][NQB][C::KSTEPS];
 #pragma unroll
-  for (int br = 0; br < 2; ++br) {
+  for (int br = 0; br < C::NBR; ++br) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       // rows past the end read row T-1 (always in bounds) and are zeroed
       const int query = q0 + qb * 32 + l32;
       const bool ok = query < T;
-      const E* src = (br ? Q2 : Q1) + (size_t)min(query, T - 1) * D;
+      const E* src = ((br + wbr) ? Q2 : Q1) + (size_t)min(query, T - 1) * D;
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks) {
         if constexpr (F32) {
@@ -144,11 +156,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
     }
   }
 
-  floatx16 acc[2][NQB][C::CB];
-  float mu[2][NQB];
-  float lsum[2][NQB];
+  floatx16 acc[C::NBR][NQB][C::CB];
+  float mu[C::NBR][NQB];
+  float lsum[C::NBR][NQB];
 #pragma unroll
-  for (int br = 0; br < 2; ++br)
+  for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       mu[br][qb] = kNegInf;
@@ -247,37 +259,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
     const E* Ks1 = smem + buf * C::STAGE;
     const E* Ks2 = Ks1 + C::KTILE;
     const E* Vs = Ks2 + C::KTILE;
+    const E* Kmap[2] = {SPLIT && wbr ? Ks2 : Ks1, Ks2};  // K tile of each map this wave runs
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
       const int key0 = kt * BC + kb * 32;
       if (key0 >= T) break;
       if (CAUSAL && key0 > q_last) break;
 
-      // S^T = K Q^T for both maps
-      floatx16 s[2][NQB];
+      // S^T = K Q^T for the maps this wave runs
+      floatx16 s[C::NBR][NQB];
 #pragma unroll
-      for (int br = 0; br < 2; ++br)
+      for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[br][qb][r] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        if constexpr (F32) {
-          const float a1 = Ks1[(kb * 32 + l32) * C::KP + 2 * ks + hi];
-          const float a2 = Ks2[(kb * 32 + l32) * C::KP + 2 * ks + hi];
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            s[0][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, qf[0][qb][ks], s[0][qb], 0, 0, 0);
-            s[1][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a2, qf[1][qb][ks], s[1][qb], 0, 0, 0);
-          }
-        } else {
-          const bf16x8 a1 = *(const bf16x8*)(Ks1 + (kb * 32 + l32) * C::KP + ks * 16 + hi * 8);
-          const bf16x8 a2 = *(const bf16x8*)(Ks2 + (kb * 32 + l32) * C::KP + ks * 16 + hi * 8);
+        for (int br = 0; br < C::NBR; ++br) {
+          if constexpr (F32) {
+            const float av = Kmap[br][(kb * 32 + l32) * C::KP + 2 * ks + hi];
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            s[0][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[0][qb][ks], s[0][qb], 0, 0, 0);
-            s[1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, qf[1][qb][ks], s[1][qb], 0, 0, 0);
+            for (int qb = 0; qb < NQB; ++qb)
+              s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
+          } else {
+            const bf16x8 av = *(const bf16x8*)(Kmap[br] + (kb * 32 + l32) * C::KP + ks * 16 + hi * 8);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
           }
         }
       }
@@ -294,18 +304,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
             const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
             const bool masked = CAUSAL ? (key > query) : (key >= T);
             if (masked) {
-              s[0][qb][r] = kNegInf;
-              s[1][qb][r] = kNegInf;
+#pragma unroll
+              for (int br = 0; br < C::NBR; ++br) s[br][qb][r] = kNegInf;
             }
           }
         }
       }
 
-      // online softmax, two independent states per query row
-      float mx[2][NQB];
+      // online softmax: one independent state per map and query row
+      float mx[C::NBR][NQB];
       bool need = false;
 #pragma unroll
-      for (int br = 0; br < 2; ++br)
+      for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           float m = s[br][qb][0];
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
         }
       if (__any(need)) {
 #pragma unroll
-        for (int br = 0; br < 2; ++br)
+        for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) {
             const float mn = fmaxf(mu[br][qb], mx[br][qb]);
@@ -333,9 +343,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
       }
 
       if constexpr (F32) {
-        float p[2][NQB][16];
+        float p[C::NBR][NQB][16];
 #pragma unroll
-        for (int br = 0; br < 2; ++br)
+        for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) {
             const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
@@ -352,16 +362,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
             const int krow = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
             const float av = Vs[krow * C::VP + cb * 32 + l32];
 #pragma unroll
-            for (int br = 0; br < 2; ++br)
+            for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
               for (int qb = 0; qb < NQB; ++qb)
                 acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, p[br][qb][r], acc[br][qb][cb], 0, 0, 0);
           }
       } else {
-        bf16x8 pk[2][NQB][2];
+        bf16x8 pk[C::NBR][NQB][2];
         const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-        for (int br = 0; br < 2; ++br)
+        for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) {
             const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
@@ -384,7 +394,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
           for (int ks = 0; ks < 2; ++ks) {
             const bf16x8 av = *(const bf16x8*)(Vs + (cb * 32 + l32) * C::VP + kb * 32 + ks * 16 + hi * 8);
 #pragma unroll
-            for (int br = 0; br < 2; ++br)
+            for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
               for (int qb = 0; qb < NQB; ++qb)
                 acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[br][qb][ks], acc[br][qb][cb], 0, 0, 0);
@@ -404,6 +414,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
     if (more) store_tile((kt + 1) & 1);
     __syncthreads();
   }
+
+  // ---- split mode: map-2 waves hand t2 = acc2 / l2 to their map-1 partners ----
+  float* const xch = (float*)smem_raw;
+  if constexpr (SPLIT) {
+    if (wbr == 1 && wave_active) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float l2 = lsum[0][qb] + __shfl_xor(lsum[0][qb], 32);
+        const float inv2 = 1.0f / l2;
+        float* row = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const floatx4 t = {acc[0][qb][cb][4 * g] * inv2, acc[0][qb][cb][4 * g + 1] * inv2,
+                               acc[0][qb][cb][4 * g + 2] * inv2, acc[0][qb][cb][4 * g + 3] * inv2};
+            *(floatx4*)(row + cb * 32 + 8 * g + 4 * hi) = t;
+          }
+      }
+    }
+    __syncthreads();
+    if (wbr == 1) return;
+  }
   if (!wave_active) return;
 
   // ---- epilogue: combine the maps, optional head norm, store -----------------
@@ -412,17 +445,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   for (int qb = 0; qb < NQB; ++qb) {
     const int query = q0 + qb * 32 + l32;
     const float l1 = lsum[0][qb] + __shfl_xor(lsum[0][qb], 32);
-    const float l2 = lsum[1][qb] + __shfl_xor(lsum[1][qb], 32);
     const float inv1 = 1.0f / l1;
-    const float inv2 = 1.0f / l2;
+    float inv2 = 0.0f;
+    if constexpr (!SPLIT) {
+      const float l2 = lsum[1][qb] + __shfl_xor(lsum[1][qb], 32);
+      inv2 = 1.0f / l2;
+    }
+    const float* xrow = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
     float o[C::CB][16];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        // t1 - lam * t2 with both branches rounded identically (no contraction)
+        // t1 - lam * t2 with both maps rounded identically (no contraction)
         const float t1 = acc[0][qb][cb][r] * inv1;
-        const float t2 = acc[1][qb][cb][r] * inv2;
+        float t2;
+        if constexpr (SPLIT) t2 = xrow[cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)];
+        else t2 = acc[C::NBR - 1][qb][cb][r] * inv2;
         const float lt2 = lamv * t2;
         o[cb][r] = t1 - lt2;
       }
@@ -459,19 +498,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   }
 }
 
-template <int D, int NQB, int NW, int BC, bool F32>
+template <int D, int NQB, int NW, int BC, bool F32, bool SPLIT>
 hipError_t launch_cfg(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
-  using C = Cfg<D, NQB, NW, BC, F32>;
+  using C = Cfg<D, NQB, NW, BC, F32, SPLIT>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (causal) {
-    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, true, true><<<g, b, 0, stream>>>(a);
-    else fwd_kernel<D, NQB, NW, BC, F32, true, false><<<g, b, 0, stream>>>(a);
+    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, SPLIT, true, true><<<g, b, 0, stream>>>(a);
+    else fwd_kernel<D, NQB, NW, BC, F32, SPLIT, true, false><<<g, b, 0, stream>>>(a);
   } else {
-    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, false, true><<<g, b, 0, stream>>>(a);
-    else fwd_kernel<D, NQB, NW, BC, F32, false, false><<<g, b, 0, stream>>>(a);
+    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, SPLIT, false, true><<<g, b, 0, stream>>>(a);
+    else fwd_kernel<D, NQB, NW, BC, F32, SPLIT, false, false><<<g, b, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
@@ -482,15 +521,15 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
                       hipStream_t stream) {
   if (dtype == 1) {  // bf16
     switch (D) {
-      case 32: return launch_cfg<32, 1, 8, 64, false>(a, causal, headnorm, stream);
-      case 64: return launch_cfg<64, 1, 8, 64, false>(a, causal, headnorm, stream);
-      case 128: return launch_cfg<128, 1, 4, 64, false>(a, causal, headnorm, stream);
+      case 32: return launch_cfg<32, 1, 8, 64, false, false>(a, causal, headnorm, stream);
+      case 64: return launch_cfg<64, 1, 8, 64, false, false>(a, causal, headnorm, stream);
+      case 128: return launch_cfg<128, 1, 8, 64, false, true>(a, causal, headnorm, stream);
     }
   } else {  // fp32
     switch (D) {
-      case 32: return launch_cfg<32, 1, 4, 32, true>(a, causal, headnorm, stream);
-      case 64: return launch_cfg<64, 1, 4, 32, true>(a, causal, headnorm, stream);
-      case 128: return launch_cfg<128, 1, 4, 32, true>(a, causal, headnorm, stream);
+      case 32: return launch_cfg<32, 1, 4, 32, true, false>(a, causal, headnorm, stream);
+      case 64: return launch_cfg<64, 1, 4, 32, true, false>(a, causal, headnorm, stream);
+      case 128: return launch_cfg<128, 1, 4, 32, true, true>(a, causal, headnorm, stream);
     }
   }
   return hipErrorInvalidValue;
