@@ -498,6 +498,421 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   }
 }
 
+// ============================================================================
+// bf16 path: asynchronous global -> LDS staging
+// ============================================================================
+//
+// K1, K2 and V tiles of 64 keys go straight from global memory into LDS with
+// global_load_lds_dwordx4 (each wave instruction fills one contiguous KiB), so
+// no VGPRs are spent on staging and NSTAGE - 1 tiles are in flight while one
+// is computed.  Rows are XOR-swizzled at 16-byte granularity instead of
+// padded: K rows so that the 32 lanes reading one 16-byte column of 32 rows
+// (the S^T A operand) hit distinct banks, V rows so that the transposing
+// reads below are conflict free.  V stays key-major in LDS; the A operand of
+// O^T = V^T P^T is assembled by two ds_read_b64_tr_b16 per MFMA.  Within a
+// group of 16 lanes that instruction hands lane j element (j mod 4) of the
+// 8-byte chunks addressed by lanes 4k + j/4 (k = 0..3); addressing row
+// (key) 4*hi + k and column 4*(j/4) of each 16-column group gives every lane
+// four consecutive keys of its own channel, in the key order in which the
+// lane's probabilities reach the MFMA.
+
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT>
+struct CfgB {
+  static constexpr int BC = 64;
+  static constexpr int DV = 2 * D;
+  static constexpr int QPW = 32 * NQB;
+  static constexpr int NBR = SPLIT ? 1 : 2;
+  static constexpr int NWQ = SPLIT ? NW / 2 : NW;
+  static constexpr int BR = NWQ * QPW;
+  static constexpr int NT = NW * 64;
+  static constexpr int KBYTES = BC * D * 2;
+  static constexpr int VBYTES = BC * DV * 2;
+  static constexpr int STAGE = 2 * KBYTES + VBYTES;
+  static constexpr int KSEG = KBYTES / 1024;   // 1-KiB segments per K tile
+  static constexpr int NSEG = STAGE / 1024;    // per stage
+  static constexpr int SEGW = NSEG / NW;       // per wave per tile
+  static constexpr int CB = DV / 32;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int XP = DV + 4;
+  static constexpr int XBYTES = SPLIT ? NWQ * QPW * XP * 4 : 0;
+  static constexpr int RBYTES = NSTAGE * STAGE;
+  static constexpr int SMEM = RBYTES > XBYTES ? RBYTES : XBYTES;
+  static_assert(NSEG % NW == 0, "each wave issues the same number of tile loads");
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "double or triple buffering");
+  static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
+};
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// 16-byte column swizzles (see above)
+template <int D>
+__device__ inline int swz_k(int row) { return D == 32 ? ((row >> 1) & 3) : (row & 7); }
+__device__ inline int swz_v(int row) { return (row & 3) << 1; }
+
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's
+// 16 bytes land at lds + 16 i.  Issued through asm so that the compiler's
+// wait-count bookkeeping does not make every later LDS read wait for all tile
+// loads in flight; their completion is awaited explicitly (vmcnt) before the
+// tile barrier.
+__device__ inline void dma16(const void* gptr, const void* lds) {
+  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then a workgroup barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+template <int N>
+__device__ inline void wait_vm_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ inline float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1))) void fwd_bf16_kernel(FwdArgs a) {
+  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
+  constexpr int BC = C::BC;
+  constexpr int PD = NSTAGE - 1;  // prefetch distance in tiles
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int T = a.T;
+
+  const int nqt = (T + C::BR - 1) / C::BR;
+  const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
+  const int bh = w / nqt;
+  const int qi = w % nqt;
+  const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
+  const int h = bh % a.H;
+
+  const size_t qk_off = (size_t)bh * T * D;
+  const size_t v_off = (size_t)bh * T * C::DV;
+  const bf16* __restrict__ Q1 = (const bf16*)a.q1 + qk_off;
+  const bf16* __restrict__ Q2 = (const bf16*)a.q2 + qk_off;
+  const bf16* __restrict__ K1 = (const bf16*)a.k1 + qk_off;
+  const bf16* __restrict__ K2 = (const bf16*)a.k2 + qk_off;
+  const bf16* __restrict__ V = (const bf16*)a.v + v_off;
+
+  const int wbr = SPLIT ? wave / C::NWQ : 0;
+  const int wq = SPLIT ? wave % C::NWQ : wave;
+  const int q_tile0 = qt * C::BR;
+  const int q0 = q_tile0 + wq * C::QPW;
+  const int q_last = min(q0 + C::QPW, T) - 1;
+  const bool wave_active = q0 < T;
+  const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
+  const int ntiles = (k_end + BC - 1) / BC;
+  const float sc = a.score_scale;
+  const float lamv = a.lam[h];
+
+  // ---- asynchronous tile loads ------------------------------------------------
+  auto issue = [&](int kt, auto st) {
+    char* sb = smem + decltype(st)::value * C::STAGE;
+    const int key0 = kt * BC;
+#pragma unroll
+    for (int i = 0; i < C::SEGW; ++i) {
+      const int seg = wave + i * NW;
+      if (seg < 2 * C::KSEG) {
+        const int which = seg / C::KSEG;
+        const int ks = seg % C::KSEG;
+        const int p = ks * 64 + lane;
+        const int r = p / (D / 8);
+        const int c = (p % (D / 8)) ^ swz_k<D>(r);
+        const bf16* src = (which ? K2 : K1) + (size_t)min(key0 + r, T - 1) * D + c * 8;
+        dma16(src, sb + which * C::KBYTES + ks * 1024);
+      } else {
+        const int vs = seg - 2 * C::KSEG;
+        const int p = vs * 64 + lane;
+        const int r = p / (C::DV / 8);
+        const int c = (p % (C::DV / 8)) ^ swz_v(r);
+        const bf16* src = V + (size_t)min(key0 + r, T - 1) * C::DV + c * 8;
+        dma16(src, sb + 2 * C::KBYTES + vs * 1024);
+      }
+    }
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
+  bf16x8 qf[C::NBR][NQB][C::KSTEPS];
+#pragma unroll
+  for (int br = 0; br < C::NBR; ++br) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int query = q0 + qb * 32 + l32;
+      const bool ok = query < T;
+      const bf16* src = ((br + wbr) ? Q2 : Q1) + (size_t)min(query, T - 1) * D;
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
+        raw = ok ? raw : u32x4{0u, 0u, 0u, 0u};
+        qf[br][qb][ks] = __builtin_bit_cast(bf16x8, raw);
+      }
+    }
+  }
+
+  // Q is in registers before any tile load is issued, so the compiler's wait
+  // for it does not also wait for the asynchronous tile loads
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  issue(0, std::integral_constant<int, 0>{});
+  if constexpr (PD > 1)
+    if (1 < ntiles) issue(1, std::integral_constant<int, 1>{});
+
+  floatx16 acc[C::NBR][NQB][C::CB];
+  float mu[C::NBR][NQB];
+  float lsum[C::NBR][NQB];
+#pragma unroll
+  for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      mu[br][qb] = kNegInf;
+      lsum[br][qb] = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[br][qb][cb][r] = 0.0f;
+    }
+
+  // per-lane LDS offsets (bytes) that do not depend on the block
+  const int k_rd = l32 * (2 * D);                 // + kb*32 rows, + chunk ^ swizzle
+  const int swk = swz_k<D>(l32);
+  const int vq = lane & 3;
+  const int vkq = (lane >> 2) & 3;
+  const int v_row = 4 * hi + vkq;                 // + kb*32 + 16*ks + 8*t
+  const int v_chunk = 2 * ((lane >> 4) & 1) + (vq >> 1);  // + 4*cb
+  const int v_sw = swz_v(vkq);
+  const int v_byte = (vq & 1) * 8;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+  auto compute_tile = [&](int kt, auto st) {
+    const char* sb = smem + decltype(st)::value * C::STAGE;
+    const char* Kb[2] = {sb + (SPLIT && wbr ? C::KBYTES : 0), sb + C::KBYTES};
+    const char* Vb = sb + 2 * C::KBYTES;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      const int key0 = kt * BC + kb * 32;
+      if (key0 >= T) break;
+      if (CAUSAL && key0 > q_last) break;
+
+      floatx16 s[C::NBR][NQB];
+#pragma unroll
+      for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[br][qb][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+#pragma unroll
+        for (int br = 0; br < C::NBR; ++br) {
+          const bf16x8 av = *(const bf16x8*)(Kb[br] + kb * 32 * (2 * D) + k_rd + (((2 * ks + hi) ^ swk) << 4));
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
+        }
+      }
+
+      const bool need_mask = CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int query = q0 + qb * 32 + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool masked = CAUSAL ? (key > query) : (key >= T);
+            if (masked) {
+#pragma unroll
+              for (int br = 0; br < C::NBR; ++br) s[br][qb][r] = kNegInf;
+            }
+          }
+        }
+      }
+
+      float mx[C::NBR][NQB];
+      bool need = false;
+#pragma unroll
+      for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float m = s[br][qb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][qb][r]);
+          m = swap_halves_max(m) * sc;
+          mx[br][qb] = m;
+          need |= m > mu[br][qb] + kTau;
+        }
+      if (__any(need)) {
+#pragma unroll
+        for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float mn = fmaxf(mu[br][qb], mx[br][qb]);
+            const float alpha = (mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(mu[br][qb] - mn);
+            mu[br][qb] = mn;
+            lsum[br][qb] *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[br][qb][cb][r] *= alpha;
+          }
+      }
+
+      bf16x8 pk[C::NBR][NQB][2];
+#pragma unroll
+      for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float pa = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j], sc, -msub));
+              const float pb = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j + 1], sc, -msub));
+              const bf16x2 pw = {(bf16)pa, (bf16)pb};
+              lsum[br][qb] = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, lsum[br][qb], false);
+              pk[br][qb][ks][2 * j] = pw[0];
+              pk[br][qb][ks][2 * j + 1] = pw[1];
+            }
+          }
+        }
+
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const char* base = Vb + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) + (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+          const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
+          const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+#pragma unroll
+          for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[br][qb][ks], acc[br][qb][cb], 0, 0, 0);
+        }
+    }
+  };
+
+  // ---- main loop: tile kt computed while tiles kt+1 .. kt+PD load --------------
+  if (PD < ntiles) wait_vm_barrier<C::SEGW * (PD - 1)>();
+  else wait_vm_barrier<0>();
+  // unrolled by NSTAGE so that every stage offset is a compile-time constant
+  auto step = [&](int kt, auto st) {
+    constexpr int S = decltype(st)::value;
+    if (kt + PD < ntiles) issue(kt + PD, std::integral_constant<int, (S + PD) % NSTAGE>{});
+    if (wave_active) compute_tile(kt, st);
+    if (kt + PD < ntiles) wait_vm_barrier<C::SEGW * (PD - 1)>();
+    else wait_vm_barrier<0>();
+  };
+  for (int kt = 0; kt < ntiles; kt += NSTAGE) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NSTAGE > 2)
+      if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2>{});
+  }
+
+  // ---- split mode: map-2 waves hand t2 = acc2 / l2 to their map-1 partners ----
+  float* const xch = (float*)smem;
+  if constexpr (SPLIT) {
+    if (wbr == 1 && wave_active) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float inv2 = 1.0f / swap_halves_sum(lsum[0][qb]);
+        float* row = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const floatx4 t = {acc[0][qb][cb][4 * g] * inv2, acc[0][qb][cb][4 * g + 1] * inv2,
+                               acc[0][qb][cb][4 * g + 2] * inv2, acc[0][qb][cb][4 * g + 3] * inv2};
+            *(floatx4*)(row + cb * 32 + 8 * g + 4 * hi) = t;
+          }
+      }
+    }
+    __syncthreads();
+    if (wbr == 1) return;
+  }
+  if (!wave_active) return;
+
+  // ---- epilogue: combine the maps, optional head norm, store -----------------
+  bf16* __restrict__ O = (bf16*)a.out + v_off;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int query = q0 + qb * 32 + l32;
+    const float inv1 = 1.0f / swap_halves_sum(lsum[0][qb]);
+    float inv2 = 0.0f;
+    if constexpr (!SPLIT) inv2 = 1.0f / swap_halves_sum(lsum[1][qb]);
+    const float* xrow = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
+    float o[C::CB][16];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // t1 - lam * t2 with both maps rounded identically (no contraction)
+        const float t1 = acc[0][qb][cb][r] * inv1;
+        float t2;
+        if constexpr (SPLIT) t2 = xrow[cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)];
+        else t2 = acc[C::NBR - 1][qb][cb][r] * inv2;
+        const float lt2 = lamv * t2;
+        o[cb][r] = t1 - lt2;
+      }
+    if constexpr (HEADNORM) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss = fmaf(o[cb][r], o[cb][r], ss);
+      ss = swap_halves_sum(ss);
+      const float f = rsqrtf(ss * (1.0f / C::DV) + a.eps) * a.out_scale;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= f;
+    }
+    if (query < T) {
+      bf16* dst = O + (size_t)query * C::DV;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const bf16x4 v4 = {(bf16)o[cb][4 * g], (bf16)o[cb][4 * g + 1], (bf16)o[cb][4 * g + 2],
+                             (bf16)o[cb][4 * g + 3]};
+          *(bf16x4*)(dst + cb * 32 + 8 * g + 4 * hi) = v4;
+        }
+    }
+  }
+}
+
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT>
+hipError_t launch_bf16(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
+  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
+  const long nqt = (a.T + C::BR - 1) / C::BR;
+  const long grid = (long)a.B * a.H * nqt;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), b(C::NT);
+  if (causal) {
+    if (headnorm) fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, true><<<g, b, 0, stream>>>(a);
+    else fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, false><<<g, b, 0, stream>>>(a);
+  } else {
+    if (headnorm) fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, false, true><<<g, b, 0, stream>>>(a);
+    else fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, false, false><<<g, b, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int NQB, int NW, int BC, bool F32, bool SPLIT>
 hipError_t launch_cfg(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
   using C = Cfg<D, NQB, NW, BC, F32, SPLIT>;
@@ -521,9 +936,9 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
                       hipStream_t stream) {
   if (dtype == 1) {  // bf16
     switch (D) {
-      case 32: return launch_cfg<32, 1, 8, 64, false, false>(a, causal, headnorm, stream);
-      case 64: return launch_cfg<64, 1, 8, 64, false, false>(a, causal, headnorm, stream);
-      case 128: return launch_cfg<128, 1, 8, 64, false, true>(a, causal, headnorm, stream);
+      case 32: return launch_bf16<32, 1, 8, 3, false>(a, causal, headnorm, stream);
+      case 64: return launch_bf16<64, 1, 8, 3, false>(a, causal, headnorm, stream);
+      case 128: return launch_bf16<128, 1, 8, 2, true>(a, causal, headnorm, stream);
     }
   } else {  // fp32
     switch (D) {
