@@ -24,6 +24,8 @@
 // loads, dot products reduced across the group), then one block-wide max per
 // map, the exponentials, and finally the V pass (each lane owns 8 channels of
 // a V row).  Partial state is rescaled only when a sub-chunk raises the max.
+// Cache rows are read exactly once, with nontemporal 16-byte loads (no reuse
+// to keep in L2), eight in flight per lane.
 #include <type_traits>
 
 #include "common.h"
@@ -35,7 +37,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSub = 512;  // keys per sub-chunk (scores kept in LDS)
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
+constexpr int kMaxSplitsLds = 1024;  // per-split maxima staged in LDS by the reduce
 
 template <bool F32>
 using Elem = typename std::conditional<F32, float, bf16>::type;
@@ -124,8 +127,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
       for (int u = 0; u < kUnroll; ++u) {
         const int kk = min(k0 + u * KPR, n - 1);  // clamped: always in bounds
         const size_t off = (size_t)(base + kk) * D + ksub * EPC;
-        w1[u] = *(const u32x4*)(K1 + off);
-        w2[u] = *(const u32x4*)(K2 + off);
+        w1[u] = __builtin_nontemporal_load((const u32x4*)(K1 + off));
+        w2[u] = __builtin_nontemporal_load((const u32x4*)(K2 + off));
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int kk = min(k0 + u * VPR, n - 1);
-        wv[u] = *(const u32x4*)(V + (size_t)(base + kk) * DV + vsub * EPC);
+        wv[u] = __builtin_nontemporal_load((const u32x4*)(V + (size_t)(base + kk) * DV + vsub * EPC));
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -248,46 +251,92 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 }
 
 template <int D, bool F32, bool HEADNORM>
-__global__ __launch_bounds__(2 * D) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  // One workgroup per (b, h): 256 threads = 2D channels x (256 / 2D) split
+  // groups.  The per-split maxima are staged in LDS first; each thread then
+  // merges a fixed, contiguous range of splits for its channel (independent
+  // loads, unrolled), and the split groups are combined in a fixed order, so
+  // the result does not depend on timing.
   using E = Elem<F32>;
   constexpr int DV = 2 * D;
   constexpr int RS = 2 * (DV + 2);
-  constexpr int NWV = (DV + 63) / 64;
-  __shared__ float red[NWV];
+  constexpr int NG = 256 / DV;  // split groups
+  __shared__ float sm[2][kMaxSplitsLds];
+  __shared__ float part[NG][4][DV];
+  __shared__ float red[4];
 
   const int bh = blockIdx.x;
-  const int c = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int c = tid % DV;
+  const int grp = tid / DV;
   const int S = a.S;
   const float* __restrict__ rec = a.ws + (size_t)bh * S * RS;
 
   float M1 = kNegInf, M2 = kNegInf;
-  for (int s = 0; s < S; ++s) {
-    M1 = fmaxf(M1, rec[s * RS]);
-    M2 = fmaxf(M2, rec[s * RS + DV + 2]);
+  for (int s = tid; s < S; s += 256) {
+    const float m1 = rec[(size_t)s * RS], m2 = rec[(size_t)s * RS + DV + 2];
+    if (s < kMaxSplitsLds) {
+      sm[0][s] = m1;
+      sm[1][s] = m2;
+    }
+    M1 = fmaxf(M1, m1);
+    M2 = fmaxf(M2, m2);
   }
+  M1 = wave_max(M1);
+  M2 = wave_max(M2);
+  __shared__ float mred[4][2];
+  if ((tid & 63) == 0) {
+    mred[tid >> 6][0] = M1;
+    mred[tid >> 6][1] = M2;
+  }
+  __syncthreads();
+  M1 = fmaxf(fmaxf(mred[0][0], mred[1][0]), fmaxf(mred[2][0], mred[3][0]));
+  M2 = fmaxf(fmaxf(mred[0][1], mred[1][1]), fmaxf(mred[2][1], mred[3][1]));
+
+  const int per = (S + NG - 1) / NG;
+  const int s0 = grp * per;
+  const int s1 = min(S, s0 + per);
   float L1 = 0.0f, L2 = 0.0f, A1 = 0.0f, A2 = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float* r = rec + s * RS;
-    const float f1 = __builtin_amdgcn_exp2f(r[0] - M1);  // empty chunk: m = -inf -> 0
-    const float f2 = __builtin_amdgcn_exp2f(r[DV + 2] - M2);
+#pragma unroll 8
+  for (int s = s0; s < s1; ++s) {
+    const float* r = rec + (size_t)s * RS;
+    const float m1 = s < kMaxSplitsLds ? sm[0][s] : r[0];
+    const float m2 = s < kMaxSplitsLds ? sm[1][s] : r[DV + 2];
+    const float f1 = __builtin_amdgcn_exp2f(m1 - M1);  // empty chunk: m = -inf -> 0
+    const float f2 = __builtin_amdgcn_exp2f(m2 - M2);
     L1 = fmaf(f1, r[1], L1);
     A1 = fmaf(f1, r[2 + c], A1);
     L2 = fmaf(f2, r[DV + 3], L2);
     A2 = fmaf(f2, r[DV + 4 + c], A2);
   }
-  const float t1 = A1 * (1.0f / L1);
-  const float t2 = A2 * (1.0f / L2);
-  const float lt2 = a.lam[bh % a.H] * t2;
-  float o = t1 - lt2;
-  if constexpr (HEADNORM) {
-    float ss = wave_sum(o * o);
-    if ((c & 63) == 0) red[c >> 6] = ss;
-    __syncthreads();
-    ss = 0.0f;
+  part[grp][0][c] = L1;
+  part[grp][1][c] = A1;
+  part[grp][2][c] = L2;
+  part[grp][3][c] = A2;
+  __syncthreads();
+  // every thread stays for the barriers below; split group 0 finishes the row
+  float o = 0.0f;
+  if (grp == 0) {
+    L1 = A1 = L2 = A2 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NWV; ++i) ss += red[i];
-    o *= rsqrtf(ss * (1.0f / DV) + a.eps) * a.out_scale;
+    for (int g = 0; g < NG; ++g) {
+      L1 += part[g][0][c];
+      A1 += part[g][1][c];
+      L2 += part[g][2][c];
+      A2 += part[g][3][c];
+    }
+    const float t1 = A1 * (1.0f / L1);
+    const float t2 = A2 * (1.0f / L2);
+    const float lt2 = a.lam[bh % a.H] * t2;
+    o = t1 - lt2;
   }
+  if constexpr (HEADNORM) {
+    const float ss = wave_sum(o * o);  // threads outside group 0 contribute 0
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    o *= rsqrtf((red[0] + red[1] + red[2] + red[3]) * (1.0f / DV) + a.eps) * a.out_scale;
+  }
+  if (grp != 0) return;
   ((E*)a.out)[(size_t)bh * DV + c] = (E)o;
 }
 
@@ -298,7 +347,7 @@ hipError_t launch_d(const DecodeArgs& a, bool headnorm, hipStream_t stream) {
   decode_partial_kernel<D, F32><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g((unsigned)(a.B * a.H)), b(2 * D);
+  const dim3 g((unsigned)(a.B * a.H)), b(256);
   if (headnorm) decode_reduce_kernel<D, F32, true><<<g, b, 0, stream>>>(a);
   else decode_reduce_kernel<D, F32, false><<<g, b, 0, stream>>>(a);
   return hipGetLastError();
