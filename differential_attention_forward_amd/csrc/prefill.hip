@@ -530,14 +530,14 @@ struct CfgB {
   static constexpr int STAGE = 2 * KBYTES + VBYTES;
   static constexpr int KSEG = KBYTES / 1024;   // 1-KiB segments per K tile
   static constexpr int NSEG = STAGE / 1024;    // per stage
-  static constexpr int SEGW = NSEG / NW;       // per wave per tile
+  static constexpr int SEGW = (NSEG + NW - 1) / NW;  // most loads one wave issues per tile
+  static constexpr int SEGW_MIN = NSEG / NW;          // fewest (waits use this: safe)
   static constexpr int CB = DV / 32;
   static constexpr int KSTEPS = D / 16;
   static constexpr int XP = DV + 4;
   static constexpr int XBYTES = SPLIT ? NWQ * QPW * XP * 4 : 0;
   static constexpr int RBYTES = NSTAGE * STAGE;
   static constexpr int SMEM = RBYTES > XBYTES ? RBYTES : XBYTES;
-  static_assert(NSEG % NW == 0, "each wave issues the same number of tile loads");
   static_assert(NSTAGE == 2 || NSTAGE == 3, "double or triple buffering");
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
@@ -579,7 +579,7 @@ __device__ inline float swap_halves_sum(float x) {
 }
 
 template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1))) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
   constexpr int BC = C::BC;
   constexpr int PD = NSTAGE - 1;  // prefetch distance in tiles
@@ -625,6 +625,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
 #pragma unroll
     for (int i = 0; i < C::SEGW; ++i) {
       const int seg = wave + i * NW;
+      if (seg >= C::NSEG) break;
       if (seg < 2 * C::KSEG) {
         const int which = seg / C::KSEG;
         const int ks = seg % C::KSEG;
@@ -807,14 +808,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   };
 
   // ---- main loop: tile kt computed while tiles kt+1 .. kt+PD load --------------
-  if (PD < ntiles) wait_vm_barrier<C::SEGW * (PD - 1)>();
+  if (PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
   else wait_vm_barrier<0>();
   // unrolled by NSTAGE so that every stage offset is a compile-time constant
   auto step = [&](int kt, auto st) {
     constexpr int S = decltype(st)::value;
     if (kt + PD < ntiles) issue(kt + PD, std::integral_constant<int, (S + PD) % NSTAGE>{});
     if (wave_active) compute_tile(kt, st);
-    if (kt + PD < ntiles) wait_vm_barrier<C::SEGW * (PD - 1)>();
+    if (kt + PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
     else wait_vm_barrier<0>();
   };
   for (int kt = 0; kt < ntiles; kt += NSTAGE) {
@@ -937,7 +938,12 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
   if (dtype == 1) {  // bf16
     switch (D) {
       case 32: return launch_bf16<32, 1, 8, 3, false>(a, causal, headnorm, stream);
-      case 64: return launch_bf16<64, 1, 8, 3, false>(a, causal, headnorm, stream);
+      case 64:
+        // short causal rows: one map per wave, three waves per SIMD (more
+        // latency hiding); long rows and full attention: both maps per wave
+        // (less LDS traffic per MFMA)
+        if (causal && a.T <= 4096) return launch_bf16<64, 1, 12, 3, true>(a, causal, headnorm, stream);
+        return launch_bf16<64, 1, 8, 3, false>(a, causal, headnorm, stream);
       case 128: return launch_bf16<128, 1, 8, 2, true>(a, causal, headnorm, stream);
     }
   } else {  // fp32

@@ -76,6 +76,25 @@ def test_fwd_sweep(dtype, D, causal, headnorm):
     say(f"  worst {worst:.3e}")
 
 
+@pytest.mark.parametrize("headnorm", [False, True])
+def test_fwd_long_causal_rows(headnorm):
+    # causal rows longer than 4096 take the two-maps-per-wave configuration at
+    # D=64 (shorter ones the one-map-per-wave one); sampled rows, full key range
+    lam = torch.tensor([0.55, -0.25], dtype=torch.float32)
+    for T, seed in ((4097, 31), (5000, 32)):
+        x = prefill_inputs(1, 2, T, 64, "bf16", seed=seed)
+        say(f"fwd bf16 D=64 T={T} causal headnorm={headnorm}")
+        out = run_fwd(to_dev(x), lam.to(DEV), True, headnorm)
+        rows = np.unique(np.concatenate([np.arange(40), np.arange(T - 40, T),
+                                         np.random.default_rng(seed).choice(T, 200, replace=False)]))
+        for h in range(2):
+            ref = oracle.diff_attention_rows(x["q1"][0, h], x["k1"][0, h], x["q2"][0, h], x["k2"][0, h],
+                                             x["v"][0, h], float(lam[h]), True, rows)
+            if headnorm:
+                ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+            assert maxerr(out[0, h, rows], ref) <= TOL["bf16"], (T, h)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_lambda_range(dtype):
     # lambda is not clamped: negative and > 1 values included
