@@ -36,7 +36,7 @@ PRIMARY = "prefill_t4k_causal"
 OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k"]
 CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
 KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip"}
-KERNEL_NAME = {"prefill": "fwd_kernel", "decode": "decode_partial_kernel"}
+KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel"}
 
 
 def log(*a):
