@@ -538,7 +538,7 @@ struct CfgB {
   static constexpr int XBYTES = SPLIT ? NWQ * QPW * XP * 4 : 0;
   static constexpr int RBYTES = NSTAGE * STAGE;
   static constexpr int SMEM = RBYTES > XBYTES ? RBYTES : XBYTES;
-  static_assert(NSTAGE == 2 || NSTAGE == 3, "double or triple buffering");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "two to four stages");
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -549,14 +549,26 @@ template <int D>
 __device__ inline int swz_k(int row) { return D == 32 ? ((row >> 1) & 3) : (row & 7); }
 __device__ inline int swz_v(int row) { return (row & 3) << 1; }
 
-// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's
-// 16 bytes land at lds + 16 i.  Issued through asm so that the compiler's
-// wait-count bookkeeping does not make every later LDS read wait for all tile
-// loads in flight; their completion is awaited explicitly (vmcnt) before the
-// tile barrier.
-__device__ inline void dma16(const void* gptr, const void* lds) {
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i
+// reads base + off_i (base uniform, kept in SGPRs; off_i an unsigned 32-bit
+// byte offset) and its 16 bytes land at lds + 16 i.  Issued through asm so that
+// the compiler's wait-count bookkeeping does not make every later LDS read wait
+// for all tile loads in flight; their completion is awaited explicitly
+// (vmcnt) before the tile barrier.
+__device__ inline void dma16(const void* base, uint32_t off, const void* lds) {
   const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory", "m0");
+}
+
+// A pointer that is the same in every lane, moved to scalar registers (64-bit
+// address arithmetic runs on the VALU, which would keep it in VGPRs).
+template <typename Tp>
+__device__ inline const Tp* scalar_ptr(const Tp* p) {
+  // readfirstlane returns int: widen through uint32_t, not by sign extension
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const Tp*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then a workgroup barrier; the empty asm
@@ -603,9 +615,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const size_t v_off = (size_t)bh * T * C::DV;
   const bf16* __restrict__ Q1 = (const bf16*)a.q1 + qk_off;
   const bf16* __restrict__ Q2 = (const bf16*)a.q2 + qk_off;
-  const bf16* __restrict__ K1 = (const bf16*)a.k1 + qk_off;
-  const bf16* __restrict__ K2 = (const bf16*)a.k2 + qk_off;
-  const bf16* __restrict__ V = (const bf16*)a.v + v_off;
+  const bf16* __restrict__ K1 = scalar_ptr((const bf16*)a.k1 + qk_off);
+  const bf16* __restrict__ K2 = scalar_ptr((const bf16*)a.k2 + qk_off);
+  const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + v_off);
 
   const int wbr = SPLIT ? wave / C::NWQ : 0;
   const int wq = SPLIT ? wave % C::NWQ : wave;
@@ -619,8 +631,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const float lamv = a.lam[h];
 
   // ---- asynchronous tile loads ------------------------------------------------
-  auto issue = [&](int kt, auto st) {
-    char* sb = smem + decltype(st)::value * C::STAGE;
+  // Segment g of a K tile (1 KiB) holds rows RK g .. RK g + RK - 1; lane l
+  // copies row RK g + l / CK, 16-byte column (l % CK) ^ swz_k(row).  The
+  // swizzle depends on g only through its parity (D = 128), so a lane's
+  // column offset takes one of two values; likewise for V.  Keys past the end
+  // load row T-1 (in bounds); their scores are masked.
+  constexpr int CK = D / 8, RK = 64 / CK, CV = C::DV / 8, RV = 64 / CV;
+  const int rl_k = lane / CK, rl_v = lane / CV;
+  auto issue_rt = [&](int kt, char* sb) __attribute__((always_inline)) {
     const int key0 = kt * BC;
 #pragma unroll
     for (int i = 0; i < C::SEGW; ++i) {
@@ -628,21 +646,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (seg >= C::NSEG) break;
       if (seg < 2 * C::KSEG) {
         const int which = seg / C::KSEG;
-        const int ks = seg % C::KSEG;
-        const int p = ks * 64 + lane;
-        const int r = p / (D / 8);
-        const int c = (p % (D / 8)) ^ swz_k<D>(r);
-        const bf16* src = (which ? K2 : K1) + (size_t)min(key0 + r, T - 1) * D + c * 8;
-        dma16(src, sb + which * C::KBYTES + ks * 1024);
+        const int g = seg % C::KSEG;
+        const int r = g * RK + rl_k;
+        const int c = (lane % CK) ^ swz_k<D>((g & 1) * RK + rl_k);
+        const uint32_t row = (uint32_t)min(key0 + r, T - 1);
+        dma16(which ? K2 : K1, row * (D * 2) + c * 16, sb + which * C::KBYTES + g * 1024);
       } else {
-        const int vs = seg - 2 * C::KSEG;
-        const int p = vs * 64 + lane;
-        const int r = p / (C::DV / 8);
-        const int c = (p % (C::DV / 8)) ^ swz_v(r);
-        const bf16* src = V + (size_t)min(key0 + r, T - 1) * C::DV + c * 8;
-        dma16(src, sb + 2 * C::KBYTES + vs * 1024);
+        const int g = seg - 2 * C::KSEG;
+        const int r = g * RV + rl_v;
+        const int c = (lane % CV) ^ swz_v((g & 1) * RV + rl_v);
+        const uint32_t row = (uint32_t)min(key0 + r, T - 1);
+        dma16(V, row * (C::DV * 2) + c * 16, sb + 2 * C::KBYTES + g * 1024);
       }
     }
+  };
+  auto issue = [&](int kt, auto st) __attribute__((always_inline)) {
+    issue_rt(kt, smem + decltype(st)::value * C::STAGE);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
@@ -696,125 +715,143 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int v_byte = (vq & 1) * 8;
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  auto compute_tile = [&](int kt, auto st) {
-    const char* sb = smem + decltype(st)::value * C::STAGE;
-    const char* Kb[2] = {sb + (SPLIT && wbr ? C::KBYTES : 0), sb + C::KBYTES};
-    const char* Vb = sb + 2 * C::KBYTES;
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
-      const int key0 = kt * BC + kb * 32;
-      if (key0 >= T) break;
-      if (CAUSAL && key0 > q_last) break;
+  // A 32-key block kb of tile kt takes part only if it holds a key this wave
+  // may attend to.
+  auto kb_live = [&](int kt, int kb) __attribute__((always_inline)) {
+    const int key0 = kt * BC + kb * 32;
+    return key0 < T && (!CAUSAL || key0 <= q_last);
+  };
 
-      floatx16 s[C::NBR][NQB];
+  // S^T of block kb for both maps (raw dot products, scale applied later)
+  auto qk = [&](int kb, const char* sb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
+    const char* Kb[2] = {sb + (SPLIT && wbr ? C::KBYTES : 0), sb + C::KBYTES};
 #pragma unroll
-      for (int br = 0; br < C::NBR; ++br)
+    for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[br][qb][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+#pragma unroll
+      for (int br = 0; br < C::NBR; ++br) {
+        const bf16x8 av = *(const bf16x8*)(Kb[br] + kb * 32 * (2 * D) + k_rd + (((2 * ks + hi) ^ swk) << 4));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[br][qb][r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-#pragma unroll
-        for (int br = 0; br < C::NBR; ++br) {
-          const bf16x8 av = *(const bf16x8*)(Kb[br] + kb * 32 * (2 * D) + k_rd + (((2 * ks + hi) ^ swk) << 4));
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
-        }
+          s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
       }
-
-      const bool need_mask = CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T);
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const int query = q0 + qb * 32 + l32;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool masked = CAUSAL ? (key > query) : (key >= T);
-            if (masked) {
-#pragma unroll
-              for (int br = 0; br < C::NBR; ++br) s[br][qb][r] = kNegInf;
-            }
-          }
-        }
-      }
-
-      float mx[C::NBR][NQB];
-      bool need = false;
-#pragma unroll
-      for (int br = 0; br < C::NBR; ++br)
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          float m = s[br][qb][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][qb][r]);
-          m = swap_halves_max(m) * sc;
-          mx[br][qb] = m;
-          need |= m > mu[br][qb] + kTau;
-        }
-      if (__any(need)) {
-#pragma unroll
-        for (int br = 0; br < C::NBR; ++br)
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            const float mn = fmaxf(mu[br][qb], mx[br][qb]);
-            const float alpha = (mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(mu[br][qb] - mn);
-            mu[br][qb] = mn;
-            lsum[br][qb] *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[br][qb][cb][r] *= alpha;
-          }
-      }
-
-      bf16x8 pk[C::NBR][NQB][2];
-#pragma unroll
-      for (int br = 0; br < C::NBR; ++br)
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float pa = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j], sc, -msub));
-              const float pb = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j + 1], sc, -msub));
-              const bf16x2 pw = {(bf16)pa, (bf16)pb};
-              lsum[br][qb] = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, lsum[br][qb], false);
-              pk[br][qb][ks][2 * j] = pw[0];
-              pk[br][qb][ks][2 * j + 1] = pw[1];
-            }
-          }
-        }
-
-#pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const char* base = Vb + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) + (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
-          const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
-          const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-#pragma unroll
-          for (int br = 0; br < C::NBR; ++br)
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[br][qb][ks], acc[br][qb][cb], 0, 0, 0);
-        }
     }
   };
 
-  // ---- main loop: tile kt computed while tiles kt+1 .. kt+PD load --------------
+  // mask, running maxima (lazy rescale of acc and lsum), probabilities P^T as
+  // the bf16 B operand of the P.V product, row sums of those bf16 values
+  auto softmax = [&](int kt, int kb, floatx16 (&s)[C::NBR][NQB], bf16x8 (&pk)[C::NBR][NQB][2])
+      __attribute__((always_inline)) {
+    const int key0 = kt * BC + kb * 32;
+    const bool need_mask = CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int query = q0 + qb * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool masked = CAUSAL ? (key > query) : (key >= T);
+          if (masked) {
+#pragma unroll
+            for (int br = 0; br < C::NBR; ++br) s[br][qb][r] = kNegInf;
+          }
+        }
+      }
+    }
+
+    float mx[C::NBR][NQB];
+    bool need = false;
+#pragma unroll
+    for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float m = s[br][qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][qb][r]);
+        m = swap_halves_max(m) * sc;
+        mx[br][qb] = m;
+        need |= m > mu[br][qb] + kTau;
+      }
+    if (__any(need)) {
+#pragma unroll
+      for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float mn = fmaxf(mu[br][qb], mx[br][qb]);
+          const float alpha = (mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(mu[br][qb] - mn);
+          mu[br][qb] = mn;
+          lsum[br][qb] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[br][qb][cb][r] *= alpha;
+        }
+    }
+
+#pragma unroll
+    for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float pa = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j], sc, -msub));
+            const float pb = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j + 1], sc, -msub));
+            const bf16x2 pw = {(bf16)pa, (bf16)pb};
+            lsum[br][qb] = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, lsum[br][qb], false);
+            pk[br][qb][ks][2 * j] = pw[0];
+            pk[br][qb][ks][2 * j + 1] = pw[1];
+          }
+        }
+      }
+  };
+
+  // acc += P^T-weighted V rows of block kb; each V fragment serves both maps
+  auto pv = [&](int kb, const char* sb, const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
+    const char* Vb = sb + 2 * C::KBYTES;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char* base = Vb + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) + (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
+        const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+#pragma unroll
+        for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[br][qb][ks], acc[br][qb][cb], 0, 0, 0);
+      }
+  };
+
   if (PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
   else wait_vm_barrier<0>();
+  // ---- main loop: tile kt computed while tiles kt+1 .. kt+PD load ------------
+  auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      if (!kb_live(kt, kb)) break;
+      floatx16 s[C::NBR][NQB];
+      bf16x8 pk[C::NBR][NQB][2];
+      qk(kb, sb, s);
+      softmax(kt, kb, s, pk);
+      pv(kb, sb, pk);
+    }
+  };
   // unrolled by NSTAGE so that every stage offset is a compile-time constant
-  auto step = [&](int kt, auto st) {
+  auto step = [&](int kt, auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
     if (kt + PD < ntiles) issue(kt + PD, std::integral_constant<int, (S + PD) % NSTAGE>{});
-    if (wave_active) compute_tile(kt, st);
+    if (wave_active) compute_tile(kt, smem + S * C::STAGE);
     if (kt + PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
     else wait_vm_barrier<0>();
   };
@@ -823,6 +860,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
     if constexpr (NSTAGE > 2)
       if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2>{});
+    if constexpr (NSTAGE > 3)
+      if (kt + 3 < ntiles) step(kt + 3, std::integral_constant<int, 3>{});
   }
 
   // ---- split mode: map-2 waves hand t2 = acc2 / l2 to their map-1 partners ----
