@@ -685,9 +685,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // Q is in registers before any tile load is issued, so the compiler's wait
   // for it does not also wait for the asynchronous tile loads
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  // prologue: tiles 0 .. PD-1 into stages 0 .. PD-1
   issue(0, std::integral_constant<int, 0>{});
   if constexpr (PD > 1)
     if (1 < ntiles) issue(1, std::integral_constant<int, 1>{});
+  if constexpr (PD > 2)
+    if (2 < ntiles) issue(2, std::integral_constant<int, 2>{});
 
   floatx16 acc[C::NBR][NQB][C::CB];
   float mu[C::NBR][NQB];
@@ -979,10 +982,11 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
       case 32: return launch_bf16<32, 1, 8, 3, false>(a, causal, headnorm, stream);
       case 64:
         // short causal rows: one map per wave, three waves per SIMD (more
-        // latency hiding); long rows and full attention: both maps per wave
-        // (less LDS traffic per MFMA)
+        // latency hiding); long causal rows: both maps per wave (less LDS
+        // traffic per MFMA); full attention: one map and 64 rows per wave
         if (causal && a.T <= 4096) return launch_bf16<64, 1, 12, 3, true>(a, causal, headnorm, stream);
-        return launch_bf16<64, 1, 8, 3, false>(a, causal, headnorm, stream);
+        if (causal) return launch_bf16<64, 1, 8, 3, false>(a, causal, headnorm, stream);
+        return launch_bf16<64, 2, 8, 3, true>(a, causal, headnorm, stream);
       case 128: return launch_bf16<128, 1, 8, 2, true>(a, causal, headnorm, stream);
     }
   } else {  // fp32
