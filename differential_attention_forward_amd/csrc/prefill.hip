@@ -8,35 +8,32 @@
 // x (1 - lambda_init) (aifetchly "Differential Transformer: Canceling LLM
 // Attention Noise", section 4).
 //
-// Design (one pass over K/V, both maps at once):
+// Design shared by both kernels (one pass over K/V, both maps at once):
 //  * One workgroup = NW waves = BR query rows of one (b, h); each wave owns
 //    32*NQB queries.  Q1/Q2 fragments stay in VGPRs for the whole kernel.
-//  * K1, K2 and V tiles of BC keys are staged global -> VGPR -> LDS, double
-//    buffered: the global loads of tile t+1 are in flight while tile t is
-//    computed, one barrier per tile.  V is written to LDS transposed
-//    ([channel][key]) so that it can be the A operand of the P.V MFMA.
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: lane l then holds 16 keys of query l%32, so the
-//    row max is an in-lane reduction plus one exchange with lane l^32, and
-//    the probabilities P^T land in exactly the register layout the P.V MFMA
-//    wants as its B operand (no data movement).
+//    Either every wave runs both maps, or (split mode) waves pair up, one per
+//    map, on the same rows and the map-2 wave hands t2 = acc2 / l2 to its
+//    partner through LDS at the end.
+//  * Scores are computed transposed, S^T = K Q^T: lane l then holds 16 keys
+//    of query l%32, so the row max is an in-lane reduction plus one exchange
+//    with lane l^32, and the probabilities P^T land in exactly the register
+//    layout the P.V MFMA wants as its B operand (no data movement).
 //  * Two independent online-softmax states per query row (one per map) with
 //    lazy rescaling: the running max only moves (and the accumulators are
 //    only rescaled) when a block max exceeds it by more than kTau (log2
 //    units), so steady-state blocks do no rescale work.
-//  * The row sums are taken over the bf16-rounded probabilities actually fed
-//    to the MFMA (v_dot2_f32_bf16 against 1.0), so a value offset shared by
-//    all keys passes through with weights that sum exactly to one.
 //  * Both P1.V and P2.V are fed from one V tile in LDS: each V fragment read
 //    serves both branches (V is read from memory once, not once per map).
 //  * Causal: key blocks above a wave's last query are skipped; only blocks
 //    that straddle the diagonal evaluate the mask.  Query tiles are issued
 //    heaviest first and workgroups are remapped so that each XCD works
 //    through consecutive tiles of the same heads (K/V reuse in its L2).
-//  * fp32 inputs use the same structure with v_mfma_f32_32x32x2_f32 and
-//    fp32 probabilities (V kept row-major in LDS).
-#include <type_traits>
-
+//
+// bf16 (fwd_bf16_kernel): K1, K2, V tiles of 64 keys go global -> LDS
+// directly (asynchronous DMA, NSTAGE-deep ring), v_mfma_f32_32x32x16_bf16,
+// probabilities rounded to bf16 for the P.V product and summed as rounded.
+// fp32 (fwd_f32_kernel): tiles of 32 keys staged global -> VGPR -> LDS,
+// double buffered, v_mfma_f32_32x32x2_f32, fp32 probabilities.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,7 +42,7 @@ namespace {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 2^8
 
-template <int D, int NQB, int NW, int BC, bool F32, bool SPLIT>
+template <int D, int NQB, int NW, int BC, bool SPLIT>
 struct Cfg {
   static constexpr int DV = 2 * D;
   static constexpr int QPW = 32 * NQB;
@@ -53,23 +50,20 @@ struct Cfg {
   static constexpr int NWQ = SPLIT ? NW / 2 : NW;   // waves per map
   static constexpr int BR = NWQ * QPW;              // query rows per workgroup
   static constexpr int NT = NW * 64;
-  static constexpr int ES = F32 ? 4 : 2;
+  static constexpr int ES = 4;
   static constexpr int EPC = 16 / ES;               // elements per 16-byte chunk
-  static constexpr int KP = F32 ? D + 4 : D + 8;    // K row pitch (elements)
-  // V in LDS: fp32 row-major [BC][DV]; bf16 transposed [DV][BC]
-  static constexpr int VP = F32 ? DV + 4 : BC + 8;
+  static constexpr int KP = D + 4;                 // K row pitch (floats)
+  static constexpr int VP = DV + 4;                 // V row pitch (floats), row-major [BC][DV]
   static constexpr int KTILE = BC * KP;
-  static constexpr int VTILE = F32 ? BC * VP : DV * VP;
+  static constexpr int VTILE = BC * VP;
   static constexpr int STAGE = 2 * KTILE + VTILE;   // elements per LDS stage
   static constexpr int NKC = BC * D / EPC;          // 16-B chunks per K tile
   static constexpr int NKPT = (NKC + NT - 1) / NT;
-  // V staging units: fp32 plain 16-B chunks; bf16 blocks of 4 keys x 8 channels
-  static constexpr int NVU = F32 ? BC * DV / EPC : (BC / 4) * (DV / 8);
+  static constexpr int NVU = BC * DV / EPC;         // 16-B chunks per V tile
   static constexpr int NVPT = (NVU + NT - 1) / NT;
-  static constexpr int VREG = F32 ? 1 : 4;
   static constexpr int NKB = BC / 32;               // 32-key blocks per tile
   static constexpr int CB = DV / 32;                // 32-channel output blocks
-  static constexpr int KSTEPS = F32 ? D / 2 : D / 16;
+  static constexpr int KSTEPS = D / 2;
   // split mode: map-2 waves hand acc2/l2 to their map-1 partners through LDS
   static constexpr int XP = DV + 4;                 // exchange row pitch (floats)
   static constexpr int XBYTES = SPLIT ? NWQ * QPW * XP * 4 : 0;
@@ -80,23 +74,11 @@ struct Cfg {
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
-// Position of key quad kq inside the transposed V row: within every group of
-// 4 quads (16 keys) the middle two are swapped, which is the key order in
-// which one lane's 8 probabilities reach the MFMA (keys 0-3 and 8-11 in the
-// lower lane half, 4-7 and 12-15 in the upper half).
-__device__ inline int vt_quad_pos(int kq) { return kq ^ ((((kq >> 1) ^ kq) & 1) * 3); }
-
-template <bool F32>
-using QFrag = typename std::conditional<F32, float, bf16x8>::type;
-template <bool F32>
-using Elem = typename std::conditional<F32, float, bf16>::type;
-
-template <int D, int NQB, int NW, int BC, bool F32, bool SPLIT, bool CAUSAL, bool HEADNORM>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
-  using C = Cfg<D, NQB, NW, BC, F32, SPLIT>;
-  using E = Elem<F32>;
+template <int D, int NQB, int NW, int BC, bool SPLIT, bool CAUSAL, bool HEADNORM>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1))) void fwd_f32_kernel(FwdArgs a) {
+  using C = Cfg<D, NQB, NW, BC, SPLIT>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::SMEM];
-  E* const smem = (E*)smem_raw;
+  float* const smem = (float*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,11 +96,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
 
   const size_t qk_off = (size_t)bh * T * D;
   const size_t v_off = (size_t)bh * T * C::DV;
-  const E* __restrict__ Q1 = (const E*)a.q1 + qk_off;
-  const E* __restrict__ Q2 = (const E*)a.q2 + qk_off;
-  const E* __restrict__ K1 = (const E*)a.k1 + qk_off;
-  const E* __restrict__ K2 = (const E*)a.k2 + qk_off;
-  const E* __restrict__ V = (const E*)a.v + v_off;
+  const float* __restrict__ Q1 = (const float*)a.q1 + qk_off;
+  const float* __restrict__ Q2 = (const float*)a.q2 + qk_off;
+  const float* __restrict__ K1 = (const float*)a.k1 + qk_off;
+  const float* __restrict__ K2 = (const float*)a.k2 + qk_off;
+  const float* __restrict__ V = (const float*)a.v + v_off;
 
   // split mode: waves [0, NWQ) run map 1 and [NWQ, 2 NWQ) map 2 on the same rows
   const int wbr = SPLIT ? wave / C::NWQ : 0;
@@ -133,7 +115,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   const float lamv = a.lam[h];
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
-  QFrag<F32> qf[C::NBR][NQB][C::KSTEPS];
+  float qf[C::NBR][NQB][C::KSTEPS];
 #pragma unroll
   for (int br = 0; br < C::NBR; ++br) {
 #pragma unroll
@@ -141,17 +123,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
       // rows past the end read row T-1 (always in bounds) and are zeroed
       const int query = q0 + qb * 32 + l32;
       const bool ok = query < T;
-      const E* src = ((br + wbr) ? Q2 : Q1) + (size_t)min(query, T - 1) * D;
+      const float* src = ((br + wbr) ? Q2 : Q1) + (size_t)min(query, T - 1) * D;
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        if constexpr (F32) {
-          const float x = src[2 * ks + hi];
-          qf[br][qb][ks] = ok ? x : 0.0f;
-        } else {
-          u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
-          raw = ok ? raw : u32x4{0u, 0u, 0u, 0u};
-          qf[br][qb][ks] = __builtin_bit_cast(bf16x8, raw);
-        }
+        const float x = src[2 * ks + hi];
+        qf[br][qb][ks] = ok ? x : 0.0f;
       }
     }
   }
@@ -173,7 +149,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
 
   // ---- staging registers ------------------------------------------------------
   u32x4 rk[2][C::NKPT];
-  u32x4 rv[C::NVPT][C::VREG];
+  u32x4 rv[C::NVPT];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   // Global -> register staging of one key tile.  Keys past the end load row
@@ -195,29 +171,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
 #pragma unroll
     for (int i = 0; i < C::NVPT; ++i) {
       const int u = (C::NVU % C::NT == 0) ? tid + i * C::NT : min(tid + i * C::NT, C::NVU - 1);
-      if constexpr (F32) {
-        const int row = u / (C::DV / 4);
-        const int col = u % (C::DV / 4);
-        const int key = kbase + row;
-        const u32x4 x = *(const u32x4*)(V + (size_t)min(key, T - 1) * C::DV + col * 4);
-        rv[i][0] = key < T ? x : zero4;
-      } else {
-        const int kq = u % (BC / 4);
-        const int cc = u / (BC / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kbase + kq * 4 + r;
-          const u32x4 x = *(const u32x4*)(V + (size_t)min(key, T - 1) * C::DV + cc * 8);
-          rv[i][r] = key < T ? x : zero4;
-        }
-      }
+      const int row = u / (C::DV / 4);
+      const int col = u % (C::DV / 4);
+      const int key = kbase + row;
+      const u32x4 x = *(const u32x4*)(V + (size_t)min(key, T - 1) * C::DV + col * 4);
+      rv[i] = key < T ? x : zero4;
     }
   };
 
   auto store_tile = [&](int buf) {
-    E* Ks1 = smem + buf * C::STAGE;
-    E* Ks2 = Ks1 + C::KTILE;
-    E* Vs = Ks2 + C::KTILE;
+    float* Ks1 = smem + buf * C::STAGE;
+    float* Ks2 = Ks1 + C::KTILE;
+    float* Vs = Ks2 + C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::NKPT; ++i) {
       const int c = tid + i * C::NT;
@@ -232,34 +197,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
     for (int i = 0; i < C::NVPT; ++i) {
       const int u = tid + i * C::NT;
       if (C::NVU % C::NT == 0 || u < C::NVU) {
-        if constexpr (F32) {
-          const int row = u / (C::DV / 4);
-          const int col = u % (C::DV / 4);
-          *(u32x4*)(Vs + row * C::VP + col * 4) = rv[i][0];
-        } else {
-          // 4 keys x 8 channels -> 8 channel rows of 4 keys each
-          const int kq = u % (BC / 4);
-          const int cc = u / (BC / 4);
-          const int pos = vt_quad_pos(kq) * 4;
-#pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const uint32_t a0 = rv[i][0][wd], a1 = rv[i][1][wd];
-            const uint32_t a2 = rv[i][2][wd], a3 = rv[i][3][wd];
-            const u32x2 even = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-            const u32x2 odd = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-            *(u32x2*)(Vs + (cc * 8 + 2 * wd) * C::VP + pos) = even;
-            *(u32x2*)(Vs + (cc * 8 + 2 * wd + 1) * C::VP + pos) = odd;
-          }
-        }
+        const int row = u / (C::DV / 4);
+        const int col = u % (C::DV / 4);
+        *(u32x4*)(Vs + row * C::VP + col * 4) = rv[i];
       }
     }
   };
 
   auto compute_tile = [&](int kt, int buf) {
-    const E* Ks1 = smem + buf * C::STAGE;
-    const E* Ks2 = Ks1 + C::KTILE;
-    const E* Vs = Ks2 + C::KTILE;
-    const E* Kmap[2] = {SPLIT && wbr ? Ks2 : Ks1, Ks2};  // K tile of each map this wave runs
+    const float* Ks1 = smem + buf * C::STAGE;
+    const float* Ks2 = Ks1 + C::KTILE;
+    const float* Vs = Ks2 + C::KTILE;
+    const float* Kmap[2] = {SPLIT && wbr ? Ks2 : Ks1, Ks2};  // K tile of each map this wave runs
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
       const int key0 = kt * BC + kb * 32;
@@ -278,17 +227,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
       for (int ks = 0; ks < C::KSTEPS; ++ks) {
 #pragma unroll
         for (int br = 0; br < C::NBR; ++br) {
-          if constexpr (F32) {
-            const float av = Kmap[br][(kb * 32 + l32) * C::KP + 2 * ks + hi];
+          const float av = Kmap[br][(kb * 32 + l32) * C::KP + 2 * ks + hi];
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
-          } else {
-            const bf16x8 av = *(const bf16x8*)(Kmap[br] + (kb * 32 + l32) * C::KP + ks * 16 + hi * 8);
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
-          }
+          for (int qb = 0; qb < NQB; ++qb)
+            s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
         }
       }
 
@@ -342,64 +284,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
           }
       }
 
-      if constexpr (F32) {
-        float p[C::NBR][NQB][16];
+      float p[C::NBR][NQB][16];
 #pragma unroll
-        for (int br = 0; br < C::NBR; ++br)
+      for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              p[br][qb][r] = __builtin_amdgcn_exp2f(fmaf(s[br][qb][r], sc, -msub));
-              lsum[br][qb] += p[br][qb][r];
-            }
-          }
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb)
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int krow = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const float av = Vs[krow * C::VP + cb * 32 + l32];
-#pragma unroll
-            for (int br = 0; br < C::NBR; ++br)
-#pragma unroll
-              for (int qb = 0; qb < NQB; ++qb)
-                acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, p[br][qb][r], acc[br][qb][cb], 0, 0, 0);
+            p[br][qb][r] = __builtin_amdgcn_exp2f(fmaf(s[br][qb][r], sc, -msub));
+            lsum[br][qb] += p[br][qb][r];
           }
-      } else {
-        bf16x8 pk[C::NBR][NQB][2];
-        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+        }
 #pragma unroll
-        for (int br = 0; br < C::NBR; ++br)
+      for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
+        for (int r = 0; r < 16; ++r) {
+          const int krow = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const float av = Vs[krow * C::VP + cb * 32 + l32];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+          for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float pa = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j], sc, -msub));
-                const float pb = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j + 1], sc, -msub));
-                const bf16x2 pw = {(bf16)pa, (bf16)pb};
-                lsum[br][qb] = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, lsum[br][qb], false);
-                pk[br][qb][ks][2 * j] = pw[0];
-                pk[br][qb][ks][2 * j + 1] = pw[1];
-              }
-            }
-          }
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 av = *(const bf16x8*)(Vs + (cb * 32 + l32) * C::VP + kb * 32 + ks * 16 + hi * 8);
-#pragma unroll
-            for (int br = 0; br < C::NBR; ++br)
-#pragma unroll
-              for (int qb = 0; qb < NQB; ++qb)
-                acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[br][qb][ks], acc[br][qb][cb], 0, 0, 0);
-          }
-      }
+            for (int qb = 0; qb < NQB; ++qb)
+              acc[br][qb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, p[br][qb][r], acc[br][qb][cb], 0, 0, 0);
+        }
     }
   };
 
@@ -440,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   if (!wave_active) return;
 
   // ---- epilogue: combine the maps, optional head norm, store -----------------
-  E* __restrict__ O = (E*)a.out + v_off;
+  float* __restrict__ O = (float*)a.out + v_off;
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int query = q0 + qb * 32 + l32;
@@ -479,20 +387,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
         for (int r = 0; r < 16; ++r) o[cb][r] *= f;
     }
     if (query < T) {
-      E* dst = O + (size_t)query * C::DV;
+      float* dst = O + (size_t)query * C::DV;
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ch = cb * 32 + 8 * g + 4 * hi;
-          if constexpr (F32) {
-            const floatx4 v4 = {o[cb][4 * g], o[cb][4 * g + 1], o[cb][4 * g + 2], o[cb][4 * g + 3]};
-            *(floatx4*)(dst + ch) = v4;
-          } else {
-            const bf16x4 v4 = {(bf16)o[cb][4 * g], (bf16)o[cb][4 * g + 1], (bf16)o[cb][4 * g + 2],
-                               (bf16)o[cb][4 * g + 3]};
-            *(bf16x4*)(dst + ch) = v4;
-          }
+          const floatx4 v4 = {o[cb][4 * g], o[cb][4 * g + 1], o[cb][4 * g + 2], o[cb][4 * g + 3]};
+          *(floatx4*)(dst + ch) = v4;
         }
     }
   }
@@ -956,21 +858,31 @@ hipError_t launch_bf16(const FwdArgs& a, bool causal, bool headnorm, hipStream_t
   return hipGetLastError();
 }
 
-template <int D, int NQB, int NW, int BC, bool F32, bool SPLIT>
-hipError_t launch_cfg(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
-  using C = Cfg<D, NQB, NW, BC, F32, SPLIT>;
+template <int D, int NQB, int NW, int BC, bool SPLIT>
+hipError_t launch_f32(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
+  using C = Cfg<D, NQB, NW, BC, SPLIT>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (causal) {
-    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, SPLIT, true, true><<<g, b, 0, stream>>>(a);
-    else fwd_kernel<D, NQB, NW, BC, F32, SPLIT, true, false><<<g, b, 0, stream>>>(a);
+    if (headnorm) fwd_f32_kernel<D, NQB, NW, BC, SPLIT, true, true><<<g, b, 0, stream>>>(a);
+    else fwd_f32_kernel<D, NQB, NW, BC, SPLIT, true, false><<<g, b, 0, stream>>>(a);
   } else {
-    if (headnorm) fwd_kernel<D, NQB, NW, BC, F32, SPLIT, false, true><<<g, b, 0, stream>>>(a);
-    else fwd_kernel<D, NQB, NW, BC, F32, SPLIT, false, false><<<g, b, 0, stream>>>(a);
+    if (headnorm) fwd_f32_kernel<D, NQB, NW, BC, SPLIT, false, true><<<g, b, 0, stream>>>(a);
+    else fwd_f32_kernel<D, NQB, NW, BC, SPLIT, false, false><<<g, b, 0, stream>>>(a);
   }
   return hipGetLastError();
+}
+
+// Compute units of the current device (256 on MI355X); used only to pick a
+// launch shape, so a failed query falls back to that value.
+long compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
 }
 
 }  // namespace
@@ -981,19 +893,29 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
     switch (D) {
       case 32: return launch_bf16<32, 1, 8, 3, false>(a, causal, headnorm, stream);
       case 64:
-        // short causal rows: one map per wave, three waves per SIMD (more
-        // latency hiding); long causal rows: both maps per wave (less LDS
-        // traffic per MFMA); full attention: one map and 64 rows per wave
-        if (causal && a.T <= 4096) return launch_bf16<64, 1, 12, 3, true>(a, causal, headnorm, stream);
+        // Short causal rows run one map per wave.  With few workgroups per
+        // compute unit the finer 128-row workgroups (two waves per SIMD)
+        // balance the causal triangle better; otherwise 192-row workgroups
+        // with three waves per SIMD hide more latency (measured on MI355X
+        // over T = 2048 / 4096 and 8 .. 64 heads).  Long causal rows run both
+        // maps per wave (less LDS traffic per MFMA); full attention runs one
+        // map and 64 rows per wave.
+        if (causal && a.T <= 4096) {
+          const long wg128 = (long)a.B * a.H * ((a.T + 127) / 128);
+          const long cus = compute_units();
+          if (wg128 <= cus || (a.T > 2048 && wg128 <= 4 * cus))
+            return launch_bf16<64, 1, 8, 3, true>(a, causal, headnorm, stream);
+          return launch_bf16<64, 1, 12, 3, true>(a, causal, headnorm, stream);
+        }
         if (causal) return launch_bf16<64, 1, 8, 3, false>(a, causal, headnorm, stream);
         return launch_bf16<64, 2, 8, 3, true>(a, causal, headnorm, stream);
       case 128: return launch_bf16<128, 1, 8, 2, true>(a, causal, headnorm, stream);
     }
   } else {  // fp32
     switch (D) {
-      case 32: return launch_cfg<32, 1, 4, 32, true, false>(a, causal, headnorm, stream);
-      case 64: return launch_cfg<64, 1, 4, 32, true, false>(a, causal, headnorm, stream);
-      case 128: return launch_cfg<128, 1, 4, 32, true, true>(a, causal, headnorm, stream);
+      case 32: return launch_f32<32, 1, 4, 32, false>(a, causal, headnorm, stream);
+      case 64: return launch_f32<64, 1, 4, 32, false>(a, causal, headnorm, stream);
+      case 128: return launch_f32<128, 1, 4, 32, true>(a, causal, headnorm, stream);
     }
   }
   return hipErrorInvalidValue;

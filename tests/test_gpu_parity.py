@@ -95,6 +95,28 @@ def test_fwd_long_causal_rows(headnorm):
             assert maxerr(out[0, h, rows], ref) <= TOL["bf16"], (T, h)
 
 
+@pytest.mark.parametrize("headnorm", [False, True])
+def test_fwd_causal_many_heads(headnorm):
+    # short causal rows over many heads take the 192-row, three-waves-per-SIMD
+    # configuration at D=64 (few heads the 128-row one, as in the sweep above);
+    # sampled heads and rows, full key range
+    B, H, T = 8, 16, 2048
+    x = prefill_inputs(B, H, T, 64, "bf16", seed=41, device=DEV)
+    lam = torch.linspace(-0.2, 1.2, H, dtype=torch.float32, device=DEV)
+    say(f"fwd bf16 D=64 B={B} H={H} T={T} causal headnorm={headnorm}")
+    out = run_fwd(x, lam, True, headnorm)
+    rng = np.random.default_rng(41)
+    for b, h in ((0, 0), (3, 9), (7, 15)):
+        rows = np.unique(np.concatenate([np.arange(32), np.arange(T - 32, T), rng.choice(T, 96, replace=False)]))
+        sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
+        ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], float(lam[h]), True, rows)
+        if headnorm:
+            ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+        assert maxerr(out[b, h, rows], ref) <= TOL["bf16"], (b, h)
+    del x, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_lambda_range(dtype):
     # lambda is not clamped: negative and > 1 values included
