@@ -3,9 +3,14 @@
 
 One "step" is one pass of the path over one batch of synthetic input that is
 already resident in HBM:
-  prefill workloads   lambda kernel (when the workload derives lambda from its
-                      four vectors) + the prefill forward kernel
+  prefill workloads   one prefill kernel; when the workload derives lambda
+                      from its four vectors, that kernel forms it too
+                      (diffattn_fwd_reparam)
   decode workload     lambda kernel + split-K partial kernel + reduce kernel
+
+Before the W warm-up steps each workload runs untimed steps for about
+SETTLE_S seconds, so that the GPU clock has ramped up before timing starts
+(a handful of sub-millisecond steps is not enough for that).
 
 The printed JSON line reports the primary workload (default: the causal T=4096
 bf16 prefill, B2 H16 D64, head norm on) as TFLOP/s counted as
@@ -74,7 +79,25 @@ def decode_bytes(w):
     return float(w.B * w.H * w.T * 4 * w.D * es)
 
 
+SETTLE_S = 0.4
+
+
+def settle(torch, step, seconds=SETTLE_S):
+    """Untimed steps for about `seconds` of wall time (clock ramp-up)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n
+
+
 def time_steps(torch, step, steps, warmup):
+    settle(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -117,10 +140,17 @@ def bench_workload(torch, da, name, steps, warmup):
     if w.kind == "prefill":
         out = torch.empty_like(x["v"])
 
-        def kernel():
-            da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"],
-                            lam if lam is not None else lam_buf, causal=w.causal,
-                            headnorm=w.headnorm, lambda_init=li, eps=w.eps, out=out)
+        if lam is not None:
+            def kernel():
+                da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, causal=w.causal,
+                                headnorm=w.headnorm, lambda_init=li, eps=w.eps, out=out)
+        else:
+            # lambda from its four vectors inside the prefill launch (the
+            # whole path, lambda included, is this one kernel)
+            def kernel():
+                da.diffattn_fwd_reparam(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lq1"], x["lk1"],
+                                        x["lq2"], x["lk2"], li, causal=w.causal, headnorm=w.headnorm,
+                                        eps=w.eps, out=out)
     else:
         out = torch.empty((w.B, w.H, 2 * w.D), device="cuda", dtype=x["v"].dtype)
         ws = torch.empty(da.diffattn_decode_workspace_bytes(w.B, w.H, w.T, w.D, w.num_splits) // 4,
@@ -133,7 +163,7 @@ def bench_workload(torch, da, name, steps, warmup):
                                workspace=ws, out=out)
 
     def step():
-        if lam is None:
+        if lam is None and w.kind != "prefill":
             da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], li, out=lam_buf)
         kernel()
 

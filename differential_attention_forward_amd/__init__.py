@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "DIFFATTN_F32", "DIFFATTN_BF16", "library_path", "lib",
     "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
+    "diffattn_fwd_reparam",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
 ]
 
@@ -42,6 +43,8 @@ _SIGS = {
     "diffattn_lambda": (_I, [_VP, _VP, _VP, _VP, _I, _I, _F, _VP, _VP]),
     "diffattn_fwd": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
                           _VP, _VP]),
+    "diffattn_fwd_reparam": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                  _I, _I, _I, _F, _F, _VP, _VP, _VP]),
     "diffattn_decode_default_splits": (_I, [_I, _I, _I]),
     "diffattn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "diffattn_decode": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F, _I,
@@ -149,9 +152,7 @@ def diffattn_lambda(lq1, lk1, lq2, lk2, lambda_init: float, out=None, stream=Non
     return out.reshape(()) if one_d else out
 
 
-def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
-                 lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
-    """Prefill forward; q*, k* [B,H,T,D], v [B,H,T,2D] -> out [B,H,T,2D]."""
+def _fwd_inputs(q1, k1, q2, k2, v):
     q1, k1, q2, k2, v = (_dev(t, n) for t, n in
                          ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")))
     if q1.dim() != 4:
@@ -162,6 +163,17 @@ def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = F
             raise ValueError(f"{n} must match q1 in shape and dtype")
     if v.shape != (b, h, t, 2 * d) or v.dtype != q1.dtype:
         raise ValueError("v must be [B, H, T, 2D] with the dtype of q1")
+    return q1, k1, q2, k2, v
+
+
+def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
+                 lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
+    """Prefill forward; q*, k* [B,H,T,D], v [B,H,T,2D] -> out [B,H,T,2D].
+
+    ``lam``: a scalar, a 0-d tensor or an [H] tensor (lambda itself).
+    """
+    q1, k1, q2, k2, v = _fwd_inputs(q1, k1, q2, k2, v)
+    b, h, t, d = q1.shape
     lamv = _lambda_vec(lam, h, q1.device)
     if out is None:
         out = torch.empty_like(v)
@@ -169,6 +181,31 @@ def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = F
                               _ptr(k2), _ptr(v), _ptr(lamv), int(bool(causal)),
                               int(bool(headnorm)), float(lambda_init), float(eps), _ptr(out),
                               _stream(stream)))
+    return out
+
+
+def diffattn_fwd_reparam(q1, k1, q2, k2, v, lq1, lk1, lq2, lk2, lambda_init: float,
+                         causal: bool = True, headnorm: bool = False, eps: float = 1e-5,
+                         lambda_out=None, out=None, stream=None):
+    """Prefill forward with lambda formed in the same launch from its four
+    [H, Dl] vectors (diffattn_lambda then diffattn_fwd, as one kernel).
+    ``lambda_out`` (optional [H] fp32 device tensor) receives lambda."""
+    q1, k1, q2, k2, v = _fwd_inputs(q1, k1, q2, k2, v)
+    b, h, t, d = q1.shape
+    vecs = [_dev(x, n).float() for x, n in ((lq1, "lq1"), (lk1, "lk1"), (lq2, "lq2"), (lk2, "lk2"))]
+    if vecs[0].dim() != 2 or vecs[0].shape[0] != h or any(x.shape != vecs[0].shape for x in vecs):
+        raise ValueError(f"the four lambda vectors must all be [{h}, Dl]")
+    dl = vecs[0].shape[1]
+    if lambda_out is not None and (lambda_out.shape != (h,) or lambda_out.dtype != torch.float32
+                                   or not lambda_out.is_cuda or not lambda_out.is_contiguous()):
+        raise ValueError(f"lambda_out must be a contiguous float32 device tensor of shape [{h}]")
+    if out is None:
+        out = torch.empty_like(v)
+    _check(lib().diffattn_fwd_reparam(_dtype_code(q1), b, h, t, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                                      _ptr(k2), _ptr(v), *map(_ptr, vecs), dl, int(bool(causal)),
+                                      int(bool(headnorm)), float(lambda_init), float(eps),
+                                      _ptr(lambda_out) if lambda_out is not None else None,
+                                      _ptr(out), _stream(stream)))
     return out
 
 

@@ -57,11 +57,13 @@ diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float*
                                           stream));
 }
 
-diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* q1,
-                             const void* k1, const void* q2, const void* k2, const void* v,
-                             const float* lambda, int causal, int headnorm, float lambda_init,
-                             float eps, void* out, hipStream_t stream) {
-  if (!q1 || !k1 || !q2 || !k2 || !v || !lambda || !out) return DIFFATTN_ERR_INVALID;
+namespace {
+
+// Checks shared by the two prefill entry points; fills the tensor part of a.
+diffattn_status check_fwd(int dtype, int B, int H, int T, int D, const void* q1, const void* k1,
+                          const void* q2, const void* k2, const void* v, int headnorm, float eps,
+                          void* out, diffattn::FwdArgs& a, size_t& out_bytes) {
+  if (!q1 || !k1 || !q2 || !k2 || !v || !out) return DIFFATTN_ERR_INVALID;
   if (B < 1 || H < 1 || T < 1) return DIFFATTN_ERR_INVALID;
   if (headnorm && !(eps > 0.0f)) return DIFFATTN_ERR_INVALID;
   if (dtype != DIFFATTN_F32 && dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
@@ -69,7 +71,7 @@ diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* 
   const void* ins[5] = {q1, k1, q2, k2, v};
   for (const void* p : ins)
     if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
-  if (!aligned(out, 16) || !aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(out, 16)) return DIFFATTN_ERR_UNSUPPORTED;
   // every (b, h) slice and every work index must fit the 32-bit index math
   if ((long long)B * H > 0x7fffffffLL || (long long)T * 2 * D > 0x7fffffffLL)
     return DIFFATTN_ERR_UNSUPPORTED;
@@ -79,20 +81,76 @@ diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* 
   const size_t sizes[5] = {nqk, nqk, nqk, nqk, nv};
   for (int i = 0; i < 5; ++i)
     if (overlaps(out, nv, ins[i], sizes[i])) return DIFFATTN_ERR_INVALID;
-  if (overlaps(out, nv, lambda, (size_t)H * sizeof(float))) return DIFFATTN_ERR_INVALID;
-
-  diffattn::FwdArgs a;
   a.q1 = q1;
   a.k1 = k1;
   a.q2 = q2;
   a.k2 = k2;
   a.v = v;
-  a.lam = lambda;
+  a.lam = nullptr;
+  for (int i = 0; i < 4; ++i) a.lvec[i] = nullptr;
+  a.Dl = 0;
+  a.lam_init = 0.0f;
+  a.lam_out = nullptr;
   a.out = out;
   a.B = B;
   a.H = H;
   a.T = T;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
+  out_bytes = nv;
+  return DIFFATTN_OK;
+}
+
+}  // namespace
+
+diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* q1,
+                             const void* k1, const void* q2, const void* k2, const void* v,
+                             const float* lambda, int causal, int headnorm, float lambda_init,
+                             float eps, void* out, hipStream_t stream) {
+  diffattn::FwdArgs a;
+  size_t nout = 0;
+  const diffattn_status st = check_fwd(dtype, B, H, T, D, q1, k1, q2, k2, v, headnorm, eps, out, a, nout);
+  if (st != DIFFATTN_OK) return st;
+  if (!lambda) return DIFFATTN_ERR_INVALID;
+  if (!aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (overlaps(out, nout, lambda, (size_t)H * sizeof(float))) return DIFFATTN_ERR_INVALID;
+  a.lam = lambda;
+  a.out_scale = 1.0f - lambda_init;
+  a.eps = eps;
+  return from_hip(diffattn::launch_fwd(a, dtype, D, causal != 0, headnorm != 0, stream));
+}
+
+diffattn_status diffattn_fwd_reparam(int dtype, int B, int H, int T, int D, const void* q1,
+                                     const void* k1, const void* q2, const void* k2,
+                                     const void* v, const float* lq1, const float* lk1,
+                                     const float* lq2, const float* lk2, int Dl, int causal,
+                                     int headnorm, float lambda_init, float eps,
+                                     float* lambda_out, void* out, hipStream_t stream) {
+  diffattn::FwdArgs a;
+  size_t nout = 0;
+  const diffattn_status st = check_fwd(dtype, B, H, T, D, q1, k1, q2, k2, v, headnorm, eps, out, a, nout);
+  if (st != DIFFATTN_OK) return st;
+  if (!lq1 || !lk1 || !lq2 || !lk2 || Dl < 1) return DIFFATTN_ERR_INVALID;
+  const float* vecs[4] = {lq1, lk1, lq2, lk2};
+  for (const float* p : vecs)
+    if (!aligned(p, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (lambda_out && !aligned(lambda_out, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  const size_t nvec = (size_t)H * Dl * sizeof(float), nlam = (size_t)H * sizeof(float);
+  for (const float* p : vecs) {
+    if (overlaps(out, nout, p, nvec)) return DIFFATTN_ERR_INVALID;
+    if (lambda_out && overlaps(lambda_out, nlam, p, nvec)) return DIFFATTN_ERR_INVALID;
+  }
+  if (lambda_out) {
+    if (overlaps(lambda_out, nlam, out, nout)) return DIFFATTN_ERR_INVALID;
+    const void* ins[5] = {q1, k1, q2, k2, v};
+    const size_t nqk = nout / 2;
+    const size_t sizes[5] = {nqk, nqk, nqk, nqk, nout};
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(lambda_out, nlam, ins[i], sizes[i])) return DIFFATTN_ERR_INVALID;
+  }
+  for (int i = 0; i < 4; ++i) a.lvec[i] = vecs[i];
+  a.Dl = Dl;
+  a.lam_init = lambda_init;
+  a.lam_out = lambda_out;
   a.out_scale = 1.0f - lambda_init;
   a.eps = eps;
   return from_hip(diffattn::launch_fwd(a, dtype, D, causal != 0, headnorm != 0, stream));

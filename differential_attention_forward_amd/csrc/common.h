@@ -48,6 +48,29 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// lambda of head h from its four re-parameterisation vectors ([H, Dl] each):
+// exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init (aifetchly "Differential
+// Transformer: Canceling LLM Attention Noise", section 3).  Called by a whole
+// wave; strided fp32 products, a fixed-order wave reduction and two expf, so
+// every caller (the lambda kernel, the fused prefill) gets the same bits.
+// The result is returned in every lane.
+__device__ inline float reparam_lambda(const float* __restrict__ lq1, const float* __restrict__ lk1,
+                                       const float* __restrict__ lq2, const float* __restrict__ lk2,
+                                       int h, int Dl, float lambda_init) {
+  const int lane = threadIdx.x & 63;
+  const size_t base = (size_t)h * Dl;
+  float d1 = 0.0f, d2 = 0.0f;
+  for (int i = lane; i < Dl; i += 64) {
+    d1 = fmaf(lq1[base + i], lk1[base + i], d1);
+    d2 = fmaf(lq2[base + i], lk2[base + i], d2);
+  }
+  d1 = wave_sum(d1);
+  d2 = wave_sum(d2);
+  const float e1 = expf(d1);
+  const float e2 = expf(d2);
+  return (e1 - e2) + lambda_init;
+}
+
 // bf16 <-> fp32 on raw 16-bit patterns (bf16 is the top half of an fp32).
 __device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -13,7 +13,13 @@ struct FwdArgs {
   const void* q2;
   const void* k2;
   const void* v;
-  const float* lam;   // [H]
+  const float* lam;   // [H], or null when lvec[0] is set
+  // fused lambda: the four re-parameterisation vectors [H, Dl] (lvec[0] null
+  // = use lam), lambda_init added to it, and an optional [H] copy of lambda
+  const float* lvec[4];
+  int Dl;
+  float lam_init;
+  float* lam_out;
   void* out;
   int B, H, T;
   float score_scale;  // log2(e) / sqrt(D)

@@ -1,8 +1,8 @@
 // lambda_h = exp(lq1_h . lk1_h) - exp(lq2_h . lk2_h) + lambda_init
 // (aifetchly "Differential Transformer: Canceling LLM Attention Noise",
 // section 3; paperleet "Differential Transformer Attention", the scalar
-// parameterisation).  One wave per head: strided fp32 products, a fixed-order
-// wavefront reduction, two exp.  The result stays on the device so the
+// parameterisation).  One wave per head (reparam_lambda, shared with the
+// prefill kernels' fused path).  The result stays on the device so the
 // forward call can consume it without a host round trip.
 #include "common.h"
 #include "kernels.h"
@@ -16,20 +16,8 @@ __global__ __launch_bounds__(64) void lambda_kernel(const float* __restrict__ lq
                                                     const float* __restrict__ lk2, int Dl,
                                                     float lambda_init, float* __restrict__ out) {
   const int h = blockIdx.x;
-  const int lane = threadIdx.x;
-  const size_t base = (size_t)h * Dl;
-  float d1 = 0.0f, d2 = 0.0f;
-  for (int i = lane; i < Dl; i += 64) {
-    d1 = fmaf(lq1[base + i], lk1[base + i], d1);
-    d2 = fmaf(lq2[base + i], lk2[base + i], d2);
-  }
-  d1 = wave_sum(d1);
-  d2 = wave_sum(d2);
-  if (lane == 0) {
-    const float e1 = expf(d1);
-    const float e2 = expf(d2);
-    out[h] = (e1 - e2) + lambda_init;
-  }
+  const float lam = reparam_lambda(lq1, lk1, lq2, lk2, h, Dl, lambda_init);
+  if (threadIdx.x == 0) out[h] = lam;
 }
 
 }  // namespace

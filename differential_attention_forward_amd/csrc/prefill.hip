@@ -42,6 +42,16 @@ namespace {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 2^8
 
+// lambda of head h: read from the [H] array, or (fused path) formed here by
+// every wave from the four vectors, with the same bits as the lambda kernel;
+// the first query tile of batch 0 stores it to lam_out when asked.
+__device__ inline float head_lambda(const FwdArgs& a, int h, int qt, int bh) {
+  if (a.lvec[0] == nullptr) return a.lam[h];
+  const float lam = reparam_lambda(a.lvec[0], a.lvec[1], a.lvec[2], a.lvec[3], h, a.Dl, a.lam_init);
+  if (a.lam_out != nullptr && qt == 0 && bh == h && threadIdx.x == 0) a.lam_out[h] = lam;
+  return lam;
+}
+
 template <int D, int NQB, int NW, int BC, bool SPLIT>
 struct Cfg {
   static constexpr int DV = 2 * D;
@@ -112,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
   const int ntiles = (k_end + BC - 1) / BC;
   const float sc = a.score_scale;
-  const float lamv = a.lam[h];
+  const float lamv = head_lambda(a, h, qt, bh);
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
   float qf[C::NBR][NQB][C::KSTEPS];
@@ -530,7 +540,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
   const int ntiles = (k_end + BC - 1) / BC;
   const float sc = a.score_scale;
-  const float lamv = a.lam[h];
+  const float lamv = head_lambda(a, h, qt, bh);
+  // formed here, before the tile loads start (not sunk into the loop)
+  asm volatile("" ::"v"(lamv));
 
   // ---- asynchronous tile loads ------------------------------------------------
   // Segment g of a K tile (1 KiB) holds rows RK g .. RK g + RK - 1; lane l

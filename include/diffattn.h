@@ -102,6 +102,32 @@ diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* 
                              float eps, void* out, hipStream_t stream);
 
 /*
+ * Prefill forward with lambda formed in the same launch: exactly
+ * diffattn_lambda(lq1, lk1, lq2, lk2, H, Dl, lambda_init, lambda) followed by
+ * diffattn_fwd(..., lambda, ...), as one kernel (aifetchly page, section 3,
+ * for lambda; paperleet page, equation for A1, A2, O, for the rest).  Every
+ * workgroup forms the lambda of its head from the four vectors with the same
+ * arithmetic as diffattn_lambda, so the result is identical bit for bit; the
+ * separate lambda launch and its kernel boundary disappear.
+ *
+ *   q1 .. v, causal, headnorm, eps, out   as for diffattn_fwd
+ *   lq1, lk1, lq2, lk2  device fp32 [H, Dl]
+ *   lambda_init         added to lambda, and the (1 - lambda_init) head-norm
+ *                       multiplier as in diffattn_fwd
+ *   lambda_out          optional device fp32 [H] that receives lambda (NULL:
+ *                       not written), e.g. for a decode call that follows
+ * Errors: as diffattn_fwd, plus ERR_INVALID for a null vector, Dl < 1 or
+ * lambda_out overlapping an input or out, and ERR_UNSUPPORTED for a vector or
+ * lambda_out not 4-byte aligned.
+ */
+diffattn_status diffattn_fwd_reparam(int dtype, int B, int H, int T, int D, const void* q1,
+                                     const void* k1, const void* q2, const void* k2,
+                                     const void* v, const float* lq1, const float* lk1,
+                                     const float* lq2, const float* lk2, int Dl, int causal,
+                                     int headnorm, float lambda_init, float eps,
+                                     float* lambda_out, void* out, hipStream_t stream);
+
+/*
  * Number of key splits decode uses for (B, H, L) when num_splits = 0.
  */
 int diffattn_decode_default_splits(int B, int H, int L);

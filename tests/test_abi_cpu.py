@@ -24,7 +24,8 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
+    assert "diffattn_fwd_reparam" in names
     for n in names:
         assert hasattr(L, n), n
 
@@ -89,6 +90,36 @@ def test_fwd_validation(L):
     assert fwd(L, ptrs=alias) == INVALID
     alias[6] = P(0)
     assert fwd(L, ptrs=alias) == INVALID
+
+
+def fwdr(L, dtype=BF16, B=1, H=2, T=8, D=64, ptrs=None, vecs=None, Dl=16, lam_out=None,
+         headnorm=0, eps=1e-5):
+    p = ptrs or [P(i) for i in range(6)]
+    vv = vecs or [P(10 + i) for i in range(4)]
+    return L.diffattn_fwd_reparam(dtype, B, H, T, D, p[0], p[1], p[2], p[3], p[4], vv[0], vv[1],
+                                  vv[2], vv[3], Dl, 1, headnorm, ctypes.c_float(0.8),
+                                  ctypes.c_float(eps), lam_out, p[5], None)
+
+
+def test_fwd_reparam_validation(L):
+    # the tensor checks are those of diffattn_fwd
+    assert fwdr(L, ptrs=[P(0), None, P(2), P(3), P(4), P(6)]) == INVALID
+    assert fwdr(L, T=0) == INVALID
+    assert fwdr(L, headnorm=1, eps=0.0) == INVALID
+    assert fwdr(L, dtype=7) == UNSUPPORTED
+    assert fwdr(L, D=48) == UNSUPPORTED
+    # the lambda vectors and the optional lambda copy
+    assert fwdr(L, vecs=[P(10), None, P(12), P(13)]) == INVALID
+    assert fwdr(L, Dl=0) == INVALID
+    assert fwdr(L, vecs=[P(10), P(11, 2), P(12), P(13)]) == UNSUPPORTED
+    assert fwdr(L, lam_out=P(20, 2)) == UNSUPPORTED
+    assert fwdr(L, lam_out=P(11, 4)) == INVALID          # lambda_out inside a vector
+    assert fwdr(L, lam_out=P(5, 64)) == INVALID          # lambda_out inside out
+    assert fwdr(L, lam_out=P(3, 16)) == INVALID          # lambda_out inside an input
+    assert fwdr(L, vecs=[P(10), P(11), P(12), P(5, 8)]) == INVALID  # out over a vector
+    # a valid call only fails at the launch: no GPU here, so it must not report
+    # a validation error (OK or ERR_HIP)
+    assert fwdr(L, lam_out=P(20)) in (OK, 4)
 
 
 def dec(L, dtype=BF16, B=1, H=2, Lk=64, D=64, splits=0, ws=None, wsb=1 << 20, ptrs=None):

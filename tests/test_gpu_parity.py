@@ -192,6 +192,37 @@ def test_lambda_kernel():
     assert torch.all(lz == torch.tensor(0.7993953, dtype=torch.float32))
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fwd_reparam_matches_two_calls(dtype):
+    # lambda formed inside the prefill launch: same bits as diffattn_lambda
+    # followed by diffattn_fwd, lambda_out equal to diffattn_lambda's output
+    g = torch.Generator().manual_seed(17)
+    for D, T, causal, headnorm, B, H, Dl in ((32, 129, True, False, 2, 3, 16), (64, 1000, True, True, 3, 4, 64),
+                                             (64, 300, False, False, 1, 2, 64), (128, 257, False, True, 2, 2, 40),
+                                             (64, 4500, True, False, 1, 2, 64)):
+        x = to_dev(prefill_inputs(B, H, T, D, dtype, seed=600 + D + T))
+        vecs = [(torch.randn(H, Dl, generator=g) * 0.1).to(DEV) for _ in range(4)]
+        li = 0.6
+        say(f"fwd_reparam {dtype} D={D} T={T} causal={causal} headnorm={headnorm} B={B} H={H}")
+        lam = da.diffattn_lambda(*vecs, li)
+        ref = da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, causal=causal,
+                              headnorm=headnorm, lambda_init=li)
+        lam_out = torch.full((H,), float("nan"), device=DEV)
+        got = da.diffattn_fwd_reparam(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], *vecs, li,
+                                      causal=causal, headnorm=headnorm, lambda_out=lam_out)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), (D, T)
+        assert torch.equal(lam_out, lam), (D, T)
+    # and against the oracle once, with lambda from the oracle's own formula
+    xc = prefill_inputs(1, 2, 200, 64, dtype, seed=5)
+    vc = [torch.randn(2, 32, generator=g) * 0.2 for _ in range(4)]
+    out = da.diffattn_fwd_reparam(*(to_dev(xc)[k] for k in ("q1", "k1", "q2", "k2", "v")),
+                                  *[v.to(DEV) for v in vc], 0.3, causal=True)
+    torch.cuda.synchronize()
+    lam_ref = oracle.reparam_lambda(*vc, 0.3)
+    assert maxerr(out, ref_fwd(xc, torch.tensor(lam_ref), True, False)) <= TOL[dtype]
+
+
 def test_lambda_chain_into_fwd():
     w = WORKLOADS["tiny_fp32_causal"]
     x = make_workload(w.name, "cpu")
