@@ -16,7 +16,8 @@ The printed JSON line reports the primary workload (default: the causal T=4096
 bf16 prefill, B2 H16 D64, head norm on) as TFLOP/s counted as
 8 * T_eff * T * D * B * H per forward (T_eff = (T+1)/2 causal, T full), and
 the other workloads (causal T=32768, full T=8192 D=128, decode L=65536) under
-"also".  "roofline" gives the dominant kernel's algorithmic rate (from HIP
+"also", together with standard softmax attention of the same size as the two
+causal workloads (head width 2D) and the time ratio of the two.  "roofline" gives the dominant kernel's algorithmic rate (from HIP
 events around each launch on the launch stream) against the MI355X peak
 (bf16 dense MFMA 2.5 PFLOP/s, fp32 MFMA 157.3 TFLOP/s, HBM 8 TB/s).
 "cpu_baseline" times the float64 oracle on the host cores on a bounded sample
@@ -200,6 +201,31 @@ def bench_workload(torch, da, name, steps, warmup):
     return res
 
 
+def bench_same_size_attention(torch, da, name, steps, warmup, diff_ms):
+    """Standard softmax attention of the same size as the named causal
+    differential workload (head width 2D, same B, H, T, same 8 T_eff T D B H
+    flops): the comparison the glossary page makes between the two kinds of
+    model, here on the forward kernels alone."""
+    from workloads import WORKLOADS, attention_inputs
+
+    w = WORKLOADS[name]
+    x = attention_inputs(w.B, w.H, w.T, 2 * w.D, seed=w.seed + 100, device="cuda")
+    out = torch.empty_like(x["v"])
+
+    def step():
+        da.diffattn_attention_fwd(x["q"], x["k"], x["v"], causal=w.causal, out=out)
+
+    ms, _ = time_steps(torch, step, steps, warmup)
+    work = prefill_flops(w)
+    log(f"[bench] same-size standard attention for {name}: {ms:.4f} ms/step")
+    del x, out
+    torch.cuda.empty_cache()
+    return {"workload": f"standard attention, B{w.B} H{w.H} T{w.T} head width {2 * w.D}, "
+                        f"{'causal' if w.causal else 'full'}, bf16",
+            "value": round(work / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+            "differential_over_standard_time": round(diff_ms / ms, 4)}
+
+
 def cpu_baseline(torch, name, budget_s=12.0):
     """The float64 oracle, as it stands, on the host cores: whole heads of the
     workload (every query row of each sampled (b, h)) until ~budget_s seconds."""
@@ -277,6 +303,10 @@ def main():
         for name in OTHERS + [PRIMARY]:
             if name != args.workload and name not in also:
                 also[name] = bench_workload(torch, da, name, args.steps, args.warmup)
+        for name in ("prefill_t4k_causal", "prefill_t32k_needles"):
+            diff_ms = (primary if name == args.workload else also[name])["ms_per_step"]
+            also[f"same_size_attention_{name}"] = bench_same_size_attention(
+                torch, da, name, args.steps, args.warmup, diff_ms)
     cpu = None
     w = WORKLOADS[args.workload]
     if not args.no_cpu_baseline and w.kind == "prefill":

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "DIFFATTN_F32", "DIFFATTN_BF16", "library_path", "lib",
     "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
-    "diffattn_fwd_reparam",
+    "diffattn_fwd_reparam", "diffattn_attention_fwd",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
 ]
 
@@ -45,6 +45,7 @@ _SIGS = {
                           _VP, _VP]),
     "diffattn_fwd_reparam": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                   _I, _I, _I, _F, _F, _VP, _VP, _VP]),
+    "diffattn_attention_fwd": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _I, _VP, _VP]),
     "diffattn_decode_default_splits": (_I, [_I, _I, _I]),
     "diffattn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "diffattn_decode": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F, _I,
@@ -206,6 +207,22 @@ def diffattn_fwd_reparam(q1, k1, q2, k2, v, lq1, lk1, lq2, lk2, lambda_init: flo
                                       int(bool(headnorm)), float(lambda_init), float(eps),
                                       _ptr(lambda_out) if lambda_out is not None else None,
                                       _ptr(out), _stream(stream)))
+    return out
+
+
+def diffattn_attention_fwd(q, k, v, causal: bool = True, out=None, stream=None):
+    """Standard softmax attention (bf16); q, k, v [B,H,T,D], D in {64, 128} ->
+    out [B,H,T,D].  The comparison kernel for differential heads of width D/2."""
+    q, k, v = (_dev(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, T, D]")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be bfloat16")
+    b, h, t, d = q.shape
+    if out is None:
+        out = torch.empty_like(v)
+    _check(lib().diffattn_attention_fwd(DIFFATTN_BF16, b, h, t, d, _ptr(q), _ptr(k), _ptr(v),
+                                        int(bool(causal)), _ptr(out), _stream(stream)))
     return out
 
 

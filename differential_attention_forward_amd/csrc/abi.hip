@@ -156,6 +156,42 @@ diffattn_status diffattn_fwd_reparam(int dtype, int B, int H, int T, int D, cons
   return from_hip(diffattn::launch_fwd(a, dtype, D, causal != 0, headnorm != 0, stream));
 }
 
+diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, const void* q,
+                                       const void* k, const void* v, int causal, void* out,
+                                       hipStream_t stream) {
+  if (!q || !k || !v || !out) return DIFFATTN_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1) return DIFFATTN_ERR_INVALID;
+  if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return DIFFATTN_ERR_UNSUPPORTED;
+  const void* ins[3] = {q, k, v};
+  for (const void* p : ins)
+    if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(out, 16)) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H > 0x7fffffffLL || (long long)T * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  const size_t n = (size_t)B * H * T * D * elem_bytes(dtype);
+  for (const void* p : ins)
+    if (overlaps(out, n, p, n)) return DIFFATTN_ERR_INVALID;
+  diffattn::FwdArgs a;
+  a.q1 = q;
+  a.k1 = k;
+  a.q2 = nullptr;
+  a.k2 = nullptr;
+  a.v = v;
+  a.lam = nullptr;
+  for (int i = 0; i < 4; ++i) a.lvec[i] = nullptr;
+  a.Dl = 0;
+  a.lam_init = 0.0f;
+  a.lam_out = nullptr;
+  a.out = out;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
+  a.out_scale = 1.0f;
+  a.eps = 1.0f;
+  return from_hip(diffattn::launch_attention(a, D, causal != 0, stream));
+}
+
 int diffattn_decode_default_splits(int B, int H, int L) {
   if (B < 1 || H < 1 || L < 1) return 0;
   // aim for ~4096 workgroups in flight, chunks of at least 256 keys

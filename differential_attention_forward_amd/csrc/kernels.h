@@ -47,6 +47,8 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
                       hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, bool headnorm,
                          hipStream_t stream);
+// standard softmax attention, bf16, Q/K/V/O [B,H,T,D] (D = 64 or 128)
+hipError_t launch_attention(const FwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2,
                          const float* lk2, int H, int Dl, float lambda_init, float* out,
                          hipStream_t stream);

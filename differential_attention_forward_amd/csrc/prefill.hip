@@ -428,18 +428,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
 // four consecutive keys of its own channel, in the key order in which the
 // lane's probabilities reach the MFMA.
 
-template <int D, int NQB, int NW, int NSTAGE, bool SPLIT>
+// MAPS = 2: differential attention (Q1, K1, Q2, K2 of width D, V of width
+// 2D).  MAPS = 1: standard softmax attention (Q, K, V of width D), the
+// comparison kernel of the same size as a differential head of width D/2.
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, int MAPS = 2>
 struct CfgB {
   static constexpr int BC = 64;
-  static constexpr int DV = 2 * D;
+  static constexpr int DV = MAPS == 2 ? 2 * D : D;
   static constexpr int QPW = 32 * NQB;
-  static constexpr int NBR = SPLIT ? 1 : 2;
+  static constexpr int NBR = SPLIT || MAPS == 1 ? 1 : 2;
   static constexpr int NWQ = SPLIT ? NW / 2 : NW;
   static constexpr int BR = NWQ * QPW;
   static constexpr int NT = NW * 64;
   static constexpr int KBYTES = BC * D * 2;
   static constexpr int VBYTES = BC * DV * 2;
-  static constexpr int STAGE = 2 * KBYTES + VBYTES;
+  static constexpr int STAGE = MAPS * KBYTES + VBYTES;
   static constexpr int KSEG = KBYTES / 1024;   // 1-KiB segments per K tile
   static constexpr int NSEG = STAGE / 1024;    // per stage
   static constexpr int SEGW = (NSEG + NW - 1) / NW;  // most loads one wave issues per tile
@@ -451,6 +454,7 @@ struct CfgB {
   static constexpr int RBYTES = NSTAGE * STAGE;
   static constexpr int SMEM = RBYTES > XBYTES ? RBYTES : XBYTES;
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "two to four stages");
+  static_assert(MAPS == 2 || !SPLIT, "one map: nothing to split");
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -502,9 +506,9 @@ __device__ inline float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM>
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM, int MAPS = 2>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
-  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
+  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, MAPS>;
   constexpr int BC = C::BC;
   constexpr int PD = NSTAGE - 1;  // prefetch distance in tiles
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -540,9 +544,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
   const int ntiles = (k_end + BC - 1) / BC;
   const float sc = a.score_scale;
-  const float lamv = head_lambda(a, h, qt, bh);
-  // formed here, before the tile loads start (not sunk into the loop)
-  asm volatile("" ::"v"(lamv));
+  float lamv = 0.0f;
+  if constexpr (MAPS == 2) {
+    lamv = head_lambda(a, h, qt, bh);
+    // formed here, before the tile loads start (not sunk into the loop)
+    asm volatile("" ::"v"(lamv));
+  }
 
   // ---- asynchronous tile loads ------------------------------------------------
   // Segment g of a K tile (1 KiB) holds rows RK g .. RK g + RK - 1; lane l
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (int i = 0; i < C::SEGW; ++i) {
       const int seg = wave + i * NW;
       if (seg >= C::NSEG) break;
-      if (seg < 2 * C::KSEG) {
+      if (seg < MAPS * C::KSEG) {
         const int which = seg / C::KSEG;
         const int g = seg % C::KSEG;
         const int r = g * RK + rl_k;
@@ -566,11 +573,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
         dma16(which ? K2 : K1, row * (D * 2) + c * 16, sb + which * C::KBYTES + g * 1024);
       } else {
-        const int g = seg - 2 * C::KSEG;
+        const int g = seg - MAPS * C::KSEG;
         const int r = g * RV + rl_v;
         const int c = (lane % CV) ^ swz_v((g & 1) * RV + rl_v);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
-        dma16(V, row * (C::DV * 2) + c * 16, sb + 2 * C::KBYTES + g * 1024);
+        dma16(V, row * (C::DV * 2) + c * 16, sb + MAPS * C::KBYTES + g * 1024);
       }
     }
   };
@@ -733,7 +740,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   // acc += P^T-weighted V rows of block kb; each V fragment serves both maps
   auto pv = [&](int kb, const char* sb, const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
-    const char* Vb = sb + 2 * C::KBYTES;
+    const char* Vb = sb + MAPS * C::KBYTES;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -811,7 +818,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const int query = q0 + qb * 32 + l32;
     const float inv1 = 1.0f / swap_halves_sum(lsum[0][qb]);
     float inv2 = 0.0f;
-    if constexpr (!SPLIT) inv2 = 1.0f / swap_halves_sum(lsum[1][qb]);
+    if constexpr (!SPLIT && MAPS == 2) inv2 = 1.0f / swap_halves_sum(lsum[1][qb]);
     const float* xrow = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
     float o[C::CB][16];
 #pragma unroll
@@ -820,11 +827,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       for (int r = 0; r < 16; ++r) {
         // t1 - lam * t2 with both maps rounded identically (no contraction)
         const float t1 = acc[0][qb][cb][r] * inv1;
-        float t2;
-        if constexpr (SPLIT) t2 = xrow[cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)];
-        else t2 = acc[C::NBR - 1][qb][cb][r] * inv2;
-        const float lt2 = lamv * t2;
-        o[cb][r] = t1 - lt2;
+        if constexpr (MAPS == 1) {
+          o[cb][r] = t1;
+        } else {
+          float t2;
+          if constexpr (SPLIT) t2 = xrow[cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)];
+          else t2 = acc[C::NBR - 1][qb][cb][r] * inv2;
+          const float lt2 = lamv * t2;
+          o[cb][r] = t1 - lt2;
+        }
       }
     if constexpr (HEADNORM) {
       float ss = 0.0f;
@@ -870,6 +881,18 @@ hipError_t launch_bf16(const FwdArgs& a, bool causal, bool headnorm, hipStream_t
   return hipGetLastError();
 }
 
+template <int D, int NQB, int NW, int NSTAGE>
+hipError_t launch_std(const FwdArgs& a, bool causal, hipStream_t stream) {
+  using C = CfgB<D, NQB, NW, NSTAGE, false, 1>;
+  const long nqt = (a.T + C::BR - 1) / C::BR;
+  const long grid = (long)a.B * a.H * nqt;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), b(C::NT);
+  if (causal) fwd_bf16_kernel<D, NQB, NW, NSTAGE, false, true, false, 1><<<g, b, 0, stream>>>(a);
+  else fwd_bf16_kernel<D, NQB, NW, NSTAGE, false, false, false, 1><<<g, b, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int D, int NQB, int NW, int BC, bool SPLIT>
 hipError_t launch_f32(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
   using C = Cfg<D, NQB, NW, BC, SPLIT>;
@@ -898,6 +921,14 @@ long compute_units() {
 }
 
 }  // namespace
+
+hipError_t launch_attention(const FwdArgs& a, int D, bool causal, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_std<64, 1, 8, 3>(a, causal, stream);
+    case 128: return launch_std<128, 1, 8, 3>(a, causal, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool headnorm,
                       hipStream_t stream) {

@@ -128,6 +128,23 @@ diffattn_status diffattn_fwd_reparam(int dtype, int B, int H, int T, int D, cons
                                      float* lambda_out, void* out, hipStream_t stream);
 
 /*
+ * Standard softmax attention, softmax(Q K^T / sqrt(D) + M) V, bf16 only: the
+ * comparison kernel for a differential head of the same size (a differential
+ * head of width D/2 has the same parameter count and the same 8 (D/2) flops
+ * per query-key pair; the glossary page compares the throughput of the two
+ * kinds of model).  It is the lambda = 0 case of diffattn_fwd with one map,
+ * and runs the same kernel with one score map.
+ *
+ *   q, k, v, out    [B, H, T, D] bf16, D = 64 or 128
+ *   causal          as for diffattn_fwd
+ * Errors: ERR_INVALID (null pointer, B/H/T < 1, out overlapping an input),
+ * ERR_UNSUPPORTED (dtype other than bf16, D, alignment, grid size), ERR_HIP.
+ */
+diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, const void* q,
+                                       const void* k, const void* v, int causal, void* out,
+                                       hipStream_t stream);
+
+/*
  * Number of key splits decode uses for (B, H, L) when num_splits = 0.
  */
 int diffattn_decode_default_splits(int B, int H, int L);

@@ -5,6 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 
 from .diffattn_oracle import (  # noqa: F401
+    attention,
     diff_attention,
     diff_attention_decode,
     diff_attention_rows,

@@ -73,6 +73,7 @@ __all__ = [
     "diff_attention_rows",
     "head_rmsnorm",
     "diff_attention_decode",
+    "attention",
 ]
 
 
@@ -246,4 +247,23 @@ def diff_attention_decode(q1, k1, q2, k2, v, lam):
             out[bi, hi] = diff_attention_rows(
                 q1[bi, hi][None, :], k1s, q2[bi, hi][None, :], k2s, vs,
                 lam_h[hi], False, np.array([0]))[0]
+    return out
+
+
+def attention(q, k, v, causal: bool = True, row_block: int = 512):
+    """Standard softmax attention softmax(Q K^T / sqrt(D) + M) V, float64.
+
+    The comparison model of the glossary page (a Transformer of the same size;
+    the paperleet page: lambda = 0 leaves ordinary attention).  q, k: [B, H, T,
+    D]; v: [B, H, T, Dv]; the same scores, mask and row softmax as above, one
+    map.  Rows are processed in blocks only to bound memory.
+    """
+    q, k, v = (_f64(t) for t in (q, k, v))
+    b, h, t, _ = q.shape
+    out = np.empty((b, h, t, v.shape[-1]))
+    for bi in range(b):
+        for hi in range(h):
+            for s0 in range(0, t, row_block):
+                r = np.arange(s0, min(t, s0 + row_block))
+                out[bi, hi, r] = _softmax_rows(_scores(q[bi, hi], k[bi, hi], r, causal)) @ v[bi, hi]
     return out

@@ -30,6 +30,8 @@ What pins what:
   brute force      an independent pure-Python scalar implementation on T <= 8
   decode           one query against the cache equals the last row of the
                    causal forward (that row sees every key)
+  standard attn    the one-map comparison function against torch's float64
+                   scaled_dot_product_attention, for V as wide as Q/K and wider
 """
 
 import json
@@ -86,6 +88,15 @@ def check_library_attention():
         o = oracle.diff_attention(q1, k1, q2, k2, v, lam, causal)
         ref = ref1 - lam[None, :, None, None] * ref2
         assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def check_standard_attention():
+    for causal in (True, False):
+        for dv in (16, 32):
+            q, k = _rand((2, 3, 29, 16), 51), _rand((2, 3, 29, 16), 52)
+            v = _rand((2, 3, 29, dv), 53)
+            o = oracle.attention(q, k, v, causal, row_block=7)
+            assert np.max(np.abs(o - _sdpa(q, k, v, causal))) < 1e-12
 
 
 def check_cancellation():
@@ -179,5 +190,5 @@ def check_decode():
 ALL_CHECKS = [
     check_worked_example, check_library_attention, check_cancellation, check_row_sums,
     check_value_offset, check_first_row, check_lambda, check_lambda_init, check_head_norm,
-    check_brute_force, check_decode,
+    check_brute_force, check_decode, check_standard_attention,
 ]

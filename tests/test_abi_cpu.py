@@ -24,8 +24,8 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 8, names
-    assert "diffattn_fwd_reparam" in names
+    assert len(names) == 9, names
+    assert "diffattn_fwd_reparam" in names and "diffattn_attention_fwd" in names
     for n in names:
         assert hasattr(L, n), n
 
@@ -120,6 +120,23 @@ def test_fwd_reparam_validation(L):
     # a valid call only fails at the launch: no GPU here, so it must not report
     # a validation error (OK or ERR_HIP)
     assert fwdr(L, lam_out=P(20)) in (OK, 4)
+
+
+def att(L, dtype=BF16, B=1, H=2, T=8, D=128, ptrs=None):
+    p = ptrs or [P(i) for i in range(4)]
+    return L.diffattn_attention_fwd(dtype, B, H, T, D, p[0], p[1], p[2], 1, p[3], None)
+
+
+def test_attention_validation(L):
+    assert att(L, ptrs=[P(0), None, P(2), P(3)]) == INVALID
+    assert att(L, ptrs=[P(0), P(1), P(2), None]) == INVALID
+    assert att(L, B=0) == INVALID
+    assert att(L, T=0) == INVALID
+    assert att(L, dtype=F32) == UNSUPPORTED
+    for d in (32, 96, 256):
+        assert att(L, D=d) == UNSUPPORTED
+    assert att(L, ptrs=[P(0), P(1, 8), P(2), P(3)]) == UNSUPPORTED
+    assert att(L, ptrs=[P(0), P(1), P(2), P(2, 512)]) == INVALID   # out over v
 
 
 def dec(L, dtype=BF16, B=1, H=2, Lk=64, D=64, splits=0, ws=None, wsb=1 << 20, ptrs=None):

@@ -13,7 +13,7 @@ import torch
 
 import differential_attention_forward_amd as da
 import oracle
-from workloads import WORKLOADS, decode_inputs, make_workload, prefill_inputs
+from workloads import WORKLOADS, attention_inputs, decode_inputs, make_workload, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -115,6 +115,22 @@ def test_fwd_causal_many_heads(headnorm):
         assert maxerr(out[b, h, rows], ref) <= TOL["bf16"], (b, h)
     del x, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+def test_standard_attention(D, causal):
+    # the one-map comparison kernel against the oracle's standard attention
+    worst = 0.0
+    for i, T in enumerate((1, 17, 64, 65, 129, 1000)):
+        x = attention_inputs(1, 3, T, D, seed=900 + D + i)
+        say(f"attention bf16 D={D} T={T} causal={causal}")
+        out = da.diffattn_attention_fwd(*(x[k].to(DEV) for k in ("q", "k", "v")), causal=causal)
+        torch.cuda.synchronize()
+        err = maxerr(out, oracle.attention(x["q"], x["k"], x["v"], causal))
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (T, err)
+    say(f"  worst {worst:.3e}")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

@@ -14,6 +14,8 @@ import pytest
 import oracle.diffattn_oracle as od
 from tests import oracle_pins
 
+_REAL_ATTENTION = od.attention  # the real function, wrapped by two mutants below
+
 
 
 def _make_scores(scale_fn=None, mask_fn=None, transpose=False):
@@ -102,6 +104,16 @@ def _norm_eps_outside(o, lambda_init, eps):
     return o / (np.sqrt(np.mean(o * o, -1, keepdims=True)) + eps) * (1 - lambda_init)
 
 
+def _attention_mask_ignored(q, k, v, causal=True, row_block=512):
+    return _REAL_ATTENTION(q, k, v, False, row_block)
+
+
+def _attention_keys_as_values(q, k, v, causal=True, row_block=512):
+    k64 = od._f64(k)
+    return _REAL_ATTENTION(q, k, np.concatenate([k64] * (od._f64(v).shape[-1] // k64.shape[-1]), -1),
+                                    causal, row_block)
+
+
 MUTANTS = {
     "scale_1_over_sqrt_2d": ("_scores", _make_scores(lambda d: 1 / math.sqrt(2 * d), lambda j, i: j > i)),
     "scale_missing": ("_scores", _make_scores(lambda d: 1.0, lambda j, i: j > i)),
@@ -122,6 +134,8 @@ MUTANTS = {
     "norm_without_scale": ("head_rmsnorm", _norm_no_scale),
     "norm_with_mean": ("head_rmsnorm", _norm_layernorm),
     "norm_eps_outside_sqrt": ("head_rmsnorm", _norm_eps_outside),
+    "attention_mask_ignored": ("attention", _attention_mask_ignored),
+    "attention_keys_as_values": ("attention", _attention_keys_as_values),
 }
 
 

@@ -96,6 +96,15 @@ def _randn(g, shape, device, scale=1.0):
     return x
 
 
+def attention_inputs(B, H, T, D, seed=0, device="cpu"):
+    """Q, K, V [B,H,T,D] bf16, iid N(0,1) cast with round-to-nearest-even: the
+    inputs of the standard-attention comparison kernel (a same-size model has
+    head width D = 2 x the differential head width)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return {n: _randn(g, (B, H, T, D), device, 1.0).to(torch.bfloat16) for n in ("q", "k", "v")}
+
+
 def prefill_inputs(B, H, T, D, dtype="bf16", seed=0, device="cpu", *, input_scale=1.0,
                    lambda_dl=0, lambda_zero=False, lam_fixed=None, lam_uniform=None,
                    needles=0, value_offset=False):
