@@ -7,11 +7,13 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 from .diffattn_oracle import (  # noqa: F401
     attention,
     diff_attention,
+    diff_attention_backward,
     diff_attention_decode,
     diff_attention_rows,
     head_rmsnorm,
     lambda_init_schedule,
     reparam_lambda,
+    reparam_lambda_backward,
     score_maps,
     signed_map,
 )

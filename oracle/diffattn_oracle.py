@@ -74,6 +74,8 @@ __all__ = [
     "head_rmsnorm",
     "diff_attention_decode",
     "attention",
+    "diff_attention_backward",
+    "reparam_lambda_backward",
 ]
 
 
@@ -267,3 +269,73 @@ def attention(q, k, v, causal: bool = True, row_block: int = 512):
                 r = np.arange(s0, min(t, s0 + row_block))
                 out[bi, hi, r] = _softmax_rows(_scores(q[bi, hi], k[bi, hi], r, causal)) @ v[bi, hi]
     return out
+
+
+def _softmax_backward_rows(a: np.ndarray, da: np.ndarray) -> np.ndarray:
+    """Vector-Jacobian product of the row softmax: given A = softmax(S) by rows
+    and dL/dA, dL/dS = A * (dA - rowsum(dA * A)).  Masked entries have A = 0 and
+    so get zero gradient."""
+    return a * (da - np.sum(da * a, axis=-1, keepdims=True))
+
+
+def _head_rmsnorm_backward(opre: np.ndarray, dy: np.ndarray, lambda_init: float, eps: float) -> np.ndarray:
+    """Vector-Jacobian product of Y = X g (1 - lambda_init), g = (mean_c X^2 + eps)^-1/2,
+    per row over the last axis:  dX = (1 - lambda_init) g (dY - X g^2 mean_c(dY X))."""
+    g = 1.0 / np.sqrt(np.mean(opre * opre, axis=-1, keepdims=True) + float(eps))
+    return (1.0 - float(lambda_init)) * g * (dy - opre * g * g * np.mean(dy * opre, axis=-1, keepdims=True))
+
+
+def diff_attention_backward(q1, k1, q2, k2, v, lam, dout, causal: bool = True, headnorm: bool = False,
+                            lambda_init: float = 0.8, eps: float = 1e-5):
+    """Gradients of the forward above (with the optional head norm) given dL/dOut.
+
+    The paperleet page asks for gradients through both Q/K branches, the value
+    and the coefficient.  Written out from the chain rule, one (b, h) at a time,
+    maps materialised:
+        O1 = A1 V, O2 = A2 V, Opre = O1 - lam O2, Out = Opre or norm(Opre)
+        dOpre = dOut, or the head-norm vector-Jacobian product of dOut
+        dV = A1^T dOpre - lam A2^T dOpre
+        dA1 = dOpre V^T,  dA2 = -lam dOpre V^T
+        dS1, dS2 = row-softmax vector-Jacobian products of dA1, dA2
+        dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D)     (per map)
+        dlam = -sum over (b, t, c) of dOpre O2           (one lambda per head)
+    Returns dq1, dk1, dq2, dk2, dv ([B, H, ...] float64) and dlam ([H]).
+    """
+    q1, k1, q2, k2, v, dout = (_f64(t) for t in (q1, k1, q2, k2, v, dout))
+    b, h, t, d = q1.shape
+    lam_h = _lam_per_head(lam, h)
+    c = 1.0 / math.sqrt(d)
+    dq1, dk1, dq2, dk2, dv = (np.empty_like(x) for x in (q1, k1, q2, k2, v))
+    dlam = np.zeros(h)
+    for bi in range(b):
+        for hi in range(h):
+            lm = lam_h[hi]
+            a1 = _softmax_rows(_scores(q1[bi, hi], k1[bi, hi], None, causal))
+            a2 = _softmax_rows(_scores(q2[bi, hi], k2[bi, hi], None, causal))
+            vv = v[bi, hi]
+            o2 = a2 @ vv
+            opre = a1 @ vv - lm * o2
+            dy = dout[bi, hi]
+            dopre = _head_rmsnorm_backward(opre, dy, lambda_init, eps) if headnorm else dy
+            dv[bi, hi] = a1.T @ dopre - lm * (a2.T @ dopre)
+            dp = dopre @ vv.T
+            ds1 = _softmax_backward_rows(a1, dp)
+            ds2 = _softmax_backward_rows(a2, -lm * dp)
+            dq1[bi, hi] = c * (ds1 @ k1[bi, hi])
+            dk1[bi, hi] = c * (ds1.T @ q1[bi, hi])
+            dq2[bi, hi] = c * (ds2 @ k2[bi, hi])
+            dk2[bi, hi] = c * (ds2.T @ q2[bi, hi])
+            dlam[hi] -= np.sum(dopre * o2)
+    return dq1, dk1, dq2, dk2, dv, dlam
+
+
+def reparam_lambda_backward(lq1, lk1, lq2, lk2, dlam):
+    """Gradients of lam = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init (aifetchly
+    page, section 3) with respect to its four vectors, given dL/dlam per head:
+    d lq1 = dlam e1 lk1, d lk1 = dlam e1 lq1, d lq2 = -dlam e2 lk2,
+    d lk2 = -dlam e2 lq2, with e1 = exp(lq1 . lk1), e2 = exp(lq2 . lk2)."""
+    a, b, c, d = (_f64(t) for t in (lq1, lk1, lq2, lk2))
+    dl = _f64(dlam)[..., None]
+    e1 = np.exp(np.sum(a * b, axis=-1, keepdims=True))
+    e2 = np.exp(np.sum(c * d, axis=-1, keepdims=True))
+    return dl * e1 * b, dl * e1 * a, -dl * e2 * d, -dl * e2 * c

@@ -32,6 +32,14 @@ What pins what:
                    causal forward (that row sees every key)
   standard attn    the one-map comparison function against torch's float64
                    scaled_dot_product_attention, for V as wide as Q/K and wider
+  backward         the hand-derived gradients against (a) torch autograd
+                   through float64 scaled_dot_product_attention and rms_norm,
+                   (b) central finite differences of the pure-Python scalar
+                   forward on T <= 5, (c) the identity sum_j dK_j = 0 per map
+                   (softmax is unchanged by a per-row score shift), and
+                   (d) lambda = 0 leaves the second branch with no gradient
+  lambda grads     the four lambda-vector gradients against autograd and
+                   central finite differences of the closed form
 """
 
 import json
@@ -187,8 +195,89 @@ def check_decode():
     assert np.max(np.abs(dec - full[:, :, -1])) < 1e-13
 
 
+def _torch_forward(q1, k1, q2, k2, v, lam, causal, headnorm, lambda_init, eps):
+    o = (F.scaled_dot_product_attention(q1, k1, v, is_causal=causal)
+         - lam.view(1, -1, 1, 1) * F.scaled_dot_product_attention(q2, k2, v, is_causal=causal))
+    if headnorm:
+        o = F.rms_norm(o, (o.shape[-1],), eps=eps) * (1.0 - lambda_init)
+    return o
+
+
+def check_backward_autograd():
+    for causal, headnorm, seed in ((True, False, 91), (False, False, 92), (True, True, 93), (False, True, 94)):
+        xs = [x.requires_grad_() for x in _case(2, 2, 11, 4, seed)]
+        lam = torch.tensor([0.35, 1.2], dtype=torch.float64, requires_grad=True)
+        o = _torch_forward(*xs, lam, causal, headnorm, 0.6, 1e-5)
+        dy = _rand(o.shape, seed + 50)
+        ref = torch.autograd.grad(o, (*xs, lam), dy)
+        got = oracle.diff_attention_backward(*(x.detach() for x in xs), lam.detach().numpy(), dy,
+                                             causal, headnorm, 0.6, 1e-5)
+        for r, g in zip(ref, got):
+            assert np.max(np.abs(r.numpy() - g)) < 1e-12 * (1.0 + float(r.abs().max()))
+
+
+def check_backward_finite_diff():
+    step = 1e-6
+    for t, causal, seed in ((4, True, 95), (5, False, 96)):
+        q1, k1, q2, k2, v = (x[0, 0] for x in _case(1, 1, t, 3, seed))
+        lam = 0.6
+        dy = _rand((t, 6), seed + 7).numpy()
+
+        def loss(x1, y1, x2, y2, vv, lm):
+            o = brute.diff_attention_head(x1.tolist(), y1.tolist(), x2.tolist(), y2.tolist(), vv.tolist(),
+                                          lm, causal)
+            return float(np.sum(np.array(o) * dy))
+
+        got = oracle.diff_attention_backward(*(x[None, None] for x in (q1, k1, q2, k2, v)), np.array([lam]),
+                                             dy[None, None], causal)
+        base = [x.numpy().copy() for x in (q1, k1, q2, k2, v)]
+        for which in range(5):
+            for idx in np.ndindex(base[which].shape):
+                plus = [x.copy() for x in base]
+                minus = [x.copy() for x in base]
+                plus[which][idx] += step
+                minus[which][idx] -= step
+                fd = (loss(*plus, lam) - loss(*minus, lam)) / (2 * step)
+                assert abs(fd - got[which][0, 0][idx]) < 1e-7, (which, idx)
+        fd = (loss(*base, lam + step) - loss(*base, lam - step)) / (2 * step)
+        assert abs(fd - got[5][0]) < 1e-7
+
+
+def check_backward_identities():
+    q1, k1, q2, k2, v = _case(2, 3, 13, 8, seed=97)
+    dy = _rand((2, 3, 13, 16), 98)
+    g = oracle.diff_attention_backward(q1, k1, q2, k2, v, np.array([0.0, 0.5, 1.1]), dy, causal=True)
+    for dk in (g[1], g[3]):
+        assert np.max(np.abs(dk.sum(axis=2))) < 1e-12
+    assert np.max(np.abs(g[2][:, 0])) == 0.0 and np.max(np.abs(g[3][:, 0])) == 0.0
+    assert np.max(np.abs(g[0][:, 0])) > 1e-3
+
+
+def check_lambda_backward():
+    for dl, seed in ((16, 101), (3, 102)):
+        vecs = [(_rand((4, dl), seed + i) * 0.2).requires_grad_() for i in range(4)]
+        dlam = _rand((4,), seed + 9)
+        lam = torch.exp((vecs[0] * vecs[1]).sum(-1)) - torch.exp((vecs[2] * vecs[3]).sum(-1)) + 0.3
+        ref = torch.autograd.grad(lam, vecs, dlam)
+        got = oracle.reparam_lambda_backward(*(x.detach() for x in vecs), dlam)
+        for r, g in zip(ref, got):
+            assert np.max(np.abs(r.numpy() - g)) < 1e-13
+        base = [x.detach().numpy() for x in vecs]
+        step = 1e-6
+        for which in range(4):
+            for idx in ((0, 0), (3, dl - 1)):
+                plus = [x.copy() for x in base]
+                minus = [x.copy() for x in base]
+                plus[which][idx] += step
+                minus[which][idx] -= step
+                fd = np.sum((oracle.reparam_lambda(*plus, 0.3) - oracle.reparam_lambda(*minus, 0.3))
+                            * dlam.numpy()) / (2 * step)
+                assert abs(fd - got[which][idx]) < 1e-8
+
+
 ALL_CHECKS = [
     check_worked_example, check_library_attention, check_cancellation, check_row_sums,
     check_value_offset, check_first_row, check_lambda, check_lambda_init, check_head_norm,
-    check_brute_force, check_decode, check_standard_attention,
+    check_brute_force, check_decode, check_standard_attention, check_backward_autograd,
+    check_backward_finite_diff, check_backward_identities, check_lambda_backward,
 ]

@@ -14,7 +14,9 @@ import pytest
 import oracle.diffattn_oracle as od
 from tests import oracle_pins
 
-_REAL_ATTENTION = od.attention  # the real function, wrapped by two mutants below
+_REAL_ATTENTION = od.attention  # the real functions, wrapped by mutants below
+_REAL_BACKWARD = od.diff_attention_backward
+_REAL_LAMBDA_BACKWARD = od.reparam_lambda_backward
 
 
 
@@ -114,6 +116,51 @@ def _attention_keys_as_values(q, k, v, causal=True, row_block=512):
                                     causal, row_block)
 
 
+def _softmax_bwd_no_rowsum(a, da):
+    return a * da
+
+
+def _softmax_bwd_wrong_axis(a, da):
+    return a * (da - np.sum(da * a, axis=-2, keepdims=True))
+
+
+def _norm_bwd_no_projection(opre, dy, lambda_init, eps):
+    g = 1.0 / np.sqrt(np.mean(opre * opre, axis=-1, keepdims=True) + eps)
+    return (1.0 - lambda_init) * g * dy
+
+
+def _norm_bwd_no_scale(opre, dy, lambda_init, eps):
+    return od._head_rmsnorm_backward(opre, dy, 0.0, eps) if lambda_init else dy
+
+
+def _bwd_dlam_sign(*args, **kw):
+    g = _REAL_BACKWARD(*args, **kw)
+    return (*g[:5], -g[5])
+
+
+def _bwd_dk_reversed_keys(*args, **kw):
+    # an index slip that writes key j's gradient to key T-1-j
+    dq1, dk1, dq2, dk2, dv, dl = _REAL_BACKWARD(*args, **kw)
+    return dq1, dk1[..., ::-1, :], dq2, dk2, dv, dl
+
+
+def _bwd_dv_first_map_only(q1, k1, q2, k2, v, lam, dout, causal=True, headnorm=False, lambda_init=0.8,
+                           eps=1e-5):
+    g = _REAL_BACKWARD(q1, k1, q2, k2, v, 0.0, dout, causal, headnorm, lambda_init, eps)
+    r = _REAL_BACKWARD(q1, k1, q2, k2, v, lam, dout, causal, headnorm, lambda_init, eps)
+    return (*r[:4], g[4], r[5])
+
+
+def _lambda_bwd_self(lq1, lk1, lq2, lk2, dlam):
+    a, b, c, d = _REAL_LAMBDA_BACKWARD(lq1, lk1, lq2, lk2, dlam)
+    return b, a, d, c
+
+
+def _lambda_bwd_plus(lq1, lk1, lq2, lk2, dlam):
+    a, b, c, d = _REAL_LAMBDA_BACKWARD(lq1, lk1, lq2, lk2, dlam)
+    return a, b, -c, -d
+
+
 MUTANTS = {
     "scale_1_over_sqrt_2d": ("_scores", _make_scores(lambda d: 1 / math.sqrt(2 * d), lambda j, i: j > i)),
     "scale_missing": ("_scores", _make_scores(lambda d: 1.0, lambda j, i: j > i)),
@@ -136,6 +183,15 @@ MUTANTS = {
     "norm_eps_outside_sqrt": ("head_rmsnorm", _norm_eps_outside),
     "attention_mask_ignored": ("attention", _attention_mask_ignored),
     "attention_keys_as_values": ("attention", _attention_keys_as_values),
+    "softmax_bwd_drops_rowsum": ("_softmax_backward_rows", _softmax_bwd_no_rowsum),
+    "softmax_bwd_wrong_axis": ("_softmax_backward_rows", _softmax_bwd_wrong_axis),
+    "norm_bwd_drops_projection": ("_head_rmsnorm_backward", _norm_bwd_no_projection),
+    "norm_bwd_drops_scale": ("_head_rmsnorm_backward", _norm_bwd_no_scale),
+    "bwd_dlambda_sign": ("diff_attention_backward", _bwd_dlam_sign),
+    "bwd_dk_reversed_keys": ("diff_attention_backward", _bwd_dk_reversed_keys),
+    "bwd_dv_first_map_only": ("diff_attention_backward", _bwd_dv_first_map_only),
+    "lambda_bwd_own_vector": ("reparam_lambda_backward", _lambda_bwd_self),
+    "lambda_bwd_second_sign": ("reparam_lambda_backward", _lambda_bwd_plus),
 }
 
 
