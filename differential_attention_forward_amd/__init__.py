@@ -25,6 +25,8 @@ __all__ = [
     "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
     "diffattn_fwd_reparam", "diffattn_attention_fwd",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
+    "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_bwd_workspace_bytes",
+    "diffattn_bwd",
 ]
 
 DIFFATTN_F32 = 0
@@ -50,6 +52,13 @@ _SIGS = {
     "diffattn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "diffattn_decode": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F, _I,
                              _VP, ctypes.c_size_t, _VP, _VP]),
+    "diffattn_train_saved_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "diffattn_fwd_train": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
+                                _VP, _VP, ctypes.c_size_t, _VP]),
+    "diffattn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "diffattn_bwd": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                          ctypes.c_size_t, _I, _I, _F, _F, _VP, _VP, _VP, _VP, _VP, _VP,
+                          _VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
 }
 
 
@@ -262,3 +271,70 @@ def diffattn_decode(q1, k1, q2, k2, v, lam, headnorm: bool = False, lambda_init:
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _ptr(out), _stream(stream)))
     return out
+
+
+def diffattn_train_saved_bytes(B: int, H: int, T: int, D: int) -> int:
+    return int(lib().diffattn_train_saved_bytes(B, H, T, D))
+
+
+def diffattn_bwd_workspace_bytes(B: int, H: int, T: int, D: int) -> int:
+    return int(lib().diffattn_bwd_workspace_bytes(B, H, T, D))
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def diffattn_fwd_train(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
+                       lambda_init: float = 0.8, eps: float = 1e-5, out=None, saved=None,
+                       stream=None):
+    """Training forward (bf16, D = 64): the output of diffattn_fwd plus the
+    saved state diffattn_bwd reads.  Returns (out, saved); ``saved`` is an
+    opaque uint8 device tensor of diffattn_train_saved_bytes bytes."""
+    q1, k1, q2, k2, v = _fwd_inputs(q1, k1, q2, k2, v)
+    b, h, t, d = q1.shape
+    lamv = _lambda_vec(lam, h, q1.device)
+    if out is None:
+        out = torch.empty_like(v)
+    if saved is None:
+        saved = torch.empty(max(diffattn_train_saved_bytes(b, h, t, d), 16), device=q1.device,
+                            dtype=torch.uint8)
+    _check(lib().diffattn_fwd_train(_dtype_code(q1), b, h, t, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                                    _ptr(k2), _ptr(v), _ptr(lamv), int(bool(causal)),
+                                    int(bool(headnorm)), float(lambda_init), float(eps), _ptr(out),
+                                    _ptr(saved), _nbytes(saved), _stream(stream)))
+    return out, saved
+
+
+def diffattn_bwd(q1, k1, q2, k2, v, lam, dout, saved, causal: bool = True,
+                 headnorm: bool = False, lambda_init: float = 0.8, eps: float = 1e-5,
+                 lvecs=None, workspace=None, stream=None):
+    """Backward of diffattn_fwd_train.  Returns (dq1, dk1, dq2, dk2, dv, dlambda)
+    and, when ``lvecs`` = (lq1, lk1, lq2, lk2) ([H, Dl] fp32) is given, a
+    seventh item: the tuple of their four gradients."""
+    q1, k1, q2, k2, v = _fwd_inputs(q1, k1, q2, k2, v)
+    b, h, t, d = q1.shape
+    dout = _dev(dout, "dout")
+    if dout.shape != v.shape or dout.dtype != v.dtype:
+        raise ValueError("dout must match v in shape and dtype")
+    lamv = _lambda_vec(lam, h, q1.device)
+    grads = [torch.empty_like(x) for x in (q1, k1, q2, k2, v)]
+    dlam = torch.empty((h,), device=q1.device, dtype=torch.float32)
+    vec_ptrs, dvec_ptrs, dl, dvecs = [None] * 4, [None] * 4, 0, None
+    if lvecs is not None:
+        vecs = [_dev(x, n).float() for x, n in zip(lvecs, ("lq1", "lk1", "lq2", "lk2"))]
+        if vecs[0].dim() != 2 or vecs[0].shape[0] != h or any(x.shape != vecs[0].shape for x in vecs):
+            raise ValueError(f"the four lambda vectors must all be [{h}, Dl]")
+        dl = vecs[0].shape[1]
+        dvecs = [torch.empty_like(x) for x in vecs]
+        vec_ptrs, dvec_ptrs = [_ptr(x) for x in vecs], [_ptr(x) for x in dvecs]
+    if workspace is None:
+        workspace = torch.empty(max(diffattn_bwd_workspace_bytes(b, h, t, d), 16), device=q1.device,
+                                dtype=torch.uint8)
+    _check(lib().diffattn_bwd(_dtype_code(q1), b, h, t, d, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2),
+                              _ptr(v), _ptr(lamv), _ptr(dout), _ptr(saved), _nbytes(saved),
+                              int(bool(causal)), int(bool(headnorm)), float(lambda_init), float(eps),
+                              *map(_ptr, grads), _ptr(dlam), *vec_ptrs, dl, *dvec_ptrs,
+                              _ptr(workspace), _nbytes(workspace), _stream(stream)))
+    res = (*grads, dlam)
+    return res + (tuple(dvecs),) if dvecs is not None else res

@@ -31,7 +31,7 @@ const char* diffattn_status_string(int status) {
     case DIFFATTN_OK: return "ok";
     case DIFFATTN_ERR_INVALID: return "invalid argument";
     case DIFFATTN_ERR_UNSUPPORTED: return "unsupported dtype, head width, alignment or size";
-    case DIFFATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case DIFFATTN_ERR_WORKSPACE: return "workspace or saved-state buffer missing or too small";
     case DIFFATTN_ERR_HIP: return "HIP kernel launch failed";
   }
   return "unknown status";
@@ -92,6 +92,9 @@ diffattn_status check_fwd(int dtype, int B, int H, int T, int D, const void* q1,
   a.lam_init = 0.0f;
   a.lam_out = nullptr;
   a.out = out;
+  a.save_o1 = nullptr;
+  a.save_o2 = nullptr;
+  a.save_lse = nullptr;
   a.B = B;
   a.H = H;
   a.T = T;
@@ -183,6 +186,9 @@ diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, co
   a.lam_init = 0.0f;
   a.lam_out = nullptr;
   a.out = out;
+  a.save_o1 = nullptr;
+  a.save_o2 = nullptr;
+  a.save_lse = nullptr;
   a.B = B;
   a.H = H;
   a.T = T;
@@ -190,6 +196,156 @@ diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, co
   a.out_scale = 1.0f;
   a.eps = 1.0f;
   return from_hip(diffattn::launch_attention(a, D, causal != 0, stream));
+}
+
+// ---- training: forward that saves what the backward needs, and the backward --
+
+namespace {
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// every span in outs must be disjoint from every span in ins and from the
+// other outs (null entries are skipped)
+bool disjoint(const Span* ins, int nin, const Span* outs, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    if (!outs[i].p) continue;
+    for (int j = 0; j < nin; ++j)
+      if (ins[j].p && overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return false;
+    for (int j = i + 1; j < nout; ++j)
+      if (outs[j].p && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return false;
+  }
+  return true;
+}
+
+bool train_sizes_ok(int B, int H, int T, int D) {
+  if (B < 1 || H < 1 || T < 1 || D != 64) return false;
+  return (long long)B * H <= 0x7fffffffLL && (long long)T * 2 * D <= 0x7fffffffLL;
+}
+
+}  // namespace
+
+size_t diffattn_train_saved_bytes(int B, int H, int T, int D) {
+  if (!train_sizes_ok(B, H, T, D)) return 0;
+  const size_t bht = (size_t)B * H * T;
+  return 2 * bht * 2 * D * sizeof(float) + 2 * bht * sizeof(float);
+}
+
+diffattn_status diffattn_fwd_train(int dtype, int B, int H, int T, int D, const void* q1,
+                                   const void* k1, const void* q2, const void* k2, const void* v,
+                                   const float* lambda, int causal, int headnorm, float lambda_init,
+                                   float eps, void* out, void* saved, size_t saved_bytes,
+                                   hipStream_t stream) {
+  diffattn::FwdArgs a;
+  size_t nout = 0;
+  const diffattn_status st = check_fwd(dtype, B, H, T, D, q1, k1, q2, k2, v, headnorm, eps, out, a, nout);
+  if (st != DIFFATTN_OK) return st;
+  if (!lambda || !saved) return DIFFATTN_ERR_INVALID;
+  if (dtype != DIFFATTN_BF16 || !train_sizes_ok(B, H, T, D)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(lambda, 4) || !aligned(saved, 16)) return DIFFATTN_ERR_UNSUPPORTED;
+  const size_t need = diffattn_train_saved_bytes(B, H, T, D);
+  if (saved_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+  const size_t nqk = nout / 2;
+  const Span ins[6] = {{q1, nqk}, {k1, nqk}, {q2, nqk}, {k2, nqk}, {v, nout}, {lambda, (size_t)H * 4}};
+  const Span outs[2] = {{out, nout}, {saved, need}};
+  if (!disjoint(ins, 6, outs, 2)) return DIFFATTN_ERR_INVALID;
+  const size_t bht = (size_t)B * H * T;
+  a.lam = lambda;
+  a.out_scale = 1.0f - lambda_init;
+  a.eps = eps;
+  a.save_o1 = (float*)saved;
+  a.save_o2 = (float*)saved + bht * 2 * D;
+  a.save_lse = (float*)saved + 2 * bht * 2 * D;
+  return from_hip(diffattn::launch_fwd(a, dtype, D, causal != 0, headnorm != 0, stream));
+}
+
+size_t diffattn_bwd_workspace_bytes(int B, int H, int T, int D) {
+  if (!train_sizes_ok(B, H, T, D)) return 0;
+  const size_t bh = (size_t)B * H;
+  const size_t tp = round_up((size_t)T, 64);
+  return round_up(bh * T * 2 * D * 2, 256) + round_up(bh * 4 * tp * 4, 256) + bh * (tp / 64) * 4;
+}
+
+diffattn_status diffattn_bwd(int dtype, int B, int H, int T, int D, const void* q1, const void* k1,
+                             const void* q2, const void* k2, const void* v, const float* lambda,
+                             const void* dout, const void* saved, size_t saved_bytes, int causal,
+                             int headnorm, float lambda_init, float eps, void* dq1, void* dk1,
+                             void* dq2, void* dk2, void* dv, float* dlambda, const float* lq1,
+                             const float* lk1, const float* lq2, const float* lk2, int Dl,
+                             float* dlq1, float* dlk1, float* dlq2, float* dlk2, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!q1 || !k1 || !q2 || !k2 || !v || !lambda || !dout || !saved) return DIFFATTN_ERR_INVALID;
+  if (!dq1 || !dk1 || !dq2 || !dk2 || !dv || !dlambda) return DIFFATTN_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1) return DIFFATTN_ERR_INVALID;
+  if (headnorm && !(eps > 0.0f)) return DIFFATTN_ERR_INVALID;
+  const bool vec = lq1 != nullptr;
+  const void* vp[8] = {lq1, lk1, lq2, lk2, dlq1, dlk1, dlq2, dlk2};
+  for (const void* p : vp)
+    if ((p != nullptr) != vec) return DIFFATTN_ERR_INVALID;
+  if (vec && Dl < 1) return DIFFATTN_ERR_INVALID;
+  if (dtype != DIFFATTN_BF16 || !train_sizes_ok(B, H, T, D)) return DIFFATTN_ERR_UNSUPPORTED;
+  const void* t16[13] = {q1, k1, q2, k2, v, dout, saved, dq1, dk1, dq2, dk2, dv, workspace};
+  for (const void* p : t16)
+    if (p && !aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(lambda, 4) || !aligned(dlambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  for (const void* p : vp)
+    if (p && !aligned(p, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  const size_t need_saved = diffattn_train_saved_bytes(B, H, T, D);
+  const size_t need_ws = diffattn_bwd_workspace_bytes(B, H, T, D);
+  if (saved_bytes < need_saved || !workspace || workspace_bytes < need_ws) return DIFFATTN_ERR_WORKSPACE;
+  const size_t nqk = (size_t)B * H * T * D * 2, nv = 2 * nqk, nl = (size_t)H * 4;
+  const size_t nvec = vec ? (size_t)H * Dl * 4 : 0;
+  const Span ins[11] = {{q1, nqk}, {k1, nqk}, {q2, nqk}, {k2, nqk}, {v, nv}, {dout, nv},
+                        {saved, need_saved}, {lambda, nl}, {lq1, nvec}, {lk1, nvec}, {lq2, nvec}};
+  const Span ins2[1] = {{lk2, nvec}};
+  const Span outs[11] = {{dq1, nqk}, {dk1, nqk}, {dq2, nqk}, {dk2, nqk}, {dv, nv}, {dlambda, nl},
+                         {dlq1, nvec}, {dlk1, nvec}, {dlq2, nvec}, {dlk2, nvec}, {workspace, need_ws}};
+  if (!disjoint(ins, 11, outs, 11) || !disjoint(ins2, 1, outs, 11)) return DIFFATTN_ERR_INVALID;
+
+  diffattn::BwdArgs a;
+  const size_t bh = (size_t)B * H, bht = bh * T;
+  const int Tp = (int)round_up((size_t)T, 64);
+  a.q1 = q1;
+  a.k1 = k1;
+  a.q2 = q2;
+  a.k2 = k2;
+  a.v = v;
+  a.dout = dout;
+  a.o1 = (const float*)saved;
+  a.o2 = (const float*)saved + bht * 2 * D;
+  a.lse = (const float*)saved + 2 * bht * 2 * D;
+  a.lam = lambda;
+  char* ws = (char*)workspace;
+  a.dopre = ws;
+  a.stats = (float*)(ws + round_up(bht * 2 * D * 2, 256));
+  a.dlam_part = (float*)(ws + round_up(bht * 2 * D * 2, 256) + round_up(bh * 4 * Tp * 4, 256));
+  a.dq1 = dq1;
+  a.dk1 = dk1;
+  a.dq2 = dq2;
+  a.dk2 = dk2;
+  a.dv = dv;
+  a.dlam = dlambda;
+  const float* lv[4] = {lq1, lk1, lq2, lk2};
+  float* dlv[4] = {dlq1, dlk1, dlq2, dlk2};
+  for (int i = 0; i < 4; ++i) {
+    a.lvec[i] = lv[i];
+    a.dlvec[i] = dlv[i];
+  }
+  a.Dl = vec ? Dl : 0;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.Tp = Tp;
+  a.nchunk = Tp / 64;
+  a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
+  a.grad_scale = (float)(1.0 / sqrt((double)D));
+  a.out_scale = 1.0f - lambda_init;
+  a.eps = eps;
+  return from_hip(diffattn::launch_bwd(a, D, causal != 0, headnorm != 0, stream));
 }
 
 int diffattn_decode_default_splits(int B, int H, int L) {

@@ -1,0 +1,743 @@
+// Differential-attention backward for gfx950 (CDNA4), bf16 inputs.
+//
+// Gradients of Out = (A1 - lam A2) V, optionally head-normed (paperleet
+// "Differential Transformer Attention": gradients flow through both Q/K
+// branches, the value and the coefficient; aifetchly "Differential
+// Transformer: Canceling LLM Attention Noise", sections 3 and 4 for lambda
+// and the head norm).  With dOpre the gradient reaching the pre-norm output
+// Opre = O1 - lam O2 (O1 = A1 V, O2 = A2 V), D1 = rowsum(dOpre * O1) and
+// D2 = -lam rowsum(dOpre * O2):
+//   dP  = dOpre V^T                       (shared by both maps)
+//   dS1 = A1 * (dP - D1),  dS2 = A2 * (-lam dP - D2)
+//   dV  = (A1 - lam A2)^T dOpre
+//   dQm = dSm Km / sqrt(D),  dKm = dSm^T Qm / sqrt(D)      (m = 1, 2)
+//   dlam = -sum dOpre * O2
+// The maps are never stored: A1, A2 are recomputed tile by tile from the
+// scores and the per-row log-sum-exp the training forward saved.
+//
+// Kernels (in launch order):
+//  * prep: one pass over rows (HBM bound).  Head-norm vector-Jacobian product
+//    (if enabled) -> dOpre in bf16, D1 and D2 from the rounded dOpre, and a
+//    per-chunk partial of dlam from the fp32 dOpre (no atomics: summed later
+//    in a fixed order).
+//  * kv: one workgroup per block of keys, one wave per 32 keys, looping over
+//    query tiles staged in LDS.  Scores are computed as S = Q K^T so that a
+//    lane owns one key and sees 16 queries: the probabilities and dS are then
+//    already the B operands of dV^T = dOpre^T P and dK^T = Q^T dS, whose A
+//    operands come from transposing LDS reads of the staged Q and dOpre rows.
+//    K1, K2 and V of the wave's keys stay in VGPRs for the whole kernel.
+//  * q: one workgroup per block of queries, one wave per 32 queries, looping
+//    over key tiles staged in LDS like the forward.  Scores as S^T = K Q^T (a
+//    lane owns one query: its log-sum-exp and D values are per lane), dS^T is
+//    the B operand of dQ^T = K^T dS^T.  Q1, Q2 and dOpre stay in VGPRs.
+//  * lambda: dlam per head from the partials; with the re-parameterisation
+//    vectors, their gradients as well.
+// LDS tiles use one XOR swizzle of 16-byte columns (swz2) that keeps both the
+// row reads (A operands of S and dP) and the transposing reads (A operands
+// of the gradient products) free of bank conflicts.
+#include "common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+// 16-byte column swizzle for rows whose pitch is a multiple of 128 bytes.
+// Row reads: 8 lanes read one column of 8 consecutive rows -> 8 distinct
+// columns.  Transposing reads: 16 lanes read two adjacent columns (even
+// first) of 4 consecutive rows starting at a multiple of 4 -> 8 distinct.
+__device__ inline int swz2(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// ============================================================================
+// prep
+// ============================================================================
+constexpr int kPrepRows = 64;  // rows per workgroup (= padding unit of Tp)
+
+template <int D, bool HEADNORM>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int DV = 2 * D;
+  constexpr int TPR = DV / 8;          // threads per row, 8 channels each
+  constexpr int RPP = 256 / TPR;       // rows per pass
+  __shared__ float red[4];
+  const int chunk = blockIdx.x % a.nchunk;
+  const int bh = blockIdx.x / a.nchunk;
+  const int h = bh % a.H;
+  const int T = a.T;
+  const int tid = threadIdx.x;
+  const int sub = tid % TPR;
+  const float lam = a.lam[h];
+  const size_t v_off = (size_t)bh * T * DV;
+  const bf16* __restrict__ dout = (const bf16*)a.dout + v_off;
+  const float* __restrict__ o1 = a.o1 + v_off;
+  const float* __restrict__ o2 = a.o2 + v_off;
+  bf16* __restrict__ dop = (bf16*)a.dopre + v_off;
+  float* __restrict__ st = a.stats + (size_t)bh * 4 * a.Tp;
+  float part = 0.0f;
+  // log-sum-exp of both maps into the padded statistics block (padding: 0,
+  // only ever read for masked queries)
+  if (tid < 2 * kPrepRows) {
+    const int br = tid / kPrepRows;
+    const int q = chunk * kPrepRows + tid % kPrepRows;
+    st[(size_t)br * a.Tp + q] = q < T ? a.lse[((size_t)bh * 2 + br) * T + q] : 0.0f;
+  }
+  for (int r0 = 0; r0 < kPrepRows; r0 += RPP) {
+    const int q = chunk * kPrepRows + r0 + tid / TPR;
+    if (q >= T) {
+      if (sub < 2) st[(size_t)(2 + sub) * a.Tp + q] = 0.0f;
+      continue;
+    }
+    const size_t e = (size_t)q * DV + sub * 8;
+    const u32x4 raw = *(const u32x4*)(dout + e);
+    float dy[8], x1[8], x2[8], op[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dy[2 * i] = bf16lo(raw[i]);
+      dy[2 * i + 1] = bf16hi(raw[i]);
+    }
+    const floatx4 a0 = *(const floatx4*)(o1 + e), a1 = *(const floatx4*)(o1 + e + 4);
+    const floatx4 b0 = *(const floatx4*)(o2 + e), b1 = *(const floatx4*)(o2 + e + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x1[i] = a0[i];
+      x1[i + 4] = a1[i];
+      x2[i] = b0[i];
+      x2[i + 4] = b1[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float lt2 = lam * x2[i];
+      op[i] = x1[i] - lt2;  // the forward's pre-norm output, same rounding
+    }
+    float g[8];
+    if constexpr (HEADNORM) {
+      float ss = 0.0f, dd = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ss = fmaf(op[i], op[i], ss);
+        dd = fmaf(dy[i], op[i], dd);
+      }
+#pragma unroll
+      for (int o = TPR / 2; o >= 1; o >>= 1) {
+        ss += __shfl_xor(ss, o);
+        dd += __shfl_xor(dd, o);
+      }
+      const float r = rsqrtf(ss * (1.0f / DV) + a.eps);
+      const float c = dd * (1.0f / DV) * r * r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = a.out_scale * r * (dy[i] - op[i] * c);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = dy[i];
+    }
+    bf16x8 gb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gb[i] = (bf16)g[i];
+    *(bf16x8*)(dop + e) = gb;
+    // D1, D2 from the rounded dOpre (the values dP is formed from, so that
+    // each row of dS sums to zero as it should); dlambda from the fp32 one
+    float d1 = 0.0f, d2 = 0.0f, dl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float gr = (float)gb[i];
+      d1 = fmaf(gr, x1[i], d1);
+      d2 = fmaf(gr, x2[i], d2);
+      dl = fmaf(g[i], x2[i], dl);
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) {
+      d1 += __shfl_xor(d1, o);
+      d2 += __shfl_xor(d2, o);
+      dl += __shfl_xor(dl, o);
+    }
+    if (sub == 0) {
+      st[(size_t)2 * a.Tp + q] = d1;
+      st[(size_t)3 * a.Tp + q] = -lam * d2;
+      part += dl;
+    }
+  }
+  part = wave_sum(part);
+  if ((tid & 63) == 0) red[tid >> 6] = part;
+  __syncthreads();
+  if (tid == 0) a.dlam_part[(size_t)bh * a.nchunk + chunk] = -((red[0] + red[1]) + (red[2] + red[3]));
+}
+
+// ============================================================================
+// lambda: dlam per head, then the re-parameterisation vectors' gradients
+// ============================================================================
+__global__ __launch_bounds__(64) void bwd_lambda_kernel(BwdArgs a) {
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x;
+  float s = 0.0f;
+  for (int b = 0; b < a.B; ++b) {
+    const float* p = a.dlam_part + ((size_t)b * a.H + h) * a.nchunk;
+    for (int i = lane; i < a.nchunk; i += 64) s += p[i];
+  }
+  const float dl = wave_sum(s);
+  if (lane == 0) a.dlam[h] = dl;
+  if (a.lvec[0] == nullptr) return;
+  // lam = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init
+  const size_t base = (size_t)h * a.Dl;
+  float d1 = 0.0f, d2 = 0.0f;
+  for (int i = lane; i < a.Dl; i += 64) {
+    d1 = fmaf(a.lvec[0][base + i], a.lvec[1][base + i], d1);
+    d2 = fmaf(a.lvec[2][base + i], a.lvec[3][base + i], d2);
+  }
+  const float e1 = dl * expf(wave_sum(d1));
+  const float e2 = -dl * expf(wave_sum(d2));
+  for (int i = lane; i < a.Dl; i += 64) {
+    a.dlvec[0][base + i] = e1 * a.lvec[1][base + i];
+    a.dlvec[1][base + i] = e1 * a.lvec[0][base + i];
+    a.dlvec[2][base + i] = e2 * a.lvec[3][base + i];
+    a.dlvec[3][base + i] = e2 * a.lvec[2][base + i];
+  }
+}
+
+// ============================================================================
+// kv: dK1, dK2, dV
+// ============================================================================
+template <int D, int NW, int NSTAGE>
+struct CfgKV {
+  static constexpr int DV = 2 * D;
+  static constexpr int BK = 32 * NW;          // keys per workgroup
+  static constexpr int BQ = 64;               // queries per staged tile
+  static constexpr int QBYTES = BQ * D * 2;   // one of Q1, Q2
+  static constexpr int OBYTES = BQ * DV * 2;  // dOpre
+  static constexpr int SBYTES = 4 * BQ * 4;   // lse1, lse2, D1, D2
+  static constexpr int STAGE = 2 * QBYTES + OBYTES + SBYTES;
+  static constexpr int QSEG = QBYTES / 1024;
+  static constexpr int OSEG = OBYTES / 1024;
+  static constexpr int NSEG = STAGE / 1024;
+  static constexpr int SEGW = (NSEG + NW - 1) / NW;
+  static constexpr int SEGW_MIN = NSEG / NW;
+  static constexpr int SOFF = 2 * QBYTES + OBYTES;  // statistics within a stage
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int VSTEPS = DV / 16;
+  static constexpr int CBK = D / 32;
+  static constexpr int CBV = DV / 32;
+  static constexpr int SMEM = NSTAGE * STAGE;
+  static_assert(BK % BQ == 0, "a key block starts on a query tile");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 3, "two or three stages");
+  static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <int D, int NW, int NSTAGE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_kernel(BwdArgs a) {
+  using C = CfgKV<D, NW, NSTAGE>;
+  constexpr int BQ = C::BQ;
+  constexpr int DV = C::DV;
+  constexpr int PD = NSTAGE - 1;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int T = a.T;
+
+  const int nkt = (T + C::BK - 1) / C::BK;
+  const int w = xcd_remap(blockIdx.x, a.B * a.H * nkt);
+  const int bh = w / nkt;
+  const int kt = w % nkt;  // causal: low key blocks see the most queries, issued first
+  const int h = bh % a.H;
+
+  const size_t qk_off = (size_t)bh * T * D;
+  const size_t v_off = (size_t)bh * T * DV;
+  const bf16* __restrict__ Q1 = scalar_ptr((const bf16*)a.q1 + qk_off);
+  const bf16* __restrict__ Q2 = scalar_ptr((const bf16*)a.q2 + qk_off);
+  const bf16* __restrict__ dO = scalar_ptr((const bf16*)a.dopre + v_off);
+  const float* __restrict__ ST = scalar_ptr((const float*)a.stats + (size_t)bh * 4 * a.Tp);
+
+  const int k0 = kt * C::BK + wave * 32;       // first key of this wave
+  const int key = k0 + l32;                    // this lane's key (B-operand column)
+  const int q_begin = CAUSAL ? kt * C::BK : 0;
+  const int ntiles = (T - q_begin + BQ - 1) / BQ;
+  const float sc = a.score_scale;
+  const float lam = a.lam[h];
+
+  // ---- K1, K2, V rows of the lane's key (B operands), clamped in bounds -----
+  bf16x8 kf[2][C::KSTEPS];
+  bf16x8 vf[C::VSTEPS];
+  {
+    const size_t kr = (size_t)min(key, T - 1);
+    const bf16* k1 = (const bf16*)a.k1 + qk_off + kr * D;
+    const bf16* k2 = (const bf16*)a.k2 + qk_off + kr * D;
+    const bf16* vv = (const bf16*)a.v + v_off + kr * DV;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      kf[0][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k1 + ks * 16 + hi * 8));
+      kf[1][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k2 + ks * 16 + hi * 8));
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::VSTEPS; ++ks)
+      vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vv + ks * 16 + hi * 8));
+  }
+
+  // ---- asynchronous query-tile loads ----------------------------------------
+  // Segments 0 .. 2 QSEG - 1: Q1 then Q2 (rows of 2D bytes), then OSEG of
+  // dOpre (rows of 2 DV bytes), then one of statistics (lane l copies 4
+  // floats of row l / 16 of the [4][Tp] block).  Rows past the end load row
+  // T - 1; the padded statistics are in bounds.
+  constexpr int CK = D / 8, RK = 64 / CK, CO = DV / 8, RO = 64 / CO;
+  auto issue_rt = [&](int jt, char* sb) __attribute__((always_inline)) {
+    const int q0 = q_begin + jt * BQ;
+#pragma unroll
+    for (int i = 0; i < C::SEGW; ++i) {
+      const int seg = wave + i * NW;
+      if (seg >= C::NSEG) break;
+      if (seg < 2 * C::QSEG) {
+        const int which = seg / C::QSEG;
+        const int g = seg % C::QSEG;
+        const int r = g * RK + lane / CK;
+        const int c = (lane % CK) ^ swz2(r);
+        const uint32_t row = (uint32_t)min(q0 + r, T - 1);
+        dma16(which ? Q2 : Q1, row * (D * 2) + c * 16, sb + which * C::QBYTES + g * 1024);
+      } else if (seg < 2 * C::QSEG + C::OSEG) {
+        const int g = seg - 2 * C::QSEG;
+        const int r = g * RO + lane / CO;
+        const int c = (lane % CO) ^ swz2(r);
+        const uint32_t row = (uint32_t)min(q0 + r, T - 1);
+        dma16(dO, row * (DV * 2) + c * 16, sb + 2 * C::QBYTES + g * 1024);
+      } else {
+        const uint32_t off = ((uint32_t)(lane >> 4) * a.Tp + q0 + 4 * (lane & 15)) * 4;
+        dma16(ST, off, sb + C::SOFF);
+      }
+    }
+  };
+  auto issue = [&](int jt, auto st) __attribute__((always_inline)) {
+    issue_rt(jt, smem + decltype(st)::value * C::STAGE);
+  };
+
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): K, V in registers
+  issue(0, std::integral_constant<int, 0>{});
+  if constexpr (PD > 1)
+    if (1 < ntiles) issue(1, std::integral_constant<int, 1>{});
+
+  floatx16 dvT[C::CBV], dk1T[C::CBK], dk2T[C::CBK];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int cb = 0; cb < C::CBV; ++cb) dvT[cb][r] = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < C::CBK; ++cb) {
+      dk1T[cb][r] = 0.0f;
+      dk2T[cb][r] = 0.0f;
+    }
+  }
+
+  // per-lane LDS offsets
+  const int sw_row = swz2(l32);                          // row reads: row = 32 sub + l32
+  const int tq = lane & 3;
+  const int tk = (lane >> 2) & 3;
+  const int t_row = 4 * hi + tk;                         // + 32 sub + 16 ks (+ 8 for the upper half)
+  const int t_chunk = 2 * ((lane >> 4) & 1) + (tq >> 1); // + 4 cb
+  const int t_sw = (tk << 1) | hi;                       // swz2 of every transposed-read row
+  const int t_byte = (tq & 1) * 8;
+
+  // A operand of a gradient product: 8 queries (in the lane's probability
+  // order) of channel 32 cb + l32, from a tile with rows of RB bytes
+  auto tr_read = [&](const char* tile, int rb, int sub, int ks, int cb) __attribute__((always_inline)) {
+    const char* base = tile + (32 * sub + 16 * ks + t_row) * rb + (((4 * cb + t_chunk) ^ t_sw) << 4) + t_byte;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * rb));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+  };
+
+  auto compute_sub = [&](int q0, int sub, const char* sb) __attribute__((always_inline)) {
+    const int qs = q0 + 32 * sub;
+    const char* tq1 = sb;
+    const char* tq2 = sb + C::QBYTES;
+    const char* tdo = sb + 2 * C::QBYTES;
+    const float* tst = (const float*)(sb + C::SOFF) + 32 * sub;
+    floatx16 s1, s2, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s1[r] = 0.0f;
+      s2[r] = 0.0f;
+      dp[r] = 0.0f;
+    }
+    // S = Q K^T (rows: queries, lane column: key) for both maps
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const int off = (32 * sub + l32) * (2 * D) + (((2 * ks + hi) ^ sw_row) << 4);
+      const bf16x8 a1 = *(const bf16x8*)(tq1 + off);
+      const bf16x8 a2 = *(const bf16x8*)(tq2 + off);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kf[0][ks], s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, kf[1][ks], s2, 0, 0, 0);
+    }
+    // dP = dOpre V^T
+#pragma unroll
+    for (int ks = 0; ks < C::VSTEPS; ++ks) {
+      const bf16x8 ao = *(const bf16x8*)(tdo + (32 * sub + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_row) << 4));
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ks], dp, 0, 0, 0);
+    }
+    // masked elements: future keys (causal) and queries past the end
+    const bool need_mask = (CAUSAL && qs < k0 + 31) || qs + 32 > T;
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = qs + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool masked = q >= T || (CAUSAL && key > q);
+        if (masked) {
+          s1[r] = kNegInf;
+          s2[r] = kNegInf;
+        }
+      }
+    }
+    bf16x8 pc[2], g1[2], g2[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 l1 = *(const floatx4*)(tst + 8 * g + 4 * hi);
+      const floatx4 l2 = *(const floatx4*)(tst + BQ + 8 * g + 4 * hi);
+      const floatx4 e1 = *(const floatx4*)(tst + 2 * BQ + 8 * g + 4 * hi);
+      const floatx4 e2 = *(const floatx4*)(tst + 3 * BQ + 8 * g + 4 * hi);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], sc, -l1[i]));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(s2[r], sc, -l2[i]));
+        const float d1 = p1 * (dp[r] - e1[i]);
+        const float d2 = p2 * fmaf(-lam, dp[r], -e2[i]);
+        const float c = fmaf(-lam, p2, p1);
+        pc[r >> 3][r & 7] = (bf16)c;
+        g1[r >> 3][r & 7] = (bf16)d1;
+        g2[r >> 3][r & 7] = (bf16)d2;
+      }
+    }
+    // dV^T += dOpre^T (P1 - lam P2);  dKm^T += Qm^T dSm
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int cb = 0; cb < C::CBV; ++cb)
+        dvT[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tdo, 2 * DV, sub, ks, cb), pc[ks], dvT[cb], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < C::CBK; ++cb) {
+        dk1T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tq1, 2 * D, sub, ks, cb), g1[ks], dk1T[cb], 0, 0, 0);
+        dk2T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tq2, 2 * D, sub, ks, cb), g2[ks], dk2T[cb], 0, 0, 0);
+      }
+    }
+  };
+
+  auto compute_tile = [&](int jt, const char* sb) __attribute__((always_inline)) {
+    const int q0 = q_begin + jt * BQ;
+#pragma unroll
+    for (int sub = 0; sub < BQ / 32; ++sub) {
+      const int qs = q0 + 32 * sub;
+      // a 32-query block takes part if it holds a query at or after one of the wave's keys
+      if (qs < T && (!CAUSAL || qs + 31 >= k0)) compute_sub(q0, sub, sb);
+    }
+  };
+
+  if (PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
+  else wait_vm_barrier<0>();
+  auto step = [&](int jt, auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    if (jt + PD < ntiles) issue(jt + PD, std::integral_constant<int, (S + PD) % NSTAGE>{});
+    compute_tile(jt, smem + S * C::STAGE);
+    if (jt + PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
+    else wait_vm_barrier<0>();
+  };
+  for (int jt = 0; jt < ntiles; jt += NSTAGE) {
+    step(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 < ntiles) step(jt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NSTAGE > 2)
+      if (jt + 2 < ntiles) step(jt + 2, std::integral_constant<int, 2>{});
+  }
+
+  // ---- store: lane holds 16 channels (4 runs of 4) of its key's rows ----------
+  if (key >= T) return;
+  const float gs = a.grad_scale;
+  bf16* dk1 = (bf16*)a.dk1 + qk_off + (size_t)key * D;
+  bf16* dk2 = (bf16*)a.dk2 + qk_off + (size_t)key * D;
+  bf16* dv = (bf16*)a.dv + v_off + (size_t)key * DV;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+#pragma unroll
+    for (int cb = 0; cb < C::CBK; ++cb) {
+      const int ch = cb * 32 + 8 * g + 4 * hi;
+      const bf16x4 x1 = {(bf16)(dk1T[cb][4 * g] * gs), (bf16)(dk1T[cb][4 * g + 1] * gs),
+                         (bf16)(dk1T[cb][4 * g + 2] * gs), (bf16)(dk1T[cb][4 * g + 3] * gs)};
+      const bf16x4 x2 = {(bf16)(dk2T[cb][4 * g] * gs), (bf16)(dk2T[cb][4 * g + 1] * gs),
+                         (bf16)(dk2T[cb][4 * g + 2] * gs), (bf16)(dk2T[cb][4 * g + 3] * gs)};
+      *(bf16x4*)(dk1 + ch) = x1;
+      *(bf16x4*)(dk2 + ch) = x2;
+    }
+#pragma unroll
+    for (int cb = 0; cb < C::CBV; ++cb) {
+      const int ch = cb * 32 + 8 * g + 4 * hi;
+      const bf16x4 x = {(bf16)dvT[cb][4 * g], (bf16)dvT[cb][4 * g + 1], (bf16)dvT[cb][4 * g + 2],
+                        (bf16)dvT[cb][4 * g + 3]};
+      *(bf16x4*)(dv + ch) = x;
+    }
+  }
+}
+
+// ============================================================================
+// q: dQ1, dQ2
+// ============================================================================
+template <int D, int NW, int NSTAGE>
+struct CfgQ {
+  static constexpr int DV = 2 * D;
+  static constexpr int BR = 32 * NW;          // queries per workgroup
+  static constexpr int BC = 64;               // keys per staged tile
+  static constexpr int KBYTES = BC * D * 2;
+  static constexpr int VBYTES = BC * DV * 2;
+  static constexpr int STAGE = 2 * KBYTES + VBYTES;
+  static constexpr int KSEG = KBYTES / 1024;
+  static constexpr int NSEG = STAGE / 1024;
+  static constexpr int SEGW = (NSEG + NW - 1) / NW;
+  static constexpr int SEGW_MIN = NSEG / NW;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int VSTEPS = DV / 16;
+  static constexpr int CBK = D / 32;
+  static constexpr int SMEM = NSTAGE * STAGE;
+  static_assert(NSTAGE >= 2 && NSTAGE <= 3, "two or three stages");
+  static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <int D, int NW, int NSTAGE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void bwd_q_kernel(BwdArgs a) {
+  using C = CfgQ<D, NW, NSTAGE>;
+  constexpr int BC = C::BC;
+  constexpr int DV = C::DV;
+  constexpr int PD = NSTAGE - 1;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int T = a.T;
+
+  const int nqt = (T + C::BR - 1) / C::BR;
+  const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
+  const int bh = w / nqt;
+  const int qi = w % nqt;
+  const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
+  const int h = bh % a.H;
+
+  const size_t qk_off = (size_t)bh * T * D;
+  const size_t v_off = (size_t)bh * T * DV;
+  const bf16* __restrict__ K1 = scalar_ptr((const bf16*)a.k1 + qk_off);
+  const bf16* __restrict__ K2 = scalar_ptr((const bf16*)a.k2 + qk_off);
+  const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + v_off);
+
+  const int q_tile0 = qt * C::BR;
+  const int q0 = q_tile0 + wave * 32;
+  const int query = q0 + l32;
+  const bool wave_active = q0 < T;
+  const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
+  const int ntiles = (k_end + BC - 1) / BC;
+  const float sc = a.score_scale;
+  const float lam = a.lam[h];
+
+  // ---- the lane's query: Q1, Q2, dOpre rows (B operands) and statistics -----
+  bf16x8 qf[2][C::KSTEPS];
+  bf16x8 df[C::VSTEPS];
+  float lse1, lse2, e1, e2;
+  {
+    const size_t qr = (size_t)min(query, T - 1);
+    const bf16* q1 = (const bf16*)a.q1 + qk_off + qr * D;
+    const bf16* q2 = (const bf16*)a.q2 + qk_off + qr * D;
+    const bf16* go = (const bf16*)a.dopre + v_off + qr * DV;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      qf[0][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q1 + ks * 16 + hi * 8));
+      qf[1][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q2 + ks * 16 + hi * 8));
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::VSTEPS; ++ks)
+      df[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(go + ks * 16 + hi * 8));
+    const float* st = a.stats + (size_t)bh * 4 * a.Tp + qr;
+    lse1 = st[0];
+    lse2 = st[a.Tp];
+    e1 = st[2 * (size_t)a.Tp];
+    e2 = st[3 * (size_t)a.Tp];
+  }
+
+  // ---- asynchronous key-tile loads (K1, K2, V; swizzled with swz2) ----------
+  constexpr int CK = D / 8, RK = 64 / CK, CV = DV / 8, RV = 64 / CV;
+  auto issue_rt = [&](int kt, char* sb) __attribute__((always_inline)) {
+    const int key0 = kt * BC;
+#pragma unroll
+    for (int i = 0; i < C::SEGW; ++i) {
+      const int seg = wave + i * NW;
+      if (seg >= C::NSEG) break;
+      if (seg < 2 * C::KSEG) {
+        const int which = seg / C::KSEG;
+        const int g = seg % C::KSEG;
+        const int r = g * RK + lane / CK;
+        const int c = (lane % CK) ^ swz2(r);
+        const uint32_t row = (uint32_t)min(key0 + r, T - 1);
+        dma16(which ? K2 : K1, row * (D * 2) + c * 16, sb + which * C::KBYTES + g * 1024);
+      } else {
+        const int g = seg - 2 * C::KSEG;
+        const int r = g * RV + lane / CV;
+        const int c = (lane % CV) ^ swz2(r);
+        const uint32_t row = (uint32_t)min(key0 + r, T - 1);
+        dma16(V, row * (DV * 2) + c * 16, sb + 2 * C::KBYTES + g * 1024);
+      }
+    }
+  };
+  auto issue = [&](int kt, auto st) __attribute__((always_inline)) {
+    issue_rt(kt, smem + decltype(st)::value * C::STAGE);
+  };
+
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  issue(0, std::integral_constant<int, 0>{});
+  if constexpr (PD > 1)
+    if (1 < ntiles) issue(1, std::integral_constant<int, 1>{});
+
+  floatx16 dq1T[C::CBK], dq2T[C::CBK];
+#pragma unroll
+  for (int cb = 0; cb < C::CBK; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dq1T[cb][r] = 0.0f;
+      dq2T[cb][r] = 0.0f;
+    }
+
+  const int sw_row = swz2(l32);
+  const int tq = lane & 3;
+  const int tk = (lane >> 2) & 3;
+  const int t_row = 4 * hi + tk;
+  const int t_chunk = 2 * ((lane >> 4) & 1) + (tq >> 1);
+  const int t_sw = (tk << 1) | hi;
+  const int t_byte = (tq & 1) * 8;
+
+  auto compute_block = [&](int kt, int kb, const char* sb) __attribute__((always_inline)) {
+    const int key0 = kt * BC + kb * 32;
+    const char* tk1 = sb;
+    const char* tk2 = sb + C::KBYTES;
+    const char* tv = sb + 2 * C::KBYTES;
+    floatx16 s1, s2, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s1[r] = 0.0f;
+      s2[r] = 0.0f;
+      dp[r] = 0.0f;
+    }
+    // S^T = K Q^T (rows: keys, lane column: query)
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const int off = (kb * 32 + l32) * (2 * D) + (((2 * ks + hi) ^ sw_row) << 4);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(tk1 + off), qf[0][ks], s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(tk2 + off), qf[1][ks], s2, 0, 0, 0);
+    }
+    // dP^T = V dOpre^T
+#pragma unroll
+    for (int ks = 0; ks < C::VSTEPS; ++ks) {
+      const bf16x8 av = *(const bf16x8*)(tv + (kb * 32 + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_row) << 4));
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[ks], dp, 0, 0, 0);
+    }
+    const bool need_mask = CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool masked = CAUSAL ? (key > query) : (key >= T);
+        if (masked) {
+          s1[r] = kNegInf;
+          s2[r] = kNegInf;
+        }
+      }
+    }
+    bf16x8 g1[2], g2[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], sc, -lse1));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(s2[r], sc, -lse2));
+      g1[r >> 3][r & 7] = (bf16)(p1 * (dp[r] - e1));
+      g2[r >> 3][r & 7] = (bf16)(p2 * fmaf(-lam, dp[r], -e2));
+    }
+    // dQm^T += Km^T dSm^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int cb = 0; cb < C::CBK; ++cb) {
+        const int boff = (kb * 32 + 16 * ks + t_row) * (2 * D) + (((4 * cb + t_chunk) ^ t_sw) << 4) + t_byte;
+        const bf16x4 lo1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk1 + boff));
+        const bf16x4 up1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk1 + boff + 8 * (2 * D)));
+        const bf16x4 lo2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk2 + boff));
+        const bf16x4 up2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk2 + boff + 8 * (2 * D)));
+        const bf16x8 a1 = {lo1[0], lo1[1], lo1[2], lo1[3], up1[0], up1[1], up1[2], up1[3]};
+        const bf16x8 a2 = {lo2[0], lo2[1], lo2[2], lo2[3], up2[0], up2[1], up2[2], up2[3]};
+        dq1T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, g1[ks], dq1T[cb], 0, 0, 0);
+        dq2T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, g2[ks], dq2T[cb], 0, 0, 0);
+      }
+  };
+
+  auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      const int key0 = kt * BC + kb * 32;
+      if (key0 >= T || (CAUSAL && key0 > q0 + 31)) break;
+      compute_block(kt, kb, sb);
+    }
+  };
+
+  if (PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
+  else wait_vm_barrier<0>();
+  auto step = [&](int kt, auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    if (kt + PD < ntiles) issue(kt + PD, std::integral_constant<int, (S + PD) % NSTAGE>{});
+    if (wave_active) compute_tile(kt, smem + S * C::STAGE);
+    if (kt + PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
+    else wait_vm_barrier<0>();
+  };
+  for (int kt = 0; kt < ntiles; kt += NSTAGE) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NSTAGE > 2)
+      if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2>{});
+  }
+
+  if (!wave_active || query >= T) return;
+  const float gs = a.grad_scale;
+  bf16* dq1 = (bf16*)a.dq1 + qk_off + (size_t)query * D;
+  bf16* dq2 = (bf16*)a.dq2 + qk_off + (size_t)query * D;
+#pragma unroll
+  for (int cb = 0; cb < C::CBK; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ch = cb * 32 + 8 * g + 4 * hi;
+      const bf16x4 x1 = {(bf16)(dq1T[cb][4 * g] * gs), (bf16)(dq1T[cb][4 * g + 1] * gs),
+                         (bf16)(dq1T[cb][4 * g + 2] * gs), (bf16)(dq1T[cb][4 * g + 3] * gs)};
+      const bf16x4 x2 = {(bf16)(dq2T[cb][4 * g] * gs), (bf16)(dq2T[cb][4 * g + 1] * gs),
+                         (bf16)(dq2T[cb][4 * g + 2] * gs), (bf16)(dq2T[cb][4 * g + 3] * gs)};
+      *(bf16x4*)(dq1 + ch) = x1;
+      *(bf16x4*)(dq2 + ch) = x2;
+    }
+}
+
+// ---- launchers --------------------------------------------------------------
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
+  const int gp = a.nchunk * a.B * a.H;
+  if (headnorm) bwd_prep_kernel<D, true><<<gp, 256, 0, stream>>>(a);
+  else bwd_prep_kernel<D, false><<<gp, 256, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int KNW = 4, QNW = 8;
+  constexpr int KST = 3;
+  constexpr int QST = 3;
+  const int nkt = (a.T + 32 * KNW - 1) / (32 * KNW);
+  bwd_kv_kernel<D, KNW, KST, CAUSAL><<<a.B * a.H * nkt, KNW * 64, 0, stream>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqt = (a.T + 32 * QNW - 1) / (32 * QNW);
+  bwd_q_kernel<D, QNW, QST, CAUSAL><<<a.B * a.H * nqt, QNW * 64, 0, stream>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_lambda_kernel<<<a.H, 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, bool headnorm, hipStream_t stream) {
+  if (D == 64) return causal ? launch_bwd_d<64, true>(a, headnorm, stream) : launch_bwd_d<64, false>(a, headnorm, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn

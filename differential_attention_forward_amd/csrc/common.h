@@ -75,4 +75,47 @@ __device__ inline float reparam_lambda(const float* __restrict__ lq1, const floa
 __device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i
+// reads base + off_i (base uniform, kept in SGPRs; off_i an unsigned 32-bit
+// byte offset) and its 16 bytes land at lds + 16 i.  Issued through asm so that
+// the compiler's wait-count bookkeeping does not make every later LDS read wait
+// for all tile loads in flight; their completion is awaited explicitly
+// (vmcnt) before the tile barrier.
+__device__ inline void dma16(const void* base, uint32_t off, const void* lds) {
+  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory", "m0");
+}
+
+// A pointer that is the same in every lane, moved to scalar registers (64-bit
+// address arithmetic runs on the VALU, which would keep it in VGPRs).
+template <typename Tp>
+__device__ inline const Tp* scalar_ptr(const Tp* p) {
+  // readfirstlane returns int: widen through uint32_t, not by sign extension
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const Tp*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then a workgroup barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+template <int N>
+__device__ inline void wait_vm_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ inline float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace diffattn

@@ -21,6 +21,12 @@ struct FwdArgs {
   float lam_init;
   float* lam_out;
   void* out;
+  // training forward (bf16 kernel only; null = inference): each map's
+  // normalised output t1 = A1 V, t2 = A2 V as fp32 [B,H,T,2D], and the
+  // log2-domain log-sum-exp of each map's scaled scores, fp32 [B,H,2,T]
+  float* save_o1;
+  float* save_o2;
+  float* save_lse;
   int B, H, T;
   float score_scale;  // log2(e) / sqrt(D)
   float out_scale;    // 1 - lambda_init (head norm only)
@@ -42,6 +48,40 @@ struct DecodeArgs {
   float eps;
 };
 
+// Backward pass (bf16).  Inputs as in the forward; o1, o2, lse are what the
+// training forward saved.  Workspace: dopre [B,H,T,2D] bf16, stats
+// [B,H,4,Tp] fp32 (lse1, lse2, D1, D2; Tp = T rounded up to 64) and
+// dlam_part [B,H,nchunk] fp32 (nchunk = Tp / 64).
+struct BwdArgs {
+  const void* q1;
+  const void* k1;
+  const void* q2;
+  const void* k2;
+  const void* v;
+  const void* dout;    // [B,H,T,2D]
+  const float* o1;     // [B,H,T,2D]
+  const float* o2;
+  const float* lse;    // [B,H,2,T]
+  const float* lam;    // [H]
+  void* dopre;
+  float* stats;
+  float* dlam_part;
+  void* dq1;
+  void* dk1;
+  void* dq2;
+  void* dk2;
+  void* dv;
+  float* dlam;         // [H]
+  const float* lvec[4];  // optional [H, Dl] re-parameterisation vectors
+  float* dlvec[4];       // their gradients (set iff lvec[0] is)
+  int Dl;
+  int B, H, T, Tp, nchunk;
+  float score_scale;   // log2(e) / sqrt(D)
+  float grad_scale;    // 1 / sqrt(D)
+  float out_scale;     // 1 - lambda_init (head norm only)
+  float eps;
+};
+
 // dtype: 0 = fp32, 1 = bf16 (same codes as the public enum)
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool headnorm,
                       hipStream_t stream);
@@ -49,6 +89,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, bool headnorm,
                          hipStream_t stream);
 // standard softmax attention, bf16, Q/K/V/O [B,H,T,D] (D = 64 or 128)
 hipError_t launch_attention(const FwdArgs& a, int D, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, bool headnorm, hipStream_t stream);
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2,
                          const float* lk2, int H, int Dl, float lambda_init, float* out,
                          hipStream_t stream);

@@ -458,53 +458,10 @@ struct CfgB {
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
-
 // 16-byte column swizzles (see above)
 template <int D>
 __device__ inline int swz_k(int row) { return D == 32 ? ((row >> 1) & 3) : (row & 7); }
 __device__ inline int swz_v(int row) { return (row & 3) << 1; }
-
-// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i
-// reads base + off_i (base uniform, kept in SGPRs; off_i an unsigned 32-bit
-// byte offset) and its 16 bytes land at lds + 16 i.  Issued through asm so that
-// the compiler's wait-count bookkeeping does not make every later LDS read wait
-// for all tile loads in flight; their completion is awaited explicitly
-// (vmcnt) before the tile barrier.
-__device__ inline void dma16(const void* base, uint32_t off, const void* lds) {
-  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory", "m0");
-}
-
-// A pointer that is the same in every lane, moved to scalar registers (64-bit
-// address arithmetic runs on the VALU, which would keep it in VGPRs).
-template <typename Tp>
-__device__ inline const Tp* scalar_ptr(const Tp* p) {
-  // readfirstlane returns int: widen through uint32_t, not by sign extension
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-  return (const Tp*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0), then a workgroup barrier; the empty asm
-// statements keep the compiler from moving memory accesses across it.
-template <int N>
-__device__ inline void wait_vm_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ inline float swap_halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float swap_halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM, int MAPS = 2>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
@@ -788,13 +745,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (kt + 3 < ntiles) step(kt + 3, std::integral_constant<int, 3>{});
   }
 
+  // training forward: map br's normalised output and its log-sum-exp
+  auto save_map = [&](int br, int query, float m, float l, float inv, const floatx16 (&ac)[C::CB])
+      __attribute__((always_inline)) {
+    if (a.save_o1 == nullptr || query >= T) return;
+    float* dst = (br ? a.save_o2 : a.save_o1) + v_off + (size_t)query * C::DV;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 t = {ac[cb][4 * g] * inv, ac[cb][4 * g + 1] * inv, ac[cb][4 * g + 2] * inv,
+                           ac[cb][4 * g + 3] * inv};
+        *(floatx4*)(dst + cb * 32 + 8 * g + 4 * hi) = t;
+      }
+    if (hi == 0) a.save_lse[((size_t)bh * 2 + br) * T + query] = m + __log2f(l);
+  };
+
   // ---- split mode: map-2 waves hand t2 = acc2 / l2 to their map-1 partners ----
   float* const xch = (float*)smem;
   if constexpr (SPLIT) {
     if (wbr == 1 && wave_active) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        const float inv2 = 1.0f / swap_halves_sum(lsum[0][qb]);
+        const float l2 = swap_halves_sum(lsum[0][qb]);
+        const float inv2 = 1.0f / l2;
+        save_map(1, q0 + qb * 32 + l32, mu[0][qb], l2, inv2, acc[0][qb]);
         float* row = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
@@ -816,9 +791,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int query = q0 + qb * 32 + l32;
-    const float inv1 = 1.0f / swap_halves_sum(lsum[0][qb]);
+    const float l1 = swap_halves_sum(lsum[0][qb]);
+    const float inv1 = 1.0f / l1;
     float inv2 = 0.0f;
-    if constexpr (!SPLIT && MAPS == 2) inv2 = 1.0f / swap_halves_sum(lsum[1][qb]);
+    if constexpr (MAPS == 2) save_map(0, query, mu[0][qb], l1, inv1, acc[0][qb]);
+    if constexpr (!SPLIT && MAPS == 2) {
+      const float l2 = swap_halves_sum(lsum[1][qb]);
+      inv2 = 1.0f / l2;
+      save_map(1, query, mu[1][qb], l2, inv2, acc[1][qb]);
+    }
     const float* xrow = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
     float o[C::CB][16];
 #pragma unroll

@@ -1,7 +1,7 @@
 /*
  * diffattn.h -- C ABI of the MI355X (gfx950) differential-attention library.
  *
- * The library computes multi-head differential attention, forward only:
+ * The library computes multi-head differential attention and its gradients:
  *
  *   O = (softmax(Q1 K1^T / sqrt(D) + M) - lambda * softmax(Q2 K2^T / sqrt(D) + M)) V
  *
@@ -45,7 +45,8 @@ typedef enum {
                                    overlapping output, bad split count */
   DIFFATTN_ERR_UNSUPPORTED = 2, /* unknown dtype, D not in {32,64,128}, misaligned pointer,
                                    sizes beyond the 32-bit grid limits */
-  DIFFATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  DIFFATTN_ERR_WORKSPACE = 3,   /* decode/backward workspace or training saved-state
+                                   buffer missing or too small */
   DIFFATTN_ERR_HIP = 4          /* the kernel launch itself failed */
 } diffattn_status;
 
@@ -181,6 +182,79 @@ diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const voi
                                 const float* lambda, int headnorm, float lambda_init, float eps,
                                 int num_splits, void* workspace, size_t workspace_bytes,
                                 void* out, hipStream_t stream);
+
+/*
+ * ---- Training: forward with saved state, and the backward pass ----
+ *
+ * The paperleet page "Differential Transformer Attention" asks for gradients
+ * through both Q/K branches, the value and the coefficient lambda, and
+ * through the four re-parameterisation vectors of lambda.  These entry points
+ * support bf16 tensors with D = 64.
+ *
+ * Bytes of the saved-state buffer diffattn_fwd_train fills and diffattn_bwd
+ * reads: 2 * B*H*T*2D*4 + B*H*2*T*4 (fp32 per-map outputs A1 V and A2 V, then
+ * each map's log2-domain log-sum-exp of its scaled scores per row, layout
+ * [B,H,2,T]).  Returns 0 for unsupported sizes.
+ */
+size_t diffattn_train_saved_bytes(int B, int H, int T, int D);
+
+/*
+ * diffattn_fwd (same arguments and output, bf16 only, D = 64) that also
+ * writes the saved state the backward pass needs into `saved` (at least
+ * diffattn_train_saved_bytes bytes, 16-byte aligned, disjoint from every
+ * input and from out).  The output is identical to diffattn_fwd's.
+ * Errors: as diffattn_fwd; ERR_UNSUPPORTED for fp32 or D other than 64;
+ * ERR_WORKSPACE when saved_bytes is too small.
+ */
+diffattn_status diffattn_fwd_train(int dtype, int B, int H, int T, int D, const void* q1,
+                                   const void* k1, const void* q2, const void* k2, const void* v,
+                                   const float* lambda, int causal, int headnorm, float lambda_init,
+                                   float eps, void* out, void* saved, size_t saved_bytes,
+                                   hipStream_t stream);
+
+/*
+ * Bytes of device workspace diffattn_bwd needs (16-byte aligned): the
+ * gradient reaching the pre-norm output (bf16 [B,H,T,2D]), per-row
+ * statistics (fp32 [B,H,4,Tp], Tp = T rounded up to 64) and per-chunk
+ * partial sums of dlambda (fp32 [B,H,Tp/64]).  Returns 0 for unsupported
+ * sizes.
+ */
+size_t diffattn_bwd_workspace_bytes(int B, int H, int T, int D);
+
+/*
+ * Backward pass of diffattn_fwd_train: given dL/dout, the gradients
+ *   dq1, dk1, dq2, dk2  [B, H, T, D]   bf16
+ *   dv                  [B, H, T, 2D]  bf16
+ *   dlambda             [H] fp32: dL/dlambda_h summed over batch and tokens
+ * and, when the four re-parameterisation vectors lq1, lk1, lq2, lk2 ([H, Dl]
+ * fp32, those lambda was formed from with diffattn_lambda) are given, their
+ * gradients dlq1, dlk1, dlq2, dlk2 ([H, Dl] fp32), by the chain rule through
+ * lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init (aifetchly page,
+ * section 3).  Pass all eight vector pointers or none.
+ *
+ *   q1 .. v, lambda, causal, headnorm, lambda_init, eps
+ *                 exactly as given to diffattn_fwd_train
+ *   dout          [B, H, T, 2D] bf16, gradient of the forward's output
+ *   saved         the buffer diffattn_fwd_train filled (read only)
+ *   workspace     device scratch of at least diffattn_bwd_workspace_bytes;
+ *                 contents on entry ignored; concurrent calls need separate
+ *                 workspaces
+ * The maps are recomputed from the saved log-sum-exp, never stored.  dlambda
+ * and the vector gradients are summed in a fixed order (deterministic).
+ * Errors: ERR_INVALID (null tensor pointer, B/H/T < 1, headnorm with eps <= 0,
+ * only some of the vector pointers, Dl < 1 with vectors, any output
+ * overlapping an input, another output or the workspace), ERR_UNSUPPORTED
+ * (dtype other than bf16, D other than 64, misalignment, sizes),
+ * ERR_WORKSPACE (saved_bytes or workspace too small), ERR_HIP.
+ */
+diffattn_status diffattn_bwd(int dtype, int B, int H, int T, int D, const void* q1, const void* k1,
+                             const void* q2, const void* k2, const void* v, const float* lambda,
+                             const void* dout, const void* saved, size_t saved_bytes, int causal,
+                             int headnorm, float lambda_init, float eps, void* dq1, void* dk1,
+                             void* dq2, void* dk2, void* dv, float* dlambda, const float* lq1,
+                             const float* lk1, const float* lq2, const float* lk2, int Dl,
+                             float* dlq1, float* dlk1, float* dlq2, float* dlk2, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

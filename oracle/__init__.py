@@ -8,6 +8,7 @@ from .diffattn_oracle import (  # noqa: F401
     attention,
     diff_attention,
     diff_attention_backward,
+    diff_attention_backward_dq_rows,
     diff_attention_decode,
     diff_attention_rows,
     head_rmsnorm,

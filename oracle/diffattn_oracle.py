@@ -75,6 +75,7 @@ __all__ = [
     "diff_attention_decode",
     "attention",
     "diff_attention_backward",
+    "diff_attention_backward_dq_rows",
     "reparam_lambda_backward",
 ]
 
@@ -327,6 +328,32 @@ def diff_attention_backward(q1, k1, q2, k2, v, lam, dout, causal: bool = True, h
             dk2[bi, hi] = c * (ds2.T @ q2[bi, hi])
             dlam[hi] -= np.sum(dopre * o2)
     return dq1, dk1, dq2, dk2, dv, dlam
+
+
+def diff_attention_backward_dq_rows(q1, k1, q2, k2, v, lam, dout, rows, causal: bool = True,
+                                    headnorm: bool = False, lambda_init: float = 0.8,
+                                    eps: float = 1e-5):
+    """dQ1, dQ2 rows of one (b, h) slice for the selected query rows.
+
+    The same chain rule as diff_attention_backward, restricted to what a query
+    row needs (its two score rows, its output row, its dOut row), so that
+    long sequences can be checked row by row.  q*, k* [T, D], v [T, 2D],
+    dout [T, 2D], lam a float; returns two [len(rows), D] arrays.
+    """
+    q1, k1, q2, k2, v, dout = (_f64(t) for t in (q1, k1, q2, k2, v, dout))
+    rows = np.asarray(rows)
+    c = 1.0 / math.sqrt(q1.shape[-1])
+    lm = float(lam)
+    a1 = _softmax_rows(_scores(q1, k1, rows, causal))
+    a2 = _softmax_rows(_scores(q2, k2, rows, causal))
+    o2 = a2 @ v
+    opre = a1 @ v - lm * o2
+    dy = dout[rows]
+    dopre = _head_rmsnorm_backward(opre, dy, lambda_init, eps) if headnorm else dy
+    dp = dopre @ v.T
+    ds1 = _softmax_backward_rows(a1, dp)
+    ds2 = _softmax_backward_rows(a2, -lm * dp)
+    return c * (ds1 @ k1), c * (ds2 @ k2)
 
 
 def reparam_lambda_backward(lq1, lk1, lq2, lk2, dlam):

@@ -37,7 +37,8 @@ What pins what:
                    (b) central finite differences of the pure-Python scalar
                    forward on T <= 5, (c) the identity sum_j dK_j = 0 per map
                    (softmax is unchanged by a per-row score shift), and
-                   (d) lambda = 0 leaves the second branch with no gradient
+                   (d) lambda = 0 leaves the second branch with no gradient;
+                   the row-wise dQ function equals the full backward's rows
   lambda grads     the four lambda-vector gradients against autograd and
                    central finite differences of the closed form
 """
@@ -251,6 +252,14 @@ def check_backward_identities():
         assert np.max(np.abs(dk.sum(axis=2))) < 1e-12
     assert np.max(np.abs(g[2][:, 0])) == 0.0 and np.max(np.abs(g[3][:, 0])) == 0.0
     assert np.max(np.abs(g[0][:, 0])) > 1e-3
+    for causal, headnorm in ((True, False), (False, True)):
+        g = oracle.diff_attention_backward(q1, k1, q2, k2, v, np.array([0.3, 0.5, 1.1]), dy, causal,
+                                           headnorm, 0.7, 1e-5)
+        rows = np.array([0, 5, 12])
+        r1, r2 = oracle.diff_attention_backward_dq_rows(q1[1, 2], k1[1, 2], q2[1, 2], k2[1, 2], v[1, 2],
+                                                        1.1, dy[1, 2], rows, causal, headnorm, 0.7, 1e-5)
+        assert np.max(np.abs(r1 - g[0][1, 2, rows])) < 1e-13
+        assert np.max(np.abs(r2 - g[2][1, 2, rows])) < 1e-13
 
 
 def check_lambda_backward():

@@ -24,8 +24,9 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 13, names
     assert "diffattn_fwd_reparam" in names and "diffattn_attention_fwd" in names
+    assert "diffattn_fwd_train" in names and "diffattn_bwd" in names
     for n in names:
         assert hasattr(L, n), n
 
@@ -177,3 +178,79 @@ def test_binding_requires_device_tensors():
     x = torch.zeros(1, 1, 4, 32)
     with pytest.raises(TypeError):
         da.diffattn_fwd(x, x, x, x, torch.zeros(1, 1, 4, 64), 0.5)
+
+
+def test_training_sizes(L):
+    b, h, t, d = 2, 3, 100, 64
+    assert da.diffattn_train_saved_bytes(b, h, t, d) == 2 * b * h * t * 2 * d * 4 + b * h * 2 * t * 4
+    tp = 128
+    ws = (b * h * t * 2 * d * 2 + 255) // 256 * 256 + (b * h * 4 * tp * 4 + 255) // 256 * 256 + b * h * 2 * 4
+    assert da.diffattn_bwd_workspace_bytes(b, h, t, d) == ws
+    for args in ((0, 1, 8, 64), (1, 1, 0, 64), (1, 1, 8, 32), (1, 1, 8, 128)):
+        assert da.diffattn_train_saved_bytes(*args) == 0
+        assert da.diffattn_bwd_workspace_bytes(*args) == 0
+
+
+def fwdt(L, dtype=BF16, B=1, H=2, T=8, D=64, ptrs=None, saved_bytes=1 << 20):
+    p = ptrs or [P(i) for i in range(8)]
+    return L.diffattn_fwd_train(dtype, B, H, T, D, p[0], p[1], p[2], p[3], p[4], p[5], 1, 0,
+                                ctypes.c_float(0.8), ctypes.c_float(1e-5), p[6], p[7],
+                                saved_bytes, None)
+
+
+def test_fwd_train_validation(L):
+    assert fwdt(L, ptrs=[P(i) for i in range(7)] + [None]) == INVALID
+    assert fwdt(L, ptrs=[P(0), None] + [P(i) for i in range(2, 8)]) == INVALID
+    assert fwdt(L, T=0) == INVALID
+    assert fwdt(L, dtype=F32) == UNSUPPORTED
+    for d in (32, 128):
+        assert fwdt(L, D=d) == UNSUPPORTED
+    assert fwdt(L, saved_bytes=da.diffattn_train_saved_bytes(1, 2, 8, 64) - 1) == WORKSPACE
+    bad = [P(i) for i in range(8)]
+    bad[7] = P(7, 8)
+    assert fwdt(L, ptrs=bad) == UNSUPPORTED
+    alias = [P(i) for i in range(8)]
+    alias[7] = P(6, 256)       # saved inside out
+    assert fwdt(L, ptrs=alias) == INVALID
+    alias[7] = P(4)            # saved over v
+    assert fwdt(L, ptrs=alias) == INVALID
+    assert fwdt(L) in (OK, 4)
+
+
+def bwd(L, dtype=BF16, B=1, H=2, T=8, D=64, ins=None, outs=None, vecs=None, dvecs=None, Dl=16,
+        saved_bytes=1 << 20, ws=None, wsb=1 << 20, headnorm=0, eps=1e-5):
+    i = ins or [P(k) for k in range(8)]          # q1 k1 q2 k2 v lambda dout saved
+    o = outs or [P(10 + k) for k in range(6)]    # dq1 dk1 dq2 dk2 dv dlambda
+    vv = vecs if vecs is not None else [None] * 4
+    dv = dvecs if dvecs is not None else [None] * 4
+    return L.diffattn_bwd(dtype, B, H, T, D, i[0], i[1], i[2], i[3], i[4], i[5], i[6], i[7],
+                          saved_bytes, 1, headnorm, ctypes.c_float(0.8), ctypes.c_float(eps),
+                          o[0], o[1], o[2], o[3], o[4], o[5], vv[0], vv[1], vv[2], vv[3], Dl,
+                          dv[0], dv[1], dv[2], dv[3], ws if ws is not None else P(30), wsb, None)
+
+
+def test_bwd_validation(L):
+    vecs = [P(20 + k) for k in range(4)]
+    dvecs = [P(24 + k) for k in range(4)]
+    assert bwd(L, ins=[P(0), None] + [P(k) for k in range(2, 8)]) == INVALID
+    assert bwd(L, ins=[P(k) for k in range(7)] + [None]) == INVALID
+    assert bwd(L, outs=[P(10 + k) for k in range(5)] + [None]) == INVALID
+    assert bwd(L, T=0) == INVALID
+    assert bwd(L, headnorm=1, eps=0.0) == INVALID
+    assert bwd(L, vecs=vecs, dvecs=[P(24), P(25), None, P(27)]) == INVALID   # some, not all
+    assert bwd(L, vecs=vecs, dvecs=dvecs, Dl=0) == INVALID
+    assert bwd(L, dtype=F32) == UNSUPPORTED
+    assert bwd(L, D=128) == UNSUPPORTED
+    assert bwd(L, ins=[P(0), P(1, 8)] + [P(k) for k in range(2, 8)]) == UNSUPPORTED
+    assert bwd(L, vecs=[P(20), P(21, 2), P(22), P(23)], dvecs=dvecs) == UNSUPPORTED
+    assert bwd(L, saved_bytes=da.diffattn_train_saved_bytes(1, 2, 8, 64) - 1) == WORKSPACE
+    assert bwd(L, wsb=da.diffattn_bwd_workspace_bytes(1, 2, 8, 64) - 1) == WORKSPACE
+    assert bwd(L, ws=ctypes.c_void_p(0)) == WORKSPACE
+    # outputs overlapping inputs, each other, or the workspace
+    assert bwd(L, outs=[P(10), P(11), P(12), P(13), P(4, 256), P(15)]) == INVALID   # dv over v
+    assert bwd(L, outs=[P(10), P(10, 512), P(12), P(13), P(14), P(15)]) == INVALID  # dk1 over dq1
+    assert bwd(L, outs=[P(10), P(11), P(12), P(13), P(14), P(7, 16)]) == INVALID    # dlambda in saved
+    assert bwd(L, ws=P(6)) == INVALID                                                # workspace over dout
+    assert bwd(L, vecs=vecs, dvecs=[P(24), P(25), P(26), P(20)]) == INVALID          # dlk2 over lq1
+    assert bwd(L, vecs=vecs, dvecs=dvecs) in (OK, 4)
+    assert bwd(L) in (OK, 4)

@@ -1,0 +1,178 @@
+"""GPU parity of the training path: the forward that saves state, and the
+backward pass, through the C ABI, against the float64 oracle.
+
+Inputs are bf16 (the training dtype); both sides see the same rounded values.
+Tolerance for a gradient tensor G: max |G_gpu - G_ref| <= 2e-2 * max |G_ref|
++ 1e-4.  The GPU rounds dOpre, the probabilities and dS to bf16 before their
+products (relative error 2^-9 each) and rounds G itself to bf16 (2^-9); the
+relative term leaves a margin of about ten such roundings at the tensor's
+scale.  The absolute term covers gradients that are exactly zero (one visible
+key: a constant softmax), where what remains is the fp32 rounding of
+dP - D (|dP| ~ sqrt(2D) ~ 11, times 2^-24, times the sum over D of |K| /
+sqrt(D)).  dlambda (an fp32 sum over all rows) gets the relative bound
+against max(|dlambda_ref|, 1).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import differential_attention_forward_amd as da
+import oracle
+from workloads import grad_output, make_workload, prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+REL = 2e-2
+ABS = 1e-4
+NAMES = ("dq1", "dk1", "dq2", "dk2", "dv", "dlambda")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    da.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_train(x, lam, dout, causal, headnorm, lambda_init=0.8, eps=1e-5, lvecs=None):
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    lam_d = lam.to(DEV)
+    out, saved = da.diffattn_fwd_train(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam_d,
+                                       causal=causal, headnorm=headnorm, lambda_init=lambda_init,
+                                       eps=eps)
+    g = da.diffattn_bwd(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam_d, dout.to(DEV), saved,
+                        causal=causal, headnorm=headnorm, lambda_init=lambda_init, eps=eps,
+                        lvecs=None if lvecs is None else [t.to(DEV) for t in lvecs])
+    torch.cuda.synchronize()
+    return out, saved, g
+
+
+def check_grads(got, ref, tag):
+    errs = {}
+    for name, g, r in zip(NAMES, got, ref):
+        scale = max(float(np.max(np.abs(r))), 1.0 if name == "dlambda" else 0.0)
+        err = float(np.max(np.abs(_np(g) - r)))
+        errs[name] = (err, scale)
+        assert np.isfinite(_np(g)).all(), (tag, name)
+        assert err <= REL * scale + ABS, (tag, name, err, scale)
+    say(tag, " ".join(f"{n}={e / max(s, 1e-30):.2e}" for n, (e, s) in errs.items()))
+
+
+SWEEP_T = [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 257]
+
+
+@pytest.mark.parametrize("headnorm", [False, True])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_sweep(causal, headnorm):
+    lam = torch.tensor([0.35, 1.3], dtype=torch.float32)
+    for i, T in enumerate(SWEEP_T):
+        say(f"bwd T={T} causal={causal} headnorm={headnorm}")
+        x = prefill_inputs(1, 2, T, 64, "bf16", seed=3000 + i)
+        dout = grad_output((1, 2, T, 128), seed=3100 + i)
+        out, _, got = run_train(x, lam, dout, causal, headnorm, lambda_init=0.6)
+        ref = oracle.diff_attention_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, dout,
+                                             causal, headnorm, 0.6, 1e-5)
+        check_grads(got, ref, f"  T={T}")
+
+
+def test_fwd_train_output_and_saved_state():
+    """The training forward's output is the inference forward's, bit for bit;
+    the saved per-map outputs and log-sum-exp match the oracle's maps."""
+    B, H, T, D = 2, 2, 300, 64
+    x = prefill_inputs(B, H, T, D, "bf16", seed=3200)
+    lam = torch.tensor([0.5, 0.9], dtype=torch.float32)
+    d = {k: v.to(DEV) for k, v in x.items()}
+    for causal, headnorm in ((True, False), (False, True)):
+        say(f"fwd_train causal={causal} headnorm={headnorm}")
+        ref_out = da.diffattn_fwd(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam.to(DEV),
+                                  causal=causal, headnorm=headnorm)
+        out, saved = da.diffattn_fwd_train(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam.to(DEV),
+                                           causal=causal, headnorm=headnorm)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
+        n = B * H * T * 2 * D
+        sv = saved.view(torch.float32)
+        o1 = sv[:n].view(B, H, T, 2 * D)
+        o2 = sv[n:2 * n].view(B, H, T, 2 * D)
+        lse = sv[2 * n:2 * n + 2 * B * H * T].view(B, H, 2, T)
+        a1, a2 = oracle.score_maps(x["q1"], x["k1"], x["q2"], x["k2"], causal)
+        v64 = x["v"].double().numpy()
+        assert np.max(np.abs(_np(o1) - a1 @ v64)) <= 2e-2
+        assert np.max(np.abs(_np(o2) - a2 @ v64)) <= 2e-2
+        # log2-domain log-sum-exp of the scaled scores, rebuilt from the
+        # maps: A = 2^(s log2(e)/sqrt(D) - lse) at any allowed entry, e.g.
+        # the diagonal (allowed under both masks)
+        s1 = np.einsum("bhtd,bhtd->bht", x["q1"].double().numpy(), x["k1"].double().numpy()) / 8.0
+        s2 = np.einsum("bhtd,bhtd->bht", x["q2"].double().numpy(), x["k2"].double().numpy()) / 8.0
+        diag1 = np.diagonal(a1, axis1=2, axis2=3)
+        diag2 = np.diagonal(a2, axis1=2, axis2=3)
+        ref1 = (s1 - np.log(diag1)) / np.log(2.0)
+        ref2 = (s2 - np.log(diag2)) / np.log(2.0)
+        # the forward sums bf16-rounded probabilities (relative error <= 2^-9
+        # each), so log2 of the sum is off by at most 2^-9 / ln 2 = 2.8e-3
+        assert np.max(np.abs(_np(lse[:, :, 0]) - ref1)) <= 3e-3
+        assert np.max(np.abs(_np(lse[:, :, 1]) - ref2)) <= 3e-3
+
+
+def test_bwd_lambda_vectors():
+    """With the re-parameterisation vectors, their gradients follow from
+    dlambda by the chain rule (oracle.reparam_lambda_backward)."""
+    H, Dl = 3, 64
+    x = prefill_inputs(1, H, 150, 64, "bf16", seed=3300, lambda_dl=Dl)
+    vecs = [x.pop(n) for n in ("lq1", "lk1", "lq2", "lk2")]
+    lam = torch.from_numpy(oracle.reparam_lambda(*vecs, 0.3)).float()
+    dout = grad_output((1, H, 150, 128), seed=3301)
+    _, _, got = run_train(x, lam, dout, True, True, lambda_init=0.3, lvecs=vecs)
+    ref = oracle.diff_attention_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam.numpy(),
+                                         dout, True, True, 0.3, 1e-5)
+    check_grads(got[:6], ref, "  vectors")
+    # chain rule applied to the GPU's own dlambda: isolates the vector step
+    ref_v = oracle.reparam_lambda_backward(*vecs, _np(got[5]))
+    for g, r in zip(got[6], ref_v):
+        assert np.max(np.abs(_np(g) - r)) <= 1e-5 * max(1.0, float(np.max(np.abs(r))))
+
+
+def test_bwd_repeatable_bitwise():
+    x = prefill_inputs(1, 2, 333, 64, "bf16", seed=3400)
+    lam = torch.tensor([0.8, 0.2], dtype=torch.float32)
+    dout = grad_output((1, 2, 333, 128), seed=3401)
+    _, _, g1 = run_train(x, lam, dout, True, False)
+    _, _, g2 = run_train(x, lam, dout, True, False)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_key_gradient_identity_long():
+    """At a size the oracle cannot materialise: sum over keys of dK is zero per
+    map (softmax is unchanged by a per-row score shift), up to the bf16
+    rounding of dS and of dK; dQ on sampled rows against the oracle."""
+    B, H, T, D = 1, 2, 8192, 64
+    x = prefill_inputs(B, H, T, D, "bf16", seed=3500)
+    lam = torch.tensor([0.8, 0.5], dtype=torch.float32)
+    dout = grad_output((B, H, T, 2 * D), seed=3501)
+    say(f"bwd long T={T}")
+    _, _, g = run_train(x, lam, dout, True, False)
+    for dk in (g[1], g[3]):
+        s = dk.float().sum(dim=2)
+        scale = dk.float().abs().sum(dim=2)
+        assert float((s.abs() / scale).max()) <= 1e-2
+    rng = np.random.default_rng(3502)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, T - 1], rng.integers(0, T, 11)]))
+    for h in range(H):
+        r1, r2 = oracle.diff_attention_backward_dq_rows(
+            x["q1"][0, h], x["k1"][0, h], x["q2"][0, h], x["k2"][0, h], x["v"][0, h], float(lam[h]),
+            dout[0, h], rows, True)
+        for got, ref in ((g[0][0, h, rows], r1), (g[2][0, h, rows], r2)):
+            err = float(np.max(np.abs(_np(got) - ref)))
+            assert err <= REL * float(np.max(np.abs(ref))), (h, err)

@@ -203,3 +203,11 @@ def make_workload(name: str, device="cpu"):
     return decode_inputs(w.B, w.H, w.T, w.D, w.dtype, w.seed, device,
                          lambda_dl=w.lambda_dl, lambda_zero=w.lambda_zero,
                          lam_fixed=w.lam_fixed, input_scale=w.input_scale)
+
+
+def grad_output(shape, seed=0, device="cpu", dtype="bf16"):
+    """dL/dOut for the backward pass: iid N(0,1) in the compute dtype (a
+    synthetic upstream gradient of the attention output's shape)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return _randn(g, tuple(shape), device).to(_tdtype(dtype))
