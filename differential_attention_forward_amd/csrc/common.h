@@ -109,6 +109,13 @@ __device__ inline void wait_vm_barrier() {
   asm volatile("" ::: "memory");
 }
 
+__device__ inline floatx16 splat16(float x) {
+  floatx16 v;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = x;
+  return v;
+}
+
 __device__ inline float swap_halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -41,6 +41,7 @@ namespace diffattn {
 namespace {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 2^8
+constexpr float kRescaleSum = 256.0f;  // 2^kTau: a partial row sum above it may hold a p > 2^kTau
 
 // lambda of head h: read from the [H] array, or (fused path) formed here by
 // every wave from the four vectors, with the same bits as the lambda kernel;
@@ -453,15 +454,32 @@ struct CfgB {
   static constexpr int XBYTES = SPLIT ? NWQ * QPW * XP * 4 : 0;
   static constexpr int RBYTES = NSTAGE * STAGE;
   static constexpr int SMEM = RBYTES > XBYTES ? RBYTES : XBYTES;
+  // -mu as a register tuple held across blocks (16 VGPRs per map and query
+  // block), or rebuilt from mu before every block where registers are short
+  static constexpr bool NEGMU_REGS = NBR * NQB == 1 && D <= 64;
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "two to four stages");
   static_assert(MAPS == 2 || !SPLIT, "one map: nothing to split");
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
-// 16-byte column swizzles (see above)
+// 16-byte column swizzles.  gfx950's LDS has 64 banks of 4 bytes (256 bytes
+// per clock): a ds_read_b128 serves 16 lanes per cycle and a
+// ds_read_b64_tr_b16 32 lanes, so those lanes must cover 256 distinct bytes
+// modulo 256.
+//  K (row pitch 2D bytes): lanes 0..15 read rows r..r+15 at one logical
+//  chunk; the swizzle makes (row mod (256 / pitch), physical chunk) distinct
+//  over those 16 rows.
+//  V (row pitch 2 DV bytes): the 32 lanes of a transposing read cover four
+//  rows (keys) and one 64-byte group of four chunks per row; the swizzle
+//  moves each of the four rows to its own 64-byte quarter of the banks.
 template <int D>
-__device__ inline int swz_k(int row) { return D == 32 ? ((row >> 1) & 3) : (row & 7); }
-__device__ inline int swz_v(int row) { return (row & 3) << 1; }
+__device__ inline int swz_k(int row) {
+  return D == 32 ? ((row >> 2) & 3) : D == 64 ? ((row >> 1) & 7) : (row & 15);
+}
+template <int DV>
+__device__ inline int swz_v(int row) {
+  return DV >= 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
 
 template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM, int MAPS = 2>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
@@ -478,9 +496,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int T = a.T;
 
   const int nqt = (T + C::BR - 1) / C::BR;
+  // the division by nqt runs on the VALU: say that the results are uniform so
+  // that every loop bound and branch derived from them stays scalar
   const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
-  const int bh = w / nqt;
-  const int qi = w % nqt;
+  const int bh = __builtin_amdgcn_readfirstlane(w / nqt);
+  const int qi = __builtin_amdgcn_readfirstlane(w % nqt);
   const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
   const int h = bh % a.H;
 
@@ -510,10 +530,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   // ---- asynchronous tile loads ------------------------------------------------
   // Segment g of a K tile (1 KiB) holds rows RK g .. RK g + RK - 1; lane l
-  // copies row RK g + l / CK, 16-byte column (l % CK) ^ swz_k(row).  The
-  // swizzle depends on g only through its parity (D = 128), so a lane's
-  // column offset takes one of two values; likewise for V.  Keys past the end
-  // load row T-1 (in bounds); their scores are masked.
+  // copies row RK g + l / CK, 16-byte column (l % CK) ^ swz_k(row); likewise
+  // for V.  Keys past the end load row T-1 (in bounds); their scores are
+  // masked.
   constexpr int CK = D / 8, RK = 64 / CK, CV = C::DV / 8, RV = 64 / CV;
   const int rl_k = lane / CK, rl_v = lane / CV;
   auto issue_rt = [&](int kt, char* sb) __attribute__((always_inline)) {
@@ -526,13 +545,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const int which = seg / C::KSEG;
         const int g = seg % C::KSEG;
         const int r = g * RK + rl_k;
-        const int c = (lane % CK) ^ swz_k<D>((g & 1) * RK + rl_k);
+        const int c = (lane % CK) ^ swz_k<D>(r);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
         dma16(which ? K2 : K1, row * (D * 2) + c * 16, sb + which * C::KBYTES + g * 1024);
       } else {
         const int g = seg - MAPS * C::KSEG;
         const int r = g * RV + rl_v;
-        const int c = (lane % CV) ^ swz_v((g & 1) * RV + rl_v);
+        const int c = (lane % CV) ^ swz_v<C::DV>(r);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
         dma16(V, row * (C::DV * 2) + c * 16, sb + MAPS * C::KBYTES + g * 1024);
       }
@@ -555,7 +574,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       for (int ks = 0; ks < C::KSTEPS; ++ks) {
         u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
         raw = ok ? raw : u32x4{0u, 0u, 0u, 0u};
-        qf[br][qb][ks] = __builtin_bit_cast(bf16x8, raw);
+        // scores come out of the MFMA already in base-2 units: q * log2(e) / sqrt(D)
+        // rounded once to bf16 (relative error <= 2^-9 per element)
+        const bf16x8 q = __builtin_bit_cast(bf16x8, raw);
+        bf16x8 qs;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[e] = (bf16)((float)q[e] * sc);
+        qf[br][qb][ks] = qs;
       }
     }
   }
@@ -570,15 +595,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   if constexpr (PD > 2)
     if (2 < ntiles) issue(2, std::integral_constant<int, 2>{});
 
+  // Softmax state per map and query row: the reference mu (base-2 units),
+  // the row sum lsum of 2^(s - mu) and the accumulators.  negmu holds -mu
+  // in all 16 elements and is the accumulator input of the first score MFMA,
+  // so the scores arrive with the reference already subtracted.  mu starts
+  // at 0 and is set to the exact row max by the wave's first key block.
   floatx16 acc[C::NBR][NQB][C::CB];
+  floatx16 negmu[C::NEGMU_REGS ? C::NBR : 1][C::NEGMU_REGS ? NQB : 1];
   float mu[C::NBR][NQB];
   float lsum[C::NBR][NQB];
 #pragma unroll
   for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      mu[br][qb] = kNegInf;
+      mu[br][qb] = 0.0f;
       lsum[br][qb] = 0.0f;
+      if constexpr (C::NEGMU_REGS) negmu[br][qb] = splat16(0.0f);
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -592,7 +624,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int vkq = (lane >> 2) & 3;
   const int v_row = 4 * hi + vkq;                 // + kb*32 + 16*ks + 8*t
   const int v_chunk = 2 * ((lane >> 4) & 1) + (vq >> 1);  // + 4*cb
-  const int v_sw = swz_v(vkq);
+  const int v_sw = swz_v<C::DV>(vkq);  // rows 16 ks + 4 hi + vkq (+ 8): same swizzle
   const int v_byte = (vq & 1) * 8;
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
@@ -603,15 +635,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     return key0 < T && (!CAUSAL || key0 <= q_last);
   };
 
-  // S^T of block kb for both maps (raw dot products, scale applied later)
+  // S^T of block kb for both maps: scaled scores minus the row reference
+  // (base-2 units), the reference entering as the first MFMA's accumulator
   auto qk = [&](int kb, const char* sb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
     const char* Kb[2] = {sb + (SPLIT && wbr ? C::KBYTES : 0), sb + C::KBYTES};
-#pragma unroll
-    for (int br = 0; br < C::NBR; ++br)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[br][qb][r] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
 #pragma unroll
@@ -619,80 +646,100 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const bf16x8 av = *(const bf16x8*)(Kb[br] + kb * 32 * (2 * D) + k_rd + (((2 * ks + hi) ^ swk) << 4));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
-          s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], s[br][qb], 0, 0, 0);
+          s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], ks > 0 ? s[br][qb]
+                                                               : C::NEGMU_REGS ? negmu[br][qb]
+                                                               : splat16(-mu[br][qb]), 0, 0, 0);
       }
     }
   };
 
-  // mask, running maxima (lazy rescale of acc and lsum), probabilities P^T as
-  // the bf16 B operand of the P.V product, row sums of those bf16 values
-  auto softmax = [&](int kt, int kb, floatx16 (&s)[C::NBR][NQB], bf16x8 (&pk)[C::NBR][NQB][2])
-      __attribute__((always_inline)) {
+  // -inf on the keys of block kb that a row may not see (causal: key > query;
+  // full attention: keys past the ragged end), both maps
+  auto mask_block = [&](int kt, int kb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
     const int key0 = kt * BC + kb * 32;
-    const bool need_mask = CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T);
-    if (need_mask) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int query = q0 + qb * 32 + l32;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int query = q0 + qb * 32 + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool masked = CAUSAL ? (key > query) : (key >= T);
-          if (masked) {
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool masked = CAUSAL ? (key > query) : (key >= T);
 #pragma unroll
-            for (int br = 0; br < C::NBR; ++br) s[br][qb][r] = kNegInf;
-          }
-        }
+        for (int br = 0; br < C::NBR; ++br) s[br][qb][r] = masked ? kNegInf : s[br][qb][r];
       }
     }
+  };
 
-    float mx[C::NBR][NQB];
-    bool need = false;
+  // probabilities 2^(s - mu) rounded to bf16 (the B operand of the P.V
+  // product) and each lane's sum of those rounded values over its 16 keys;
+  auto expo_one = [&](const floatx16& s, bf16x8 (&pk)[2], float& bsum) __attribute__((always_inline)) {
+    float b = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pa = __builtin_amdgcn_exp2f(s[8 * ks + 2 * j]);
+        const float pb = __builtin_amdgcn_exp2f(s[8 * ks + 2 * j + 1]);
+        const bf16x2 pw = {(bf16)pa, (bf16)pb};
+        b = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, b, false);
+        pk[ks][2 * j] = pw[0];
+        pk[ks][2 * j + 1] = pw[1];
+      }
+    }
+    bsum = b;
+  };
+  auto expo = [&](floatx16 (&s)[C::NBR][NQB], bf16x8 (&pk)[C::NBR][NQB][2], float (&bsum)[C::NBR][NQB])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float m = s[br][qb][0];
+      for (int qb = 0; qb < NQB; ++qb) expo_one(s[br][qb], pk[br][qb], bsum[br][qb]);
+  };
+
+  // Lazy rescale, after expo: the reference only moves when some probability
+  // of the block would exceed 2^kTau (then the lane's partial sum does), and
+  // on the wave's first block, which sets mu to the exact row max.  Otherwise
+  // mu stays at or below the running row max and within kTau of it from
+  // below, so every p <= 2^kTau and the final row sum is >= 1.  The rare path
+  // rescales acc and lsum and recomputes the block's probabilities.
+  auto settle = [&](bool first, floatx16 (&s)[C::NBR][NQB], bf16x8 (&pk)[C::NBR][NQB][2],
+                    float (&bsum)[C::NBR][NQB]) __attribute__((always_inline)) {
+    bool need = first;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][qb][r]);
-        m = swap_halves_max(m) * sc;
-        mx[br][qb] = m;
-        need |= m > mu[br][qb] + kTau;
-      }
+    for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) need |= bsum[br][qb] > kRescaleSum;
     if (__any(need)) {
 #pragma unroll
       for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          const float mn = fmaxf(mu[br][qb], mx[br][qb]);
-          const float alpha = (mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(mu[br][qb] - mn);
-          mu[br][qb] = mn;
+          float m = s[br][qb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][qb][r]);
+          m = swap_halves_max(m);  // block max of s - mu over the row's 32 keys
+          // first block: every row sees key 0, so m is finite; later blocks
+          // only ever raise the reference
+          const float delta = first ? (m == kNegInf ? 0.0f : m) : fmaxf(m, 0.0f);
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          mu[br][qb] += delta;
           lsum[br][qb] *= alpha;
 #pragma unroll
           for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[br][qb][cb][r] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if constexpr (C::NEGMU_REGS) negmu[br][qb][r] = -mu[br][qb];
+            s[br][qb][r] -= delta;
+          }
+          expo_one(s[br][qb], pk[br][qb], bsum[br][qb]);
         }
     }
-
 #pragma unroll
     for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float msub = mu[br][qb] == kNegInf ? 0.0f : mu[br][qb];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float pa = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j], sc, -msub));
-            const float pb = __builtin_amdgcn_exp2f(fmaf(s[br][qb][8 * ks + 2 * j + 1], sc, -msub));
-            const bf16x2 pw = {(bf16)pa, (bf16)pb};
-            lsum[br][qb] = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, lsum[br][qb], false);
-            pk[br][qb][ks][2 * j] = pw[0];
-            pk[br][qb][ks][2 * j + 1] = pw[1];
-          }
-        }
-      }
+      for (int qb = 0; qb < NQB; ++qb) lsum[br][qb] += bsum[br][qb];
   };
 
   // acc += P^T-weighted V rows of block kb; each V fragment serves both maps
@@ -718,13 +765,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   else wait_vm_barrier<0>();
   // ---- main loop: tile kt computed while tiles kt+1 .. kt+PD load ------------
   auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {
+    // whether any block of this tile crosses the causal diagonal (or the
+    // ragged end) for this wave's rows
+    const bool masked = CAUSAL ? (kt * BC + BC - 1 > q0) : (kt * BC + BC > T);
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
       if (!kb_live(kt, kb)) break;
       floatx16 s[C::NBR][NQB];
       bf16x8 pk[C::NBR][NQB][2];
+      float bs[C::NBR][NQB];
       qk(kb, sb, s);
-      softmax(kt, kb, s, pk);
+      if (masked) mask_block(kt, kb, s);
+      expo(s, pk, bs);
+      settle(kt == 0 && kb == 0, s, pk, bs);
       pv(kb, sb, pk);
     }
   };

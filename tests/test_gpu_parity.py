@@ -34,7 +34,7 @@ def say(*a):
 
 
 def to_dev(d):
-    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) and k != "needle_pos" else v)
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) and k not in ("needle_pos", "needle_query") else v)
             for k, v in d.items()}
 
 
@@ -323,6 +323,9 @@ def _check_prefill_workload(name, heads):
         if "needle_pos" in x:
             for j in x["needle_pos"][b, h].tolist():
                 extra += [j, j + 1, j + 100]
+            # the query rows the needles copy: their maps peak on the needle
+            for i in x["needle_query"][b, h].tolist():
+                extra += [i - 1, i, i + 1]
         rows = _sample_rows(w.T, rng, extra)
         sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
         ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"],

@@ -112,8 +112,9 @@ def prefill_inputs(B, H, T, D, dtype="bf16", seed=0, device="cpu", *, input_scal
 
     Returns a dict with q1, q2, k1, k2, v (compute dtype, on ``device``), and,
     when requested, lq1, lk1, lq2, lk2 ([H, Dl] float32) and/or lam ([H]
-    float32, lambda given directly), needle_pos ([H, needles] key positions,
-    CPU int64) and offset ([2D] float32).
+    float32, lambda given directly), needle_pos ([B, H, needles] key positions,
+    CPU int64), needle_query ([B, H, needles] the query row each needle key
+    copies, CPU int64) and offset ([2D] float32).
     """
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -143,6 +144,7 @@ def prefill_inputs(B, H, T, D, dtype="bf16", seed=0, device="cpu", *, input_scal
         # i >= j so the key is visible under the causal mask; K1[j] <- 4 Q1[i]
         # (a power-of-two multiple: exact in fp32 and after the bf16 cast).
         pos = torch.empty((B, H, needles), dtype=torch.int64)
+        qpos = torch.empty((B, H, needles), dtype=torch.int64)
         for b in range(B):
             for h in range(H):
                 js = torch.randperm(T, generator=gi)[:needles]
@@ -150,7 +152,9 @@ def prefill_inputs(B, H, T, D, dtype="bf16", seed=0, device="cpu", *, input_scal
                     i = int(torch.randint(j, T, (1,), generator=gi))
                     k1[b, h, j] = 4.0 * q1[b, h, i]
                     pos[b, h, n] = j
+                    qpos[b, h, n] = i
         out["needle_pos"] = pos
+        out["needle_query"] = qpos
     if value_offset:
         c = _randn(g, (2 * D,), device)
         v += c
