@@ -11,6 +11,8 @@ from .diffattn_oracle import (  # noqa: F401
     diff_attention_backward_dq_rows,
     diff_attention_decode,
     diff_attention_rows,
+    diff_attention_v2,
+    diff_attention_v2_decode,
     head_rmsnorm,
     lambda_init_schedule,
     reparam_lambda,

@@ -40,6 +40,11 @@ constant x (1 - lambda_init).
 Decode: one query row per (batch, head) against all L cached keys, no mask;
 the same steps as above with T_q = 1.
 
+DIFF V2 (the French lesson page, "V1 contre V2"): twice the query heads, the
+baseline's KV heads and head width, one K and one V per group of differential
+heads shared by both maps, no per-head norm.  Same steps per differential head
+with K1 = K2 = K_g and V = V_g, g = p // (Hq / Hkv).
+
 Readings where the pages are loose (all recorded in the design notes):
   - softmax scale is 1/sqrt(D) with D the width of Q1/K1 (not 2D);
   - lambda is not clamped and may be negative or exceed 1;
@@ -74,6 +79,8 @@ __all__ = [
     "head_rmsnorm",
     "diff_attention_decode",
     "attention",
+    "diff_attention_v2",
+    "diff_attention_v2_decode",
     "diff_attention_backward",
     "diff_attention_backward_dq_rows",
     "reparam_lambda_backward",
@@ -250,6 +257,64 @@ def diff_attention_decode(q1, k1, q2, k2, v, lam):
             out[bi, hi] = diff_attention_rows(
                 q1[bi, hi][None, :], k1s, q2[bi, hi][None, :], k2s, vs,
                 lam_h[hi], False, np.array([0]))[0]
+    return out
+
+
+def _group_of(hq: int, hkv: int) -> int:
+    if hkv < 1 or hq % hkv:
+        raise ValueError("query heads must be a whole multiple of KV heads")
+    return hq // hkv
+
+
+def diff_attention_v2(q1, q2, k, v, lam, causal: bool = True, row_block: int = 512):
+    """DIFF V2 forward with grouped KV heads, float64.
+
+    The French lesson page, "V1 contre V2": V2 doubles the query heads and
+    keeps the KV heads of the baseline, at the baseline head width; the two
+    queries of a differential head read the same K and V, so each map is
+    ordinary attention over that shared cache and the difference is taken
+    after attention; the per-head norm of V1 is gone.  The page's exercise
+    pairs this with grouped KV heads (8 KV heads for 32 query heads).
+    Reading taken: differential head p (of Hq) reads KV head p // (Hq / Hkv),
+    the grouping of grouped-query attention.
+
+    q1, q2: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; lam scalar or [Hq].
+    O_p = (softmax(Q1_p K_g^T/sqrt(D) + M) - lam_p softmax(Q2_p K_g^T/sqrt(D) + M)) V_g,
+    returned as [B, Hq, T, D].
+    """
+    q1, q2, k, v = (_f64(t) for t in (q1, q2, k, v))
+    b, hq, t, _ = q1.shape
+    grp = _group_of(hq, k.shape[1])
+    lam_h = _lam_per_head(lam, hq)
+    out = np.empty((b, hq, t, v.shape[-1]))
+    rows = np.arange(t)
+    for bi in range(b):
+        for p in range(hq):
+            g = p // grp
+            out[bi, p] = diff_attention_rows(q1[bi, p], k[bi, g], q2[bi, p], k[bi, g], v[bi, g],
+                                             lam_h[p], causal, rows, row_block)
+    return out
+
+
+def diff_attention_v2_decode(q1, q2, k, v, lam):
+    """DIFF V2 decode: one query pair per (b, differential head) against all L
+    cached rows of its KV head, no mask.
+
+    q1, q2: [B, Hq, D]; k, v: [B, Hkv, L, D]; lam scalar or [Hq].  Returns
+    [B, Hq, D].  The same steps as ``diff_attention_v2`` for one query row that
+    sees every key.
+    """
+    q1, q2 = _f64(q1), _f64(q2)
+    b, hq, _ = q1.shape
+    grp = _group_of(hq, k.shape[1])
+    lam_h = _lam_per_head(lam, hq)
+    out = np.empty((b, hq, v.shape[-1]))
+    for bi in range(b):
+        for p in range(hq):
+            g = p // grp
+            ks, vs = _f64(k[bi, g]), _f64(v[bi, g])
+            out[bi, p] = diff_attention_rows(q1[bi, p][None, :], ks, q2[bi, p][None, :], ks, vs,
+                                             lam_h[p], False, np.array([0]))[0]
     return out
 
 

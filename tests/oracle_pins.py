@@ -41,6 +41,9 @@ What pins what:
                    the row-wise dQ function equals the full backward's rows
   lambda grads     the four lambda-vector gradients against autograd and
                    central finite differences of the closed form
+  DIFF V2          grouped-query form (shared K/V per group, V as wide as Q):
+                   torch's scaled_dot_product_attention with enable_gqa, for
+                   every lambda and lambda = 0; V2 decode = last causal row
 """
 
 import json
@@ -284,9 +287,40 @@ def check_lambda_backward():
                 assert abs(fd - got[which][idx]) < 1e-8
 
 
+def check_v2_library():
+    """DIFF V2: each map is ordinary attention over the shared K/V of its group
+    (the French page, "V1 contre V2"), so O = SDPA(Q1, K, V) - lam SDPA(Q2, K, V)
+    with torch's grouped-query mapping (enable_gqa: query head p reads KV head
+    p // (Hq / Hkv)); lambda = 0 is ordinary grouped-query attention."""
+    for causal in (True, False):
+        for hq, hkv in ((8, 2), (6, 6), (4, 1)):
+            q1, q2 = _rand((2, hq, 21, 16), 401), _rand((2, hq, 21, 16), 402)
+            k, v = _rand((2, hkv, 21, 16), 403), _rand((2, hkv, 21, 16), 404)
+            lam = np.linspace(-0.4, 1.3, hq)
+            ref1 = F.scaled_dot_product_attention(q1, k, v, is_causal=causal, enable_gqa=True).numpy()
+            ref2 = F.scaled_dot_product_attention(q2, k, v, is_causal=causal, enable_gqa=True).numpy()
+            o = oracle.diff_attention_v2(q1, q2, k, v, lam, causal)
+            assert o.shape == (2, hq, 21, 16)
+            assert np.max(np.abs(o - (ref1 - lam[None, :, None, None] * ref2))) < 1e-12
+            o0 = oracle.diff_attention_v2(q1, q2, k, v, 0.0, causal)
+            assert np.max(np.abs(o0 - ref1)) < 1e-12
+
+
+def check_v2_decode():
+    """V2 decode = the last row of the causal V2 forward (that row sees every
+    key), per differential head of every group."""
+    q1, q2 = _rand((2, 8, 19, 8), 411), _rand((2, 8, 19, 8), 412)
+    k, v = _rand((2, 2, 19, 8), 413), _rand((2, 2, 19, 8), 414)
+    lam = np.linspace(0.1, 0.9, 8)
+    full = oracle.diff_attention_v2(q1, q2, k, v, lam, causal=True)
+    dec = oracle.diff_attention_v2_decode(q1[:, :, -1], q2[:, :, -1], k, v, lam)
+    assert np.max(np.abs(dec - full[:, :, -1])) < 1e-13
+
+
 ALL_CHECKS = [
     check_worked_example, check_library_attention, check_cancellation, check_row_sums,
     check_value_offset, check_first_row, check_lambda, check_lambda_init, check_head_norm,
     check_brute_force, check_decode, check_standard_attention, check_backward_autograd,
     check_backward_finite_diff, check_backward_identities, check_lambda_backward,
+    check_v2_library, check_v2_decode,
 ]

@@ -10,6 +10,7 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 import oracle.diffattn_oracle as od
 from tests import oracle_pins
@@ -17,6 +18,8 @@ from tests import oracle_pins
 _REAL_ATTENTION = od.attention  # the real functions, wrapped by mutants below
 _REAL_BACKWARD = od.diff_attention_backward
 _REAL_LAMBDA_BACKWARD = od.reparam_lambda_backward
+_REAL_V2 = od.diff_attention_v2
+_REAL_V2_DECODE = od.diff_attention_v2_decode
 
 
 
@@ -161,6 +164,24 @@ def _lambda_bwd_plus(lq1, lk1, lq2, lk2, dlam):
     return a, b, -c, -d
 
 
+def _v2_group_modulo(q1, q2, k, v, lam, causal=True, row_block=512):
+    # differential head p reads KV head p % Hkv instead of p // (Hq / Hkv)
+    hq, hkv = q1.shape[1], k.shape[1]
+    idx = [p % hkv for p in range(hq)]
+    kk = torch.as_tensor(np.asarray(od._f64(k))[:, idx])
+    vv = torch.as_tensor(np.asarray(od._f64(v))[:, idx])
+    return od.diff_attention(q1, kk, q2, kk, vv, lam, causal, row_block)
+
+
+def _v2_first_query_twice(q1, q2, k, v, lam, causal=True, row_block=512):
+    return _REAL_V2(q1, q1, k, v, lam, causal, row_block)
+
+
+def _v2_decode_wrong_group(q1, q2, k, v, lam):
+    return _REAL_V2_DECODE(q1, q2, torch.flip(torch.as_tensor(od._f64(k)), [1]),
+                           torch.flip(torch.as_tensor(od._f64(v)), [1]), lam)
+
+
 MUTANTS = {
     "scale_1_over_sqrt_2d": ("_scores", _make_scores(lambda d: 1 / math.sqrt(2 * d), lambda j, i: j > i)),
     "scale_missing": ("_scores", _make_scores(lambda d: 1.0, lambda j, i: j > i)),
@@ -192,6 +213,9 @@ MUTANTS = {
     "bwd_dv_first_map_only": ("diff_attention_backward", _bwd_dv_first_map_only),
     "lambda_bwd_own_vector": ("reparam_lambda_backward", _lambda_bwd_self),
     "lambda_bwd_second_sign": ("reparam_lambda_backward", _lambda_bwd_plus),
+    "v2_group_modulo": ("diff_attention_v2", _v2_group_modulo),
+    "v2_first_query_twice": ("diff_attention_v2", _v2_first_query_twice),
+    "v2_decode_wrong_group": ("diff_attention_v2_decode", _v2_decode_wrong_group),
 }
 
 
