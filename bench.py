@@ -15,9 +15,10 @@ SETTLE_S seconds, so that the GPU clock has ramped up before timing starts
 The printed JSON line reports the primary workload (default: the causal T=4096
 bf16 prefill, B2 H16 D64, head norm on) as TFLOP/s counted as
 8 * T_eff * T * D * B * H per forward (T_eff = (T+1)/2 causal, T full), and
-the other workloads (causal T=32768, full T=8192 D=128, decode L=65536) under
-"also", together with standard softmax attention of the same size as the two
-causal workloads (head width 2D) and the time ratio of the two.  "roofline" gives the dominant kernel's algorithmic rate (from HIP
+the other workloads (causal T=32768, full T=8192 D=128, decode L=65536, and
+the DIFF V2 prefill and decode with grouped KV heads) under "also", together
+with standard softmax attention of the same size as the two causal workloads
+(head width 2D) and the time ratio of the two.  "roofline" gives the dominant kernel's algorithmic rate (from HIP
 events around each launch on the launch stream) against the MI355X peak
 (bf16 dense MFMA 2.5 PFLOP/s, fp32 MFMA 157.3 TFLOP/s, HBM 8 TB/s).
 "cpu_baseline" times the float64 oracle on the host cores on a bounded sample
@@ -39,7 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DiffAttn fwd TFLOP/s (bf16 causal T=4k/32k) & % MFMA peak; decode HBM GB/s"
 PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
 PRIMARY = "prefill_t4k_causal"
-OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k"]
+OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k", "v2_prefill_t4k", "v2_decode_l64k"]
 CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
 KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip"}
 KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel"}
@@ -71,12 +72,20 @@ def measured_traffic(kind, workload):
 
 
 def prefill_flops(w):
+    """Per visible (query, key) pair and head: two D-wide score dot products
+    and one signed weighted sum over the value row (2D wide in the first
+    version, D wide in V2), 2 flops per multiply-add."""
     t_eff = (w.T + 1) / 2.0 if w.causal else float(w.T)
-    return 8.0 * t_eff * w.T * w.D * w.B * w.H
+    per_pair = 6.0 * w.D if w.kind == "v2_prefill" else 8.0 * w.D
+    return per_pair * t_eff * w.T * w.B * w.H
 
 
 def decode_bytes(w):
+    """Cache bytes one step must read: K1, K2 (D) and V (2D) per key and head;
+    V2: one K and one V (D each) per key and KV head."""
     es = 2 if w.dtype == "bf16" else 4
+    if w.kind == "v2_decode":
+        return float(w.B * w.Hkv * w.T * 2 * w.D * es)
     return float(w.B * w.H * w.T * 4 * w.D * es)
 
 
@@ -135,10 +144,24 @@ def bench_workload(torch, da, name, steps, warmup):
     log(f"[bench] {name}: generating inputs")
     x = make_workload(name, "cuda")
     torch.cuda.synchronize()
-    li = w.lambda_init if w.lambda_init is not None else da.diffattn_lambda_init(w.layer)
+    li = w.lambda_init if w.lambda_init is not None else (
+        da.diffattn_lambda_init(w.layer) if w.layer else 0.0)  # V2 has no lambda_init-scaled norm
     lam = x.get("lam")
     lam_buf = torch.empty(w.H, device="cuda", dtype=torch.float32)
-    if w.kind == "prefill":
+    if w.kind == "v2_prefill":
+        out = torch.empty_like(x["q1"])
+
+        def kernel():
+            da.diffattn_v2_fwd(x["q1"], x["q2"], x["k"], x["v"], lam, causal=w.causal, out=out)
+    elif w.kind == "v2_decode":
+        out = torch.empty((w.B, w.H, w.D), device="cuda", dtype=x["q1"].dtype)
+        ws = torch.empty(da.diffattn_v2_decode_workspace_bytes(w.B, w.H, w.Hkv, w.T, w.D, w.num_splits) // 4,
+                         device="cuda", dtype=torch.float32)
+
+        def kernel():
+            da.diffattn_v2_decode(x["q1"], x["q2"], x["k"], x["v"], lam, num_splits=w.num_splits,
+                                  workspace=ws, out=out)
+    elif w.kind == "prefill":
         out = torch.empty_like(x["v"])
 
         if lam is not None:
@@ -164,7 +187,7 @@ def bench_workload(torch, da, name, steps, warmup):
                                workspace=ws, out=out)
 
     def step():
-        if lam is None and w.kind != "prefill":
+        if lam is None and w.kind == "decode":
             da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], li, out=lam_buf)
         kernel()
 
@@ -172,14 +195,15 @@ def bench_workload(torch, da, name, steps, warmup):
     ms, wall = time_steps(torch, step, steps, warmup)
     kern_ms = time_kernel(torch, kernel, steps)
     log(f"[bench] {name}: {ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
-    if w.kind == "prefill":
+    if w.kind in ("prefill", "v2_prefill"):
         work = prefill_flops(w)
         value = work / (ms * 1e-3) / 1e12
         achieved = work / (kern_ms * 1e-3) / 1e12
         peak = PEAK["bf16_mfma_tflops"] if w.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic("prefill", name), "kernel": KERNEL_NAME["prefill"],
+                "traffic": measured_traffic("prefill", name) if w.kind == "prefill" else None,
+                "kernel": KERNEL_NAME["prefill"],
                 "algorithmic_per_launch": work}
         unit = "TFLOP/s"
     else:
@@ -188,14 +212,15 @@ def bench_workload(torch, da, name, steps, warmup):
         achieved = work / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"],
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm_gbs"], 4),
-                "traffic": measured_traffic("decode", name), "kernel": KERNEL_NAME["decode"],
+                "traffic": measured_traffic("decode", name) if w.kind == "decode" else None,
+                "kernel": KERNEL_NAME["decode"] if w.kind == "decode" else "decode_v2_partial_kernel",
                 "algorithmic_per_launch": work}
         unit = "GB/s"
     res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
            "kernel_ms": round(kern_ms, 5), "wall_s": round(wall, 4), "roofline": roof,
-           "shape": {"B": w.B, "H": w.H, ("T" if w.kind == "prefill" else "L"): w.T, "D": w.D,
-                     "causal": w.causal if w.kind == "prefill" else False,
-                     "headnorm": w.headnorm, "dtype": w.dtype}}
+           "shape": {"B": w.B, "H": w.H, ("T" if w.kind.endswith("prefill") else "L"): w.T, "D": w.D,
+                     "causal": w.causal if w.kind.endswith("prefill") else False,
+                     "headnorm": w.headnorm, "dtype": w.dtype, **({"Hkv": w.Hkv} if w.Hkv else {})}}
     del x, out
     torch.cuda.empty_cache()
     return res

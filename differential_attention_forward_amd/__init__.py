@@ -26,7 +26,7 @@ __all__ = [
     "diffattn_fwd_reparam", "diffattn_attention_fwd",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
     "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_bwd_workspace_bytes",
-    "diffattn_bwd",
+    "diffattn_bwd", "diffattn_v2_fwd", "diffattn_v2_decode_workspace_bytes", "diffattn_v2_decode",
 ]
 
 DIFFATTN_F32 = 0
@@ -56,6 +56,10 @@ _SIGS = {
     "diffattn_fwd_train": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
                                 _VP, _VP, ctypes.c_size_t, _VP]),
     "diffattn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "diffattn_v2_fwd": (_I, [_I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _I, _VP, _VP]),
+    "diffattn_v2_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "diffattn_v2_decode": (_I, [_I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _I, _VP,
+                                ctypes.c_size_t, _VP, _VP]),
     "diffattn_bwd": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                           ctypes.c_size_t, _I, _I, _F, _F, _VP, _VP, _VP, _VP, _VP, _VP,
                           _VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -270,6 +274,57 @@ def diffattn_decode(q1, k1, q2, k2, v, lam, headnorm: bool = False, lambda_init:
                                  float(lambda_init), float(eps), int(num_splits),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _ptr(out), _stream(stream)))
+    return out
+
+
+def _v2_inputs(q1, q2, k, v, tdim):
+    q1, q2, k, v = (_dev(t, n) for t, n in ((q1, "q1"), (q2, "q2"), (k, "k"), (v, "v")))
+    if q1.dim() != tdim or k.dim() != 4:
+        raise ValueError("DIFF V2 shapes: q1, q2 [B, H, (T,) D], k, v [B, Hkv, T, D]")
+    if q2.shape != q1.shape or v.shape != k.shape:
+        raise ValueError("q2 must match q1 and v must match k")
+    if k.shape[0] != q1.shape[0] or k.shape[-1] != q1.shape[-1]:
+        raise ValueError("k, v must have the batch and head width of q1")
+    for x in (q2, k, v):
+        if x.dtype != q1.dtype:
+            raise ValueError("all inputs must share one dtype")
+    return q1, q2, k, v
+
+
+def diffattn_v2_fwd(q1, q2, k, v, lam, causal: bool = True, out=None, stream=None):
+    """DIFF V2 prefill; q1, q2 [B,H,T,D], k, v [B,Hkv,T,D] -> out [B,H,T,D]."""
+    q1, q2, k, v = _v2_inputs(q1, q2, k, v, 4)
+    b, h, t, d = q1.shape
+    hkv = k.shape[1]
+    if k.shape[2] != t:
+        raise ValueError("k, v must have the sequence length of q1")
+    lamv = _lambda_vec(lam, h, q1.device)
+    if out is None:
+        out = torch.empty_like(q1)
+    _check(lib().diffattn_v2_fwd(_dtype_code(q1), b, h, hkv, t, d, _ptr(q1), _ptr(q2), _ptr(k),
+                                 _ptr(v), _ptr(lamv), int(bool(causal)), _ptr(out), _stream(stream)))
+    return out
+
+
+def diffattn_v2_decode_workspace_bytes(B: int, H: int, Hkv: int, L: int, D: int, num_splits: int = 0) -> int:
+    return int(lib().diffattn_v2_decode_workspace_bytes(B, H, Hkv, L, D, num_splits))
+
+
+def diffattn_v2_decode(q1, q2, k, v, lam, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """DIFF V2 decode; q1, q2 [B,H,D], caches k, v [B,Hkv,L,D] -> out [B,H,D]."""
+    q1, q2, k, v = _v2_inputs(q1, q2, k, v, 3)
+    b, h, d = q1.shape
+    hkv, l = k.shape[1], k.shape[2]
+    lamv = _lambda_vec(lam, h, q1.device)
+    need = diffattn_v2_decode_workspace_bytes(b, h, hkv, l, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, device=q1.device, dtype=torch.float32)
+    if out is None:
+        out = torch.empty((b, h, d), device=q1.device, dtype=q1.dtype)
+    _check(lib().diffattn_v2_decode(_dtype_code(q1), b, h, hkv, l, d, _ptr(q1), _ptr(q2), _ptr(k),
+                                    _ptr(v), _ptr(lamv), int(num_splits), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _ptr(out),
+                                    _stream(stream)))
     return out
 
 

@@ -97,6 +97,7 @@ diffattn_status check_fwd(int dtype, int B, int H, int T, int D, const void* q1,
   a.save_lse = nullptr;
   a.B = B;
   a.H = H;
+  a.Hkv = H;
   a.T = T;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   out_bytes = nv;
@@ -191,6 +192,7 @@ diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, co
   a.save_lse = nullptr;
   a.B = B;
   a.H = H;
+  a.Hkv = H;
   a.T = T;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   a.out_scale = 1.0f;
@@ -412,10 +414,110 @@ diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const voi
   a.H = H;
   a.L = L;
   a.S = S;
+  a.Hkv = H;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   a.out_scale = 1.0f - lambda_init;
   a.eps = eps;
   return from_hip(diffattn::launch_decode(a, dtype, D, headnorm != 0, stream));
+}
+
+// ---- DIFF V2: two query heads per differential head, K/V shared per group ----
+
+diffattn_status diffattn_v2_fwd(int dtype, int B, int H, int Hkv, int T, int D, const void* q1,
+                                const void* q2, const void* k, const void* v, const float* lambda,
+                                int causal, void* out, hipStream_t stream) {
+  if (!q1 || !q2 || !k || !v || !lambda || !out) return DIFFATTN_ERR_INVALID;
+  if (B < 1 || H < 1 || Hkv < 1 || T < 1 || H % Hkv) return DIFFATTN_ERR_INVALID;
+  if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return DIFFATTN_ERR_UNSUPPORTED;
+  const void* ins[4] = {q1, q2, k, v};
+  for (const void* p : ins)
+    if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(out, 16) || !aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H > 0x7fffffffLL || (long long)T * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  const size_t nq = (size_t)B * H * T * D * 2, nkv = (size_t)B * Hkv * T * D * 2;
+  const size_t sizes[4] = {nq, nq, nkv, nkv};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(out, nq, ins[i], sizes[i])) return DIFFATTN_ERR_INVALID;
+  if (overlaps(out, nq, lambda, (size_t)H * 4)) return DIFFATTN_ERR_INVALID;
+  diffattn::FwdArgs a;
+  a.q1 = q1;
+  a.k1 = k;
+  a.q2 = q2;
+  a.k2 = k;
+  a.v = v;
+  a.lam = lambda;
+  for (int i = 0; i < 4; ++i) a.lvec[i] = nullptr;
+  a.Dl = 0;
+  a.lam_init = 0.0f;
+  a.lam_out = nullptr;
+  a.out = out;
+  a.save_o1 = nullptr;
+  a.save_o2 = nullptr;
+  a.save_lse = nullptr;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.Hkv = Hkv;
+  a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
+  a.out_scale = 1.0f;
+  a.eps = 1.0f;
+  return from_hip(diffattn::launch_v2(a, D, causal != 0, stream));
+}
+
+size_t diffattn_v2_decode_workspace_bytes(int B, int H, int Hkv, int L, int D, int num_splits) {
+  if (B < 1 || H < 1 || Hkv < 1 || L < 1 || D < 1 || num_splits < 0 || num_splits > L) return 0;
+  const int s = num_splits ? num_splits : diffattn_decode_default_splits(B, Hkv, L);
+  return (size_t)B * H * s * 2 * ((size_t)D + 2) * sizeof(float);
+}
+
+diffattn_status diffattn_v2_decode(int dtype, int B, int H, int Hkv, int L, int D, const void* q1,
+                                   const void* q2, const void* k, const void* v, const float* lambda,
+                                   int num_splits, void* workspace, size_t workspace_bytes, void* out,
+                                   hipStream_t stream) {
+  if (!q1 || !q2 || !k || !v || !lambda || !out) return DIFFATTN_ERR_INVALID;
+  if (B < 1 || H < 1 || Hkv < 1 || L < 1 || H % Hkv) return DIFFATTN_ERR_INVALID;
+  if (num_splits < 0 || num_splits > L) return DIFFATTN_ERR_INVALID;
+  if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return DIFFATTN_ERR_UNSUPPORTED;
+  const int grp = H / Hkv;
+  if (grp != 1 && grp != 2 && grp != 4) return DIFFATTN_ERR_UNSUPPORTED;
+  const void* ins[4] = {q1, q2, k, v};
+  for (const void* p : ins)
+    if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(out, 16) || !aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  const int S = num_splits ? num_splits : diffattn_decode_default_splits(B, Hkv, L);
+  if ((long long)B * H * S > 0x7fffffffLL || (long long)L * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  const size_t need = diffattn_v2_decode_workspace_bytes(B, H, Hkv, L, D, S);
+  if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return DIFFATTN_ERR_UNSUPPORTED;
+  const size_t nq = (size_t)B * H * D * 2, nkv = (size_t)B * Hkv * L * D * 2;
+  const size_t sizes[4] = {nq, nq, nkv, nkv};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(out, nq, ins[i], sizes[i])) return DIFFATTN_ERR_INVALID;
+    if (overlaps(workspace, need, ins[i], sizes[i])) return DIFFATTN_ERR_INVALID;
+  }
+  if (overlaps(out, nq, workspace, need) || overlaps(out, nq, lambda, (size_t)H * 4) ||
+      overlaps(workspace, need, lambda, (size_t)H * 4))
+    return DIFFATTN_ERR_INVALID;
+  diffattn::DecodeArgs a;
+  a.q1 = q1;
+  a.k1 = k;
+  a.q2 = q2;
+  a.k2 = k;
+  a.v = v;
+  a.lam = lambda;
+  a.ws = (float*)workspace;
+  a.out = out;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.S = S;
+  a.Hkv = Hkv;
+  a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
+  a.out_scale = 1.0f;
+  a.eps = 1.0f;
+  return from_hip(diffattn::launch_decode_v2(a, D, stream));
 }
 
 }  // extern "C"

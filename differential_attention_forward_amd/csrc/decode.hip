@@ -250,15 +250,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   }
 }
 
-template <int D, bool F32, bool HEADNORM>
+template <int DV, bool F32, bool HEADNORM>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  // One workgroup per (b, h): 256 threads = 2D channels x (256 / 2D) split
-  // groups.  The per-split maxima are staged in LDS first; each thread then
-  // merges a fixed, contiguous range of splits for its channel (independent
-  // loads, unrolled), and the split groups are combined in a fixed order, so
-  // the result does not depend on timing.
+  // One workgroup per (b, h): 256 threads = DV channels x (256 / DV) split
+  // groups (DV = 2D for the first version, D for V2).  The per-split maxima
+  // are staged in LDS first; each thread then merges a fixed, contiguous
+  // range of splits for its channel (independent loads, unrolled), and the
+  // split groups are combined in a fixed order, so the result does not depend
+  // on timing.
   using E = Elem<F32>;
-  constexpr int DV = 2 * D;
   constexpr int RS = 2 * (DV + 2);
   constexpr int NG = 256 / DV;  // split groups
   __shared__ float sm[2][kMaxSplitsLds];
@@ -348,12 +348,232 @@ hipError_t launch_d(const DecodeArgs& a, bool headnorm, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g((unsigned)(a.B * a.H)), b(256);
-  if (headnorm) decode_reduce_kernel<D, F32, true><<<g, b, 0, stream>>>(a);
-  else decode_reduce_kernel<D, F32, false><<<g, b, 0, stream>>>(a);
+  if (headnorm) decode_reduce_kernel<2 * D, F32, true><<<g, b, 0, stream>>>(a);
+  else decode_reduce_kernel<2 * D, F32, false><<<g, b, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// DIFF V2 decode partial (the French lesson page, "V1 contre V2": the two
+// queries of a differential head read one shared K/V cache, so the cache is
+// read once per step and the arithmetic per cache byte rises).  One workgroup
+// per (b, KV head g, split) serves all G differential heads of the group: NR =
+// 2G query rows (q1 and q2 of each head) against one read of the chunk's K
+// and V rows.  Same sub-chunk structure as decode_partial_kernel; the records
+// it writes have the first version's layout with value width D, one per
+// (b, head, split), so decode_reduce_kernel<D> finishes them.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_v2_partial_kernel(DecodeArgs a) {
+  constexpr int NR = 2 * G;           // query rows: row 2j + m is map m of head j
+  constexpr int EPC = 8;              // bf16 elements per 16-byte chunk
+  constexpr int LPK = D / EPC;        // lanes per K row
+  constexpr int KPR = kThreads / LPK; // key rows per pass (score phase)
+  constexpr int LPV = D / EPC;        // lanes per V row
+  constexpr int VPR = kThreads / LPV; // V rows per pass
+  constexpr int RS = 2 * (D + 2);     // floats per (b, head, split) record
+  static_assert(LPK <= 64, "row must fit in one wave");
+
+  __shared__ float sp[kSub][NR];      // per key and row: score, then probability
+  __shared__ float red[kWaves][NR];
+  __shared__ float accred[kWaves][NR][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int S = a.S;
+  const int split = blockIdx.x % S;
+  const int bg = blockIdx.x / S;       // b * Hkv + g
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int head0 = b * a.H + g * G;   // first (b, head) index of the group
+  const int L = a.L;
+  const int chunk = (L + S - 1) / S;
+  const int kb = min(L, split * chunk);
+  const int ke = min(L, kb + chunk);
+
+  const bf16* __restrict__ K = (const bf16*)a.k1 + (size_t)bg * L * D;
+  const bf16* __restrict__ V = (const bf16*)a.v + (size_t)bg * L * D;
+  const float sc = a.score_scale;
+
+  const int ksub = tid % LPK;
+  float qf[NR][EPC];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const bf16* qp = (const bf16*)(r & 1 ? a.q2 : a.q1) + (size_t)(head0 + r / 2) * D + ksub * EPC;
+    unpack16<false>(*(const u32x4*)qp, qf[r]);
+  }
+  const int vsub = tid % LPV;
+
+  float m[NR], l[NR], acc[NR][EPC];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    m[r] = kNegInf;
+    l[r] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[r][e] = 0.0f;
+  }
+
+  for (int base = kb; base < ke; base += kSub) {
+    const int n = min(kSub, ke - base);
+
+    // ---- scores of every query row against each key, one read per key ----------
+    for (int k0 = tid / LPK; k0 < n; k0 += KPR * kUnroll) {
+      u32x4 w[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = min(k0 + u * KPR, n - 1);  // clamped: always in bounds
+        w[u] = __builtin_nontemporal_load((const u32x4*)(K + (size_t)(base + kk) * D + ksub * EPC));
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float kf[EPC];
+        unpack16<false>(w[u], kf);
+        float d[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          d[r] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) d[r] = fmaf(qf[r][e], kf[e], d[r]);
+#pragma unroll
+          for (int o = 1; o < LPK; o <<= 1) d[r] += __shfl_xor(d[r], o);
+        }
+        const int kk = k0 + u * KPR;
+        if (ksub == 0 && kk < n) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r) sp[kk][r] = d[r] * sc;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- block max per row, rescale the running state ---------------------------
+    float bm[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) bm[r] = kNegInf;
+    for (int kk = tid; kk < n; kk += kThreads) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) bm[r] = fmaxf(bm[r], sp[kk][r]);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) bm[r] = wave_max(bm[r]);
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) red[wave][r] = bm[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      float mx = red[0][r];
+#pragma unroll
+      for (int wv = 1; wv < kWaves; ++wv) mx = fmaxf(mx, red[wv][r]);
+      const float nm = fmaxf(m[r], mx);
+      const float al = __builtin_amdgcn_exp2f(m[r] - nm);  // m = -inf -> 0
+      m[r] = nm;
+      l[r] *= al;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[r][e] *= al;
+    }
+    for (int kk = tid; kk < n; kk += kThreads) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sp[kk][r] - m[r]);
+        l[r] += p;
+        sp[kk][r] = p;
+      }
+    }
+    __syncthreads();
+
+    // ---- V pass: every row's weighted sum from one read of each V row ------------
+    for (int k0 = tid / LPV; k0 < n; k0 += VPR * kUnroll) {
+      u32x4 wv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = min(k0 + u * VPR, n - 1);
+        wv[u] = __builtin_nontemporal_load((const u32x4*)(V + (size_t)(base + kk) * D + vsub * EPC));
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = k0 + u * VPR;
+        if (kk < n) {
+          float vf[EPC];
+          unpack16<false>(wv[u], vf);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const float p = sp[kk][r];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[r][e] = fmaf(p, vf[e], acc[r][e]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // sp and red are rewritten by the next sub-chunk
+  }
+
+  // ---- reduce the per-thread shares and write one record per (head, split) -------
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    l[r] = wave_sum(l[r]);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+#pragma unroll
+      for (int o = LPV; o < 64; o <<= 1) acc[r][e] += __shfl_xor(acc[r][e], o);
+    }
+  }
+  if (lane < LPV) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) accred[wave][r][vsub * EPC + e] = acc[r][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) red[wave][r] = l[r];
+  }
+  __syncthreads();
+  for (int i = tid; i < NR * D; i += kThreads) {
+    const int r = i / D, c = i % D;
+    float t = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) t += accred[wv][r][c];
+    a.ws[((size_t)(head0 + r / 2) * S + split) * RS + (r & 1) * (D + 2) + 2 + c] = t;
+  }
+  if (tid < NR) {
+    float t = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) t += red[wv][tid];
+    float* rec = a.ws + ((size_t)(head0 + tid / 2) * S + split) * RS + (tid & 1) * (D + 2);
+    // each thread's own m is the row's block-wide running max (same in every thread)
+    float mrow = m[0];
+#pragma unroll
+    for (int r = 1; r < NR; ++r) mrow = r == tid ? m[r] : mrow;
+    rec[0] = mrow;
+    rec[1] = t;
+  }
+}
+
+template <int D, int G>
+hipError_t launch_v2_d(const DecodeArgs& a, hipStream_t stream) {
+  const long nblk = (long)a.B * a.Hkv * a.S;
+  if (nblk > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  decode_v2_partial_kernel<D, G><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_reduce_kernel<D, false, false><<<dim3((unsigned)(a.B * a.H)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_decode_v2(const DecodeArgs& a, int D, hipStream_t stream) {
+  const int grp = a.H / a.Hkv;
+  if (D == 64) {
+    if (grp == 1) return launch_v2_d<64, 1>(a, stream);
+    if (grp == 2) return launch_v2_d<64, 2>(a, stream);
+    if (grp == 4) return launch_v2_d<64, 4>(a, stream);
+  } else if (D == 128) {
+    if (grp == 1) return launch_v2_d<128, 1>(a, stream);
+    if (grp == 2) return launch_v2_d<128, 2>(a, stream);
+    if (grp == 4) return launch_v2_d<128, 4>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, bool headnorm, hipStream_t stream) {
   if (dtype == 1) {

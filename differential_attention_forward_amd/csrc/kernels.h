@@ -28,6 +28,7 @@ struct FwdArgs {
   float* save_o2;
   float* save_lse;
   int B, H, T;
+  int Hkv;            // V2 only: KV heads; head h reads KV head h / (H / Hkv)
   float score_scale;  // log2(e) / sqrt(D)
   float out_scale;    // 1 - lambda_init (head norm only)
   float eps;
@@ -43,6 +44,7 @@ struct DecodeArgs {
   float* ws;          // [B,H,S, 2*(2D+2)] fp32 partial states
   void* out;          // [B,H,2D]
   int B, H, L, S;
+  int Hkv;            // V2 only: KV heads; head h reads KV head h / (H / Hkv)
   float score_scale;
   float out_scale;
   float eps;
@@ -87,8 +89,13 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
                       hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, bool headnorm,
                          hipStream_t stream);
+// DIFF V2 decode, bf16: q1/q2 [B,H,D], k/v caches [B,Hkv,L,D], out [B,H,D];
+// group size H / Hkv in {1, 2, 4}, D = 64 or 128
+hipError_t launch_decode_v2(const DecodeArgs& a, int D, hipStream_t stream);
 // standard softmax attention, bf16, Q/K/V/O [B,H,T,D] (D = 64 or 128)
 hipError_t launch_attention(const FwdArgs& a, int D, bool causal, hipStream_t stream);
+// DIFF V2, bf16: Q1/Q2/O [B,H,T,D], K/V [B,Hkv,T,D] (D = 64 or 128)
+hipError_t launch_v2(const FwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, bool headnorm, hipStream_t stream);
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2,
                          const float* lk2, int H, int Dl, float lambda_init, float* out,

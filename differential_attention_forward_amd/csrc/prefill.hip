@@ -430,12 +430,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
 // lane's probabilities reach the MFMA.
 
 // MAPS = 2: differential attention (Q1, K1, Q2, K2 of width D, V of width
-// 2D).  MAPS = 1: standard softmax attention (Q, K, V of width D), the
+// 2D); with SHKV, the V2 form instead: both maps read one K tile and one V
+// tile of width D, shared by a group of heads.  MAPS = 1: standard softmax
+// attention (Q, K, V of width D), the
 // comparison kernel of the same size as a differential head of width D/2.
-template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, int MAPS = 2>
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, int MAPS = 2, bool SHKV = false>
 struct CfgB {
   static constexpr int BC = 64;
-  static constexpr int DV = MAPS == 2 ? 2 * D : D;
+  static constexpr int DV = MAPS == 2 && !SHKV ? 2 * D : D;
+  static constexpr int KT = SHKV ? 1 : MAPS;        // K tiles per stage
   static constexpr int QPW = 32 * NQB;
   static constexpr int NBR = SPLIT || MAPS == 1 ? 1 : 2;
   static constexpr int NWQ = SPLIT ? NW / 2 : NW;
@@ -443,7 +446,7 @@ struct CfgB {
   static constexpr int NT = NW * 64;
   static constexpr int KBYTES = BC * D * 2;
   static constexpr int VBYTES = BC * DV * 2;
-  static constexpr int STAGE = MAPS * KBYTES + VBYTES;
+  static constexpr int STAGE = KT * KBYTES + VBYTES;
   static constexpr int KSEG = KBYTES / 1024;   // 1-KiB segments per K tile
   static constexpr int NSEG = STAGE / 1024;    // per stage
   static constexpr int SEGW = (NSEG + NW - 1) / NW;  // most loads one wave issues per tile
@@ -459,6 +462,7 @@ struct CfgB {
   static constexpr bool NEGMU_REGS = NBR * NQB == 1 && D <= 64;
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "two to four stages");
   static_assert(MAPS == 2 || !SPLIT, "one map: nothing to split");
+  static_assert(MAPS == 2 || !SHKV, "shared K/V is the two-map V2 form");
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -481,9 +485,10 @@ __device__ inline int swz_v(int row) {
   return DV >= 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM, int MAPS = 2>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
-  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, MAPS>;
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM, int MAPS = 2,
+          bool SHKV = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 ? 2 : NW / 4, NW < 8 ? 2 : NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
+  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, MAPS, SHKV>;
   constexpr int BC = C::BC;
   constexpr int PD = NSTAGE - 1;  // prefetch distance in tiles
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -504,12 +509,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
   const int h = bh % a.H;
 
+  // V2: head h of batch b reads KV head h / (H / Hkv) of that batch
+  const int kvbh = SHKV ? (bh / a.H) * a.Hkv + h / (a.H / a.Hkv) : bh;
   const size_t qk_off = (size_t)bh * T * D;
-  const size_t v_off = (size_t)bh * T * C::DV;
+  const size_t kv_off = (size_t)kvbh * T * D;
+  const size_t v_off = (size_t)kvbh * T * C::DV;
+  const size_t o_off = (size_t)bh * T * C::DV;
   const bf16* __restrict__ Q1 = (const bf16*)a.q1 + qk_off;
   const bf16* __restrict__ Q2 = (const bf16*)a.q2 + qk_off;
-  const bf16* __restrict__ K1 = scalar_ptr((const bf16*)a.k1 + qk_off);
-  const bf16* __restrict__ K2 = scalar_ptr((const bf16*)a.k2 + qk_off);
+  const bf16* __restrict__ K1 = scalar_ptr((const bf16*)a.k1 + kv_off);
+  const bf16* __restrict__ K2 = SHKV ? K1 : scalar_ptr((const bf16*)a.k2 + kv_off);
   const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + v_off);
 
   const int wbr = SPLIT ? wave / C::NWQ : 0;
@@ -541,7 +550,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (int i = 0; i < C::SEGW; ++i) {
       const int seg = wave + i * NW;
       if (seg >= C::NSEG) break;
-      if (seg < MAPS * C::KSEG) {
+      if (seg < C::KT * C::KSEG) {
         const int which = seg / C::KSEG;
         const int g = seg % C::KSEG;
         const int r = g * RK + rl_k;
@@ -549,11 +558,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
         dma16(which ? K2 : K1, row * (D * 2) + c * 16, sb + which * C::KBYTES + g * 1024);
       } else {
-        const int g = seg - MAPS * C::KSEG;
+        const int g = seg - C::KT * C::KSEG;
         const int r = g * RV + rl_v;
         const int c = (lane % CV) ^ swz_v<C::DV>(r);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
-        dma16(V, row * (C::DV * 2) + c * 16, sb + MAPS * C::KBYTES + g * 1024);
+        dma16(V, row * (C::DV * 2) + c * 16, sb + C::KT * C::KBYTES + g * 1024);
       }
     }
   };
@@ -638,12 +647,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // S^T of block kb for both maps: scaled scores minus the row reference
   // (base-2 units), the reference entering as the first MFMA's accumulator
   auto qk = [&](int kb, const char* sb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
-    const char* Kb[2] = {sb + (SPLIT && wbr ? C::KBYTES : 0), sb + C::KBYTES};
+    // (V2: one K tile serves both maps, and each fragment is read once)
+    const char* Kb[2] = {sb + (SPLIT && wbr && !SHKV ? C::KBYTES : 0), sb + (SHKV ? 0 : C::KBYTES)};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      bf16x8 av;
 #pragma unroll
       for (int br = 0; br < C::NBR; ++br) {
-        const bf16x8 av = *(const bf16x8*)(Kb[br] + kb * 32 * (2 * D) + k_rd + (((2 * ks + hi) ^ swk) << 4));
+        if (br == 0 || !SHKV)
+          av = *(const bf16x8*)(Kb[br] + kb * 32 * (2 * D) + k_rd + (((2 * ks + hi) ^ swk) << 4));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           s[br][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[br][qb][ks], ks > 0 ? s[br][qb]
@@ -744,7 +756,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   // acc += P^T-weighted V rows of block kb; each V fragment serves both maps
   auto pv = [&](int kb, const char* sb, const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
-    const char* Vb = sb + MAPS * C::KBYTES;
+    const char* Vb = sb + C::KT * C::KBYTES;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -802,7 +814,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   auto save_map = [&](int br, int query, float m, float l, float inv, const floatx16 (&ac)[C::CB])
       __attribute__((always_inline)) {
     if (a.save_o1 == nullptr || query >= T) return;
-    float* dst = (br ? a.save_o2 : a.save_o1) + v_off + (size_t)query * C::DV;
+    float* dst = (br ? a.save_o2 : a.save_o1) + o_off + (size_t)query * C::DV;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -840,7 +852,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   if (!wave_active) return;
 
   // ---- epilogue: combine the maps, optional head norm, store -----------------
-  bf16* __restrict__ O = (bf16*)a.out + v_off;
+  bf16* __restrict__ O = (bf16*)a.out + o_off;
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int query = q0 + qb * 32 + l32;
@@ -915,6 +927,18 @@ hipError_t launch_bf16(const FwdArgs& a, bool causal, bool headnorm, hipStream_t
   return hipGetLastError();
 }
 
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT>
+hipError_t launch_v2_d(const FwdArgs& a, bool causal, hipStream_t stream) {
+  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, 2, true>;
+  const long nqt = (a.T + C::BR - 1) / C::BR;
+  const long grid = (long)a.B * a.H * nqt;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), b(C::NT);
+  if (causal) fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, false, 2, true><<<g, b, 0, stream>>>(a);
+  else fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, false, false, 2, true><<<g, b, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int D, int NQB, int NW, int NSTAGE>
 hipError_t launch_std(const FwdArgs& a, bool causal, hipStream_t stream) {
   using C = CfgB<D, NQB, NW, NSTAGE, false, 1>;
@@ -955,6 +979,16 @@ long compute_units() {
 }
 
 }  // namespace
+
+hipError_t launch_v2(const FwdArgs& a, int D, bool causal, hipStream_t stream) {
+  switch (D) {
+    // both maps per wave: K and V fragments each serve two MFMAs
+    case 64: return launch_v2_d<64, 1, 8, 3, false>(a, causal, stream);
+    // one map per wave (registers: the accumulators alone take 64 VGPRs per map)
+    case 128: return launch_v2_d<128, 1, 8, 3, true>(a, causal, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_attention(const FwdArgs& a, int D, bool causal, hipStream_t stream) {
   switch (D) {

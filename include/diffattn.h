@@ -184,6 +184,61 @@ diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const voi
                                 void* out, hipStream_t stream);
 
 /*
+ * ---- DIFF V2 (the French lesson page "Attention différentielle (V2)",
+ *      "V1 contre V2") ----
+ *
+ * V2 doubles the query heads and keeps the baseline's KV heads and head
+ * width: the two queries of differential head p read the same K and V (those
+ * of KV head g = p / (H / Hkv), the grouping of grouped-query attention), the
+ * difference is taken after attention, and there is no per-head norm:
+ *
+ *   O_p = (softmax(Q1_p K_g^T / sqrt(D) + M) - lambda_p softmax(Q2_p K_g^T / sqrt(D) + M)) V_g
+ *
+ * bf16 only, D = 64 or 128, fp32 accumulation; mask and lambda as for
+ * diffattn_fwd.
+ *
+ *   q1, q2   [B, H, T, D]    the two query heads of each differential head
+ *   k, v     [B, Hkv, T, D]  H must be a whole multiple of Hkv
+ *   lambda   [H] fp32 (device)
+ *   out      [B, H, T, D]
+ * Errors: ERR_INVALID (null pointer, sizes < 1, H not a multiple of Hkv,
+ * overlapping output), ERR_UNSUPPORTED (dtype other than bf16, D, alignment,
+ * grid size), ERR_HIP.
+ */
+diffattn_status diffattn_v2_fwd(int dtype, int B, int H, int Hkv, int T, int D, const void* q1,
+                                const void* q2, const void* k, const void* v, const float* lambda,
+                                int causal, void* out, hipStream_t stream);
+
+/*
+ * Bytes of fp32 workspace diffattn_v2_decode needs: B*H*S*2*(D+2)*4, with
+ * S = num_splits or, for num_splits = 0, diffattn_decode_default_splits(B, Hkv, L).
+ * Returns 0 for invalid sizes.
+ */
+size_t diffattn_v2_decode_workspace_bytes(int B, int H, int Hkv, int L, int D, int num_splits);
+
+/*
+ * V2 decode: one new query pair per (b, differential head) against the KV
+ * cache of its group, no mask.  Each workgroup reads a chunk of one KV head's
+ * cache once and serves all H / Hkv differential heads of the group (both
+ * maps of each), so the cache bytes per step are those of a grouped-query
+ * baseline with the same (Hkv, H).
+ *
+ *   q1, q2   [B, H, D]
+ *   k, v     [B, Hkv, L, D]  caches; H / Hkv must be 1, 2 or 4
+ *   lambda   [H] fp32 (device)
+ *   num_splits, workspace, workspace_bytes   as for diffattn_decode (sized by
+ *            diffattn_v2_decode_workspace_bytes)
+ *   out      [B, H, D]
+ * Errors: as diffattn_v2_fwd, plus ERR_INVALID for num_splits < 0 or > L,
+ * ERR_UNSUPPORTED for another group size, ERR_WORKSPACE for a null or too
+ * small workspace.
+ */
+diffattn_status diffattn_v2_decode(int dtype, int B, int H, int Hkv, int L, int D, const void* q1,
+                                   const void* q2, const void* k, const void* v, const float* lambda,
+                                   int num_splits, void* workspace, size_t workspace_bytes, void* out,
+                                   hipStream_t stream);
+
+/*
  * ---- Training: forward with saved state, and the backward pass ----
  *
  * The paperleet page "Differential Transformer Attention" asks for gradients

@@ -24,8 +24,9 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     assert "diffattn_fwd_reparam" in names and "diffattn_attention_fwd" in names
+    assert "diffattn_v2_fwd" in names and "diffattn_v2_decode" in names
     assert "diffattn_fwd_train" in names and "diffattn_bwd" in names
     for n in names:
         assert hasattr(L, n), n
@@ -161,6 +162,46 @@ def test_decode_validation(L):
     assert dec(L, ws=P(8, 8)) == UNSUPPORTED
     # workspace overlapping the value cache
     assert dec(L, ws=P(4, 64)) == INVALID
+
+
+def v2f(L, dtype=BF16, B=1, H=4, Hkv=2, T=8, D=64, ptrs=None):
+    p = ptrs or [P(i) for i in range(6)]
+    return L.diffattn_v2_fwd(dtype, B, H, Hkv, T, D, p[0], p[1], p[2], p[3], p[4], 1, p[5], None)
+
+
+def test_v2_fwd_validation(L):
+    assert v2f(L, ptrs=[P(0), None, P(2), P(3), P(4), P(5)]) == INVALID
+    assert v2f(L, ptrs=[P(0), P(1), P(2), P(3), None, P(5)]) == INVALID   # lambda
+    assert v2f(L, B=0) == INVALID
+    assert v2f(L, Hkv=0) == INVALID
+    assert v2f(L, H=6, Hkv=4) == INVALID                                  # H not a multiple
+    assert v2f(L, dtype=F32) == UNSUPPORTED
+    for d in (32, 96):
+        assert v2f(L, D=d) == UNSUPPORTED
+    assert v2f(L, ptrs=[P(0), P(1), P(2, 8), P(3), P(4), P(5)]) == UNSUPPORTED
+    assert v2f(L, ptrs=[P(0), P(1), P(2), P(3), P(4), P(3, 64)]) == INVALID   # out over v
+
+
+def v2d(L, dtype=BF16, B=1, H=4, Hkv=2, Lk=64, D=64, splits=0, ws=None, wsb=1 << 20, ptrs=None):
+    p = ptrs or [P(i) for i in range(6)]
+    return L.diffattn_v2_decode(dtype, B, H, Hkv, Lk, D, p[0], p[1], p[2], p[3], p[4], splits,
+                                ws if ws is not None else P(8), wsb, p[5], None)
+
+
+def test_v2_decode_validation(L):
+    assert v2d(L, Lk=0) == INVALID
+    assert v2d(L, H=6, Hkv=4) == INVALID
+    assert v2d(L, splits=-1) == INVALID
+    assert v2d(L, Lk=10, splits=11) == INVALID
+    assert v2d(L, H=16, Hkv=2) == UNSUPPORTED                            # group of 8
+    assert v2d(L, dtype=F32) == UNSUPPORTED
+    assert v2d(L, D=32) == UNSUPPORTED
+    assert v2d(L, ws=ctypes.c_void_p(0)) == WORKSPACE
+    need = da.diffattn_v2_decode_workspace_bytes(1, 4, 2, 64, 64, 4)
+    assert need == 1 * 4 * 4 * 2 * (64 + 2) * 4
+    assert v2d(L, splits=4, wsb=need - 1) == WORKSPACE
+    assert v2d(L, ws=P(3, 64)) == INVALID                                # workspace over v
+    assert da.diffattn_v2_decode_workspace_bytes(1, 4, 2, 0, 64) == 0
 
 
 def test_lambda_validation(L):

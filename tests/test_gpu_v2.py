@@ -1,0 +1,134 @@
+"""GPU parity of the DIFF V2 path (two query heads per differential head, K
+and V shared by a group of heads, V as wide as Q, no head norm) through the C
+ABI, against the float64 oracle on the same seeded bf16 inputs.
+
+Tolerance: max |GPU - oracle| <= 2e-2 (bf16 inputs, fp32 accumulation), the
+bar the workload statement sets for bf16.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import differential_attention_forward_amd as da
+import oracle
+from workloads import WORKLOADS, make_workload, v2_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    da.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def maxerr(out, ref):
+    return float(np.max(np.abs(out.float().cpu().double().numpy() - ref)))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+def test_v2_fwd_sweep(D, causal):
+    for (H, Hkv) in ((4, 1), (4, 2), (2, 2)):
+        lam = torch.linspace(-0.3, 1.2, H)
+        for i, T in enumerate((1, 31, 64, 130, 300)):
+            x = v2_inputs(2, H, Hkv, T, D, "bf16", seed=5000 + 7 * D + 31 * H + i)
+            say(f"v2 fwd D={D} H={H} Hkv={Hkv} T={T} causal={causal}")
+            xd = {k: t.to(DEV) for k, t in x.items()}
+            out = da.diffattn_v2_fwd(xd["q1"], xd["q2"], xd["k"], xd["v"], lam.to(DEV), causal=causal)
+            torch.cuda.synchronize()
+            ref = oracle.diff_attention_v2(x["q1"], x["q2"], x["k"], x["v"], lam, causal)
+            err = maxerr(out, ref)
+            assert err <= TOL, (H, Hkv, T, err)
+
+
+def test_v2_identical_maps_cancel():
+    # q1 = q2 and lambda = 1: both maps are the same, the output is exactly 0
+    x = v2_inputs(1, 4, 2, 200, 64, "bf16", seed=77)
+    xd = {k: t.to(DEV) for k, t in x.items()}
+    for causal in (True, False):
+        out = da.diffattn_v2_fwd(xd["q1"], xd["q1"], xd["k"], xd["v"], 1.0, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_v2_decode_sweep(D):
+    for (H, Hkv) in ((2, 2), (4, 2), (8, 2)):
+        lam = torch.linspace(0.9, -0.2, H)
+        for Lk, splits in ((1, 0), (7, 3), (300, 0), (1000, 8), (4097, 64), (10, 8)):
+            x = v2_inputs(2, H, Hkv, Lk, D, "bf16", seed=6000 + D + Lk + H, decode=True)
+            say(f"v2 decode D={D} H={H} Hkv={Hkv} L={Lk} splits={splits}")
+            xd = {k: t.to(DEV) for k, t in x.items()}
+            out = da.diffattn_v2_decode(xd["q1"], xd["q2"], xd["k"], xd["v"], lam.to(DEV),
+                                        num_splits=splits)
+            torch.cuda.synchronize()
+            ref = oracle.diff_attention_v2_decode(x["q1"], x["q2"], x["k"], x["v"], lam)
+            err = maxerr(out, ref)
+            assert err <= TOL, (H, Hkv, Lk, splits, err)
+
+
+def test_v2_decode_is_last_causal_row():
+    x = v2_inputs(2, 4, 1, 777, 64, "bf16", seed=88)
+    xd = {k: t.to(DEV) for k, t in x.items()}
+    lam = torch.tensor([0.2, 0.5, 0.8, 1.1], device=DEV)
+    fwd = da.diffattn_v2_fwd(xd["q1"], xd["q2"], xd["k"], xd["v"], lam, causal=True)[:, :, -1]
+    outs = []
+    for s in (1, 5, 64):
+        outs.append(da.diffattn_v2_decode(xd["q1"][:, :, -1], xd["q2"][:, :, -1], xd["k"], xd["v"], lam,
+                                          num_splits=s))
+    torch.cuda.synchronize()
+    for o in outs:
+        # both are bf16 results of the same real numbers: within two roundings
+        assert (o.float() - fwd.float()).abs().max().item() <= TOL
+
+
+def test_workload_v2_prefill_t4k():
+    w = WORKLOADS["v2_prefill_t4k"]
+    x = make_workload(w.name, DEV)
+    out = da.diffattn_v2_fwd(x["q1"], x["q2"], x["k"], x["v"], x["lam"], causal=w.causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(w.seed)
+    lam = x["lam"].cpu().double().numpy()
+    grp = w.H // w.Hkv
+    worst = 0.0
+    for (b, p) in ((0, 0), (0, 7), (1, 13), (1, 15)):
+        rows = np.unique(np.concatenate([np.arange(24), np.arange(w.T - 16, w.T), rng.choice(w.T, 64, replace=False)]))
+        g = p // grp
+        ref = oracle.diff_attention_rows(x["q1"][b, p].cpu(), x["k"][b, g].cpu(), x["q2"][b, p].cpu(),
+                                         x["k"][b, g].cpu(), x["v"][b, g].cpu(), lam[p], w.causal, rows)
+        worst = max(worst, maxerr(out[b, p, rows], ref))
+    say(f"workload v2_prefill_t4k: max err {worst:.3e}")
+    assert worst <= TOL
+
+
+def test_workload_v2_decode_l64k():
+    w = WORKLOADS["v2_decode_l64k"]
+    say("workload v2_decode_l64k: generating 8.6 GB cache")
+    x = make_workload(w.name, DEV)
+    out = da.diffattn_v2_decode(x["q1"], x["q2"], x["k"], x["v"], x["lam"], num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    lam = x["lam"].cpu()
+    grp = w.H // w.Hkv
+    worst = 0.0
+    for (b, g) in ((0, 0), (9, 3), (31, 7)):
+        sl = slice(g * grp, (g + 1) * grp)
+        ref = oracle.diff_attention_v2_decode(x["q1"][b:b + 1, sl].cpu(), x["q2"][b:b + 1, sl].cpu(),
+                                              x["k"][b:b + 1, g:g + 1].cpu(), x["v"][b:b + 1, g:g + 1].cpu(),
+                                              lam[sl])
+        worst = max(worst, maxerr(out[b:b + 1, sl], ref))
+    say(f"workload v2_decode_l64k: max err {worst:.3e}")
+    del x
+    torch.cuda.empty_cache()
+    assert worst <= TOL

@@ -30,6 +30,18 @@ V and O [B,H,T,2D]; decode: one query per (b, h) against an L-row cache):
   decode_l64k               B32 H16, cache L=65536, D64, bf16, seed 5, lambda
                             vectors all zero (so lambda = lambda_init(24)),
                             64 key splits, no head norm
+
+DIFF V2 workloads (the French lesson page, "V1 contre V2" and its exercise of
+8 KV heads for 32 query heads; Q1, Q2 [B,H,T,D], K, V [B,Hkv,T,D]):
+
+  v2_prefill_t4k            B2 H16 Hkv4 T4096 D128, causal, bf16, seed 6,
+                            lambda_h ~ U[0.2, 0.8]
+  v2_decode_l64k            B32 H32 Hkv8, cache L=65536, D128, bf16, seed 7,
+                            lambda_h ~ U[0.2, 0.8], default key splits
+                            (the same cache bytes per KV head and key as
+                            decode_l64k has per head)
+
+V2 draw order: Q1, Q2, K, V (caches one batch row at a time), then lambda.
 """
 
 from __future__ import annotations
@@ -39,7 +51,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "prefill_inputs", "decode_inputs", "make_workload"]
+__all__ = ["Workload", "WORKLOADS", "prefill_inputs", "decode_inputs", "v2_inputs", "make_workload"]
 
 
 @dataclass(frozen=True)
@@ -65,6 +77,7 @@ class Workload:
     needles: int = 0
     value_offset: bool = False
     num_splits: int = 0
+    Hkv: int = 0              # DIFF V2: KV heads (0 = the first version)
     extra: dict = field(default_factory=dict)
 
 
@@ -81,6 +94,10 @@ WORKLOADS = {
                  input_scale=1.0 / math.sqrt(2.0)),
         Workload("decode_l64k", "decode", 32, 16, 65536, 64, "bf16", 5,
                  layer=24, lambda_dl=64, lambda_zero=True, num_splits=64),
+        Workload("v2_prefill_t4k", "v2_prefill", 2, 16, 4096, 128, "bf16", 6, causal=True,
+                 lam_uniform=(0.2, 0.8), Hkv=4),
+        Workload("v2_decode_l64k", "v2_decode", 32, 32, 65536, 128, "bf16", 7,
+                 lam_uniform=(0.2, 0.8), Hkv=8),
     ]
 }
 
@@ -195,9 +212,36 @@ def decode_inputs(B, H, L, D, dtype="bf16", seed=0, device="cpu", *, lambda_dl=0
     return out
 
 
+def v2_inputs(B, H, Hkv, T, D, dtype="bf16", seed=0, device="cpu", *, decode=False,
+              lam_uniform=None):
+    """DIFF V2 inputs: q1, q2 [B,H,T,D] (decode: [B,H,D]), K, V [B,Hkv,T,D],
+    iid N(0,1) cast to the compute dtype; lam [H] ~ U[lo, hi] when asked.
+    Caches are drawn one batch row at a time (small float32 temporaries)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = _tdtype(dtype)
+    qshape = (B, H, D) if decode else (B, H, T, D)
+    q1 = _randn(g, qshape, device).to(td)
+    q2 = _randn(g, qshape, device).to(td)
+    k = torch.empty((B, Hkv, T, D), device=device, dtype=td)
+    v = torch.empty((B, Hkv, T, D), device=device, dtype=td)
+    for b in range(B):
+        k[b] = _randn(g, (Hkv, T, D), device).to(td)
+        v[b] = _randn(g, (Hkv, T, D), device).to(td)
+    out = dict(q1=q1, q2=q2, k=k, v=v)
+    if lam_uniform is not None:
+        lo, hi = lam_uniform
+        u = torch.rand((H,), generator=g, device=device, dtype=torch.float32)
+        out["lam"] = lo + (hi - lo) * u
+    return out
+
+
 def make_workload(name: str, device="cpu"):
     """Inputs of a named workload, drawn on ``device`` with its recipe."""
     w = WORKLOADS[name]
+    if w.kind in ("v2_prefill", "v2_decode"):
+        return v2_inputs(w.B, w.H, w.Hkv, w.T, w.D, w.dtype, w.seed, device,
+                         decode=w.kind == "v2_decode", lam_uniform=w.lam_uniform)
     if w.kind == "prefill":
         return prefill_inputs(w.B, w.H, w.T, w.D, w.dtype, w.seed, device,
                               input_scale=w.input_scale, lambda_dl=w.lambda_dl,
