@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "DIFFATTN_F32", "DIFFATTN_BF16", "library_path", "lib",
     "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
-    "diffattn_fwd_reparam", "diffattn_attention_fwd",
+    "diffattn_fwd_reparam", "diffattn_fwd_window", "diffattn_attention_fwd",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
     "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_bwd_workspace_bytes",
     "diffattn_bwd", "diffattn_v2_fwd", "diffattn_v2_decode_workspace_bytes", "diffattn_v2_decode",
@@ -48,6 +48,8 @@ _SIGS = {
     "diffattn_fwd_reparam": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                   _I, _I, _I, _F, _F, _VP, _VP, _VP]),
     "diffattn_attention_fwd": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _I, _VP, _VP]),
+    "diffattn_fwd_window": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
+                                 _VP, _VP]),
     "diffattn_decode_default_splits": (_I, [_I, _I, _I]),
     "diffattn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "diffattn_decode": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F, _I,
@@ -195,6 +197,20 @@ def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = F
                               _ptr(k2), _ptr(v), _ptr(lamv), int(bool(causal)),
                               int(bool(headnorm)), float(lambda_init), float(eps), _ptr(out),
                               _stream(stream)))
+    return out
+
+
+def diffattn_fwd_window(q1, k1, q2, k2, v, lam, window: int, headnorm: bool = False,
+                        lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
+    """Causal prefill with a sliding window: row i sees keys i - window < j <= i."""
+    q1, k1, q2, k2, v = _fwd_inputs(q1, k1, q2, k2, v)
+    b, h, t, d = q1.shape
+    lamv = _lambda_vec(lam, h, q1.device)
+    if out is None:
+        out = torch.empty_like(v)
+    _check(lib().diffattn_fwd_window(_dtype_code(q1), b, h, t, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                                     _ptr(k2), _ptr(v), _ptr(lamv), int(window), int(bool(headnorm)),
+                                     float(lambda_init), float(eps), _ptr(out), _stream(stream)))
     return out
 
 

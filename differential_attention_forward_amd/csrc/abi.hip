@@ -98,6 +98,7 @@ diffattn_status check_fwd(int dtype, int B, int H, int T, int D, const void* q1,
   a.B = B;
   a.H = H;
   a.Hkv = H;
+  a.window = 0;
   a.T = T;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   out_bytes = nv;
@@ -121,6 +122,25 @@ diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* 
   a.out_scale = 1.0f - lambda_init;
   a.eps = eps;
   return from_hip(diffattn::launch_fwd(a, dtype, D, causal != 0, headnorm != 0, stream));
+}
+
+diffattn_status diffattn_fwd_window(int dtype, int B, int H, int T, int D, const void* q1,
+                                    const void* k1, const void* q2, const void* k2, const void* v,
+                                    const float* lambda, int window, int headnorm, float lambda_init,
+                                    float eps, void* out, hipStream_t stream) {
+  diffattn::FwdArgs a;
+  size_t nout = 0;
+  const diffattn_status st = check_fwd(dtype, B, H, T, D, q1, k1, q2, k2, v, headnorm, eps, out, a, nout);
+  if (st != DIFFATTN_OK) return st;
+  if (!lambda || window < 1) return DIFFATTN_ERR_INVALID;
+  if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (overlaps(out, nout, lambda, (size_t)H * sizeof(float))) return DIFFATTN_ERR_INVALID;
+  a.lam = lambda;
+  a.window = window < T ? window : 0;  // a window covering every key is the causal mask
+  a.out_scale = 1.0f - lambda_init;
+  a.eps = eps;
+  return from_hip(diffattn::launch_fwd(a, dtype, D, true, headnorm != 0, stream));
 }
 
 diffattn_status diffattn_fwd_reparam(int dtype, int B, int H, int T, int D, const void* q1,
@@ -193,6 +213,7 @@ diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, co
   a.B = B;
   a.H = H;
   a.Hkv = H;
+  a.window = 0;
   a.T = T;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   a.out_scale = 1.0f;
@@ -459,6 +480,7 @@ diffattn_status diffattn_v2_fwd(int dtype, int B, int H, int Hkv, int T, int D, 
   a.H = H;
   a.T = T;
   a.Hkv = Hkv;
+  a.window = 0;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   a.out_scale = 1.0f;
   a.eps = 1.0f;

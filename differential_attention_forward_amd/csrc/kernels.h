@@ -29,6 +29,7 @@ struct FwdArgs {
   float* save_lse;
   int B, H, T;
   int Hkv;            // V2 only: KV heads; head h reads KV head h / (H / Hkv)
+  int window;         // causal sliding window W (bf16 kernel): keys i - W < j <= i; 0 = none
   float score_scale;  // log2(e) / sqrt(D)
   float out_scale;    // 1 - lambda_init (head norm only)
   float eps;

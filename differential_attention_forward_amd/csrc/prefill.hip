@@ -486,7 +486,7 @@ __device__ inline int swz_v(int row) {
 }
 
 template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM, int MAPS = 2,
-          bool SHKV = false>
+          bool SHKV = false, bool WIN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 ? 2 : NW / 4, NW < 8 ? 2 : NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, MAPS, SHKV>;
   constexpr int BC = C::BC;
@@ -528,7 +528,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   const int q_last = min(q0 + C::QPW, T) - 1;
   const bool wave_active = q0 < T;
   const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
-  const int ntiles = (k_end + BC - 1) / BC;
+  // sliding window (causal only): row i sees keys i - W < j <= i.  Key tiles
+  // below the workgroup's first row's window are never loaded; kt below
+  // counts tiles from kt0.
+  const int W = CAUSAL && WIN ? a.window : 0;
+  const int kt0 = W > 0 ? max(0, q_tile0 - W + 1) / BC : 0;
+  const int ntiles = (k_end + BC - 1) / BC - kt0;
   const float sc = a.score_scale;
   float lamv = 0.0f;
   if constexpr (MAPS == 2) {
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   constexpr int CK = D / 8, RK = 64 / CK, CV = C::DV / 8, RV = 64 / CV;
   const int rl_k = lane / CK, rl_v = lane / CV;
   auto issue_rt = [&](int kt, char* sb) __attribute__((always_inline)) {
-    const int key0 = kt * BC;
+    const int key0 = (kt0 + kt) * BC;
 #pragma unroll
     for (int i = 0; i < C::SEGW; ++i) {
       const int seg = wave + i * NW;
@@ -608,17 +613,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // the row sum lsum of 2^(s - mu) and the accumulators.  negmu holds -mu
   // in all 16 elements and is the accumulator input of the first score MFMA,
   // so the scores arrive with the reference already subtracted.  mu starts
-  // at 0 and is set to the exact row max by the wave's first key block.
+  // at 0 and is set to the exact row max by the first block in which the row
+  // sees a key.
   floatx16 acc[C::NBR][NQB][C::CB];
   floatx16 negmu[C::NEGMU_REGS ? C::NBR : 1][C::NEGMU_REGS ? NQB : 1];
   float mu[C::NBR][NQB];
   float lsum[C::NBR][NQB];
+  bool seen[C::NBR][NQB];
 #pragma unroll
   for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       mu[br][qb] = 0.0f;
       lsum[br][qb] = 0.0f;
+      seen[br][qb] = false;
       if constexpr (C::NEGMU_REGS) negmu[br][qb] = splat16(0.0f);
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb)
@@ -640,8 +648,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // A 32-key block kb of tile kt takes part only if it holds a key this wave
   // may attend to.
   auto kb_live = [&](int kt, int kb) __attribute__((always_inline)) {
-    const int key0 = kt * BC + kb * 32;
-    return key0 < T && (!CAUSAL || key0 <= q_last);
+    const int key0 = (kt0 + kt) * BC + kb * 32;
+    return key0 < T && (!CAUSAL || key0 <= q_last) && (W == 0 || key0 + 31 > q0 - W);
   };
 
   // S^T of block kb for both maps: scaled scores minus the row reference
@@ -668,14 +676,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // -inf on the keys of block kb that a row may not see (causal: key > query;
   // full attention: keys past the ragged end), both maps
   auto mask_block = [&](int kt, int kb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
-    const int key0 = kt * BC + kb * 32;
+    const int key0 = (kt0 + kt) * BC + kb * 32;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int query = q0 + qb * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const bool masked = CAUSAL ? (key > query) : (key >= T);
+        const bool masked = CAUSAL ? (key > query || (W > 0 && query - key >= W)) : (key >= T);
 #pragma unroll
         for (int br = 0; br < C::NBR; ++br) s[br][qb][r] = masked ? kNegInf : s[br][qb][r];
       }
@@ -709,18 +717,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   };
 
   // Lazy rescale, after expo: the reference only moves when some probability
-  // of the block would exceed 2^kTau (then the lane's partial sum does), and
-  // on the wave's first block, which sets mu to the exact row max.  Otherwise
-  // mu stays at or below the running row max and within kTau of it from
-  // below, so every p <= 2^kTau and the final row sum is >= 1.  The rare path
-  // rescales acc and lsum and recomputes the block's probabilities.
+  // of the block would exceed 2^kTau (then the lane's partial sum does), or
+  // while a row has not yet seen a key (seen[] false): the first block in
+  // which it sees one sets mu to the exact row max.  Otherwise mu stays at or
+  // below the running row max and within kTau of it from below, so every
+  // p <= 2^kTau and the final row sum is >= 1.  The rare path rescales acc and
+  // lsum and recomputes the block's probabilities.
   auto settle = [&](bool first, floatx16 (&s)[C::NBR][NQB], bf16x8 (&pk)[C::NBR][NQB][2],
                     float (&bsum)[C::NBR][NQB]) __attribute__((always_inline)) {
-    bool need = first;
+    bool need = false;
 #pragma unroll
     for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) need |= bsum[br][qb] > kRescaleSum;
+    // without a window every row sees key 0, in the wave's first block
+    if constexpr (WIN) {
+#pragma unroll
+      for (int br = 0; br < C::NBR; ++br)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) need |= !seen[br][qb];
+    } else {
+      need |= first;
+    }
     if (__any(need)) {
 #pragma unroll
       for (int br = 0; br < C::NBR; ++br)
@@ -730,9 +748,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
 #pragma unroll
           for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][qb][r]);
           m = swap_halves_max(m);  // block max of s - mu over the row's 32 keys
-          // first block: every row sees key 0, so m is finite; later blocks
-          // only ever raise the reference
-          const float delta = first ? (m == kNegInf ? 0.0f : m) : fmaxf(m, 0.0f);
+          // a row's first visible key sets the reference; afterwards it only
+          // ever rises
+          const bool had = WIN ? seen[br][qb] : !first;
+          if constexpr (WIN) seen[br][qb] = had || m != kNegInf;
+          const float delta = had ? fmaxf(m, 0.0f) : (m == kNegInf ? 0.0f : m);
           const float alpha = __builtin_amdgcn_exp2f(-delta);
           mu[br][qb] += delta;
           lsum[br][qb] *= alpha;
@@ -779,10 +799,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {
     // whether any block of this tile crosses the causal diagonal (or the
     // ragged end) for this wave's rows
-    const bool masked = CAUSAL ? (kt * BC + BC - 1 > q0) : (kt * BC + BC > T);
+    const int tk0 = (kt0 + kt) * BC;
+    const bool masked = CAUSAL ? (tk0 + BC - 1 > q0 || (W > 0 && tk0 <= q_last - W)) : (tk0 + BC > T);
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
-      if (!kb_live(kt, kb)) break;
+      // (with a window the live blocks need not be a prefix of the tile)
+      if (!kb_live(kt, kb)) {
+        if constexpr (WIN) continue;
+        else break;
+      }
       floatx16 s[C::NBR][NQB];
       bf16x8 pk[C::NBR][NQB][2];
       float bs[C::NBR][NQB];
@@ -928,6 +953,18 @@ hipError_t launch_bf16(const FwdArgs& a, bool causal, bool headnorm, hipStream_t
 }
 
 template <int D, int NQB, int NW, int NSTAGE, bool SPLIT>
+hipError_t launch_window(const FwdArgs& a, bool headnorm, hipStream_t stream) {
+  using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
+  const long nqt = (a.T + C::BR - 1) / C::BR;
+  const long grid = (long)a.B * a.H * nqt;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), b(C::NT);
+  if (headnorm) fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, true, 2, false, true><<<g, b, 0, stream>>>(a);
+  else fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, false, 2, false, true><<<g, b, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int D, int NQB, int NW, int NSTAGE, bool SPLIT>
 hipError_t launch_v2_d(const FwdArgs& a, bool causal, hipStream_t stream) {
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, 2, true>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
@@ -1000,6 +1037,14 @@ hipError_t launch_attention(const FwdArgs& a, int D, bool causal, hipStream_t st
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool headnorm,
                       hipStream_t stream) {
+  if (dtype == 1 && a.window > 0) {  // causal sliding window (bf16)
+    switch (D) {
+      case 32: return launch_window<32, 1, 8, 3, false>(a, headnorm, stream);
+      case 64: return launch_window<64, 1, 8, 3, true>(a, headnorm, stream);
+      case 128: return launch_window<128, 1, 8, 2, true>(a, headnorm, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   if (dtype == 1) {  // bf16
     switch (D) {
       case 32: return launch_bf16<32, 1, 8, 3, false>(a, causal, headnorm, stream);

@@ -103,6 +103,24 @@ diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* 
                              float eps, void* out, hipStream_t stream);
 
 /*
+ * Prefill with a causal sliding window (the French lesson page, "Utilisez-le":
+ * hybrid stacks that alternate differential attention with sliding-window
+ * attention).  Row i sees the `window` most recent positions including itself,
+ * keys j with i - window < j <= i, in both maps; a window of T or more is the
+ * causal mask.  Key tiles outside every row's window are neither loaded nor
+ * computed.
+ *
+ *   window          >= 1
+ *   other arguments as for diffattn_fwd (causal implied); bf16 only
+ * Errors: as diffattn_fwd, plus ERR_INVALID for window < 1 and
+ * ERR_UNSUPPORTED for fp32.
+ */
+diffattn_status diffattn_fwd_window(int dtype, int B, int H, int T, int D, const void* q1,
+                                    const void* k1, const void* q2, const void* k2, const void* v,
+                                    const float* lambda, int window, int headnorm, float lambda_init,
+                                    float eps, void* out, hipStream_t stream);
+
+/*
  * Prefill forward with lambda formed in the same launch: exactly
  * diffattn_lambda(lq1, lk1, lq2, lk2, H, Dl, lambda_init, lambda) followed by
  * diffattn_fwd(..., lambda, ...), as one kernel (aifetchly page, section 3,

@@ -132,12 +132,18 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def _scores(q: np.ndarray, k: np.ndarray, rows: np.ndarray | None, causal: bool) -> np.ndarray:
+def _scores(q: np.ndarray, k: np.ndarray, rows: np.ndarray | None, causal: bool,
+            window: int | None = None) -> np.ndarray:
     """S = Q K^T / sqrt(D) for the given query rows, with the causal mask.
 
     paperleet page: scaled scores, M = -inf on keys j > i (future positions).
     q: [Tq_all, D], k: [Tk, D]; rows: indices into q (None = all rows, which are
     then positions 0..Tq-1).
+
+    ``window`` (with causal): sliding-window mask, the French lesson page's
+    hybrid stacks ("attention des fenêtres coulissantes").  Reading taken: row
+    i sees the W most recent positions including itself, keys j with
+    i - W < j <= i; M = -inf on every other key.
     """
     d = q.shape[-1]
     if rows is None:
@@ -146,6 +152,8 @@ def _scores(q: np.ndarray, k: np.ndarray, rows: np.ndarray | None, causal: bool)
     if causal:
         keys = np.arange(k.shape[0])
         s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+        if window is not None:
+            s = np.where(rows[:, None] - keys[None, :] >= window, -np.inf, s)
     return s
 
 
@@ -187,13 +195,14 @@ def _lam_per_head(lam, h: int) -> np.ndarray:
     return lam
 
 
-def diff_attention_rows(q1, k1, q2, k2, v, lam, causal: bool, rows, row_block: int = 512):
+def diff_attention_rows(q1, k1, q2, k2, v, lam, causal: bool, rows, row_block: int = 512,
+                        window: int | None = None):
     """O rows (A1 - lam A2) V for the selected query rows of one (b, h) slice.
 
     q*, k*: [T, D]; v: [T, 2D]; lam: python/0-d scalar; rows: 1-D int array of
     query positions.  Returns [len(rows), 2D] float64.  Each selected row's two
     score rows over all keys are materialised whole; ``row_block`` only bounds
-    how many rows are held at once.
+    how many rows are held at once.  ``window``: sliding-window mask (causal).
     """
     q1, k1, q2, k2, v = (_f64(t) for t in (q1, k1, q2, k2, v))
     lam = float(_f64(lam))
@@ -201,18 +210,20 @@ def diff_attention_rows(q1, k1, q2, k2, v, lam, causal: bool, rows, row_block: i
     out = np.empty((rows.shape[0], v.shape[-1]))
     for s in range(0, rows.shape[0], row_block):
         r = rows[s:s + row_block]
-        a1 = _softmax_rows(_scores(q1, k1, r, causal))
-        a2 = _softmax_rows(_scores(q2, k2, r, causal))
+        a1 = _softmax_rows(_scores(q1, k1, r, causal, window))
+        a2 = _softmax_rows(_scores(q2, k2, r, causal, window))
         out[s:s + row_block] = (a1 - lam * a2) @ v
     return out
 
 
-def diff_attention(q1, k1, q2, k2, v, lam, causal: bool = True, row_block: int = 512):
+def diff_attention(q1, k1, q2, k2, v, lam, causal: bool = True, row_block: int = 512,
+                   window: int | None = None):
     """O = (softmax(Q1K1^T/sqrt(D)+M) - lam softmax(Q2K2^T/sqrt(D)+M)) V.
 
     paperleet page: q*, k* are [B, H, T, D], v is [B, H, T, 2D], result
     [B, H, T, 2D] (the value aggregate before any head normalisation).
     ``lam`` is a scalar or one value per head [H].  float64 result.
+    ``window``: sliding-window mask (with causal), see ``_scores``.
     """
     q1, k1, q2, k2, v = (_f64(t) for t in (q1, k1, q2, k2, v))
     b, h, t, _ = q1.shape
@@ -223,7 +234,7 @@ def diff_attention(q1, k1, q2, k2, v, lam, causal: bool = True, row_block: int =
         for hi in range(h):
             out[bi, hi] = diff_attention_rows(
                 q1[bi, hi], k1[bi, hi], q2[bi, hi], k2[bi, hi], v[bi, hi],
-                lam_h[hi], causal, rows, row_block)
+                lam_h[hi], causal, rows, row_block, window)
     return out
 
 

@@ -41,6 +41,8 @@ What pins what:
                    the row-wise dQ function equals the full backward's rows
   lambda grads     the four lambda-vector gradients against autograd and
                    central finite differences of the closed form
+  sliding window   a window covering all keys is the causal mask; window 1
+                   gives (1 - lam) V_i; torch SDPA with the explicit band mask
   DIFF V2          grouped-query form (shared K/V per group, V as wide as Q):
                    torch's scaled_dot_product_attention with enable_gqa, for
                    every lambda and lambda = 0; V2 decode = last causal row
@@ -317,10 +319,33 @@ def check_v2_decode():
     assert np.max(np.abs(dec - full[:, :, -1])) < 1e-13
 
 
+def check_window():
+    """Sliding window (with causal): a window covering every key is the causal
+    mask; a window of 1 leaves each row its own key, O_i = (1 - lam) V_i; any
+    window equals torch's float64 scaled_dot_product_attention with the band
+    mask given explicitly (allowed iff i - W < j <= i), by linearity in the
+    two maps."""
+    q1, k1, q2, k2, v = _case(2, 3, 41, 8, seed=501)
+    lam = np.array([-0.3, 0.5, 1.2])
+    full = oracle.diff_attention(q1, k1, q2, k2, v, lam, True)
+    assert np.max(np.abs(oracle.diff_attention(q1, k1, q2, k2, v, lam, True, window=41) - full)) < 1e-13
+    o1 = oracle.diff_attention(q1, k1, q2, k2, v, lam, True, window=1)
+    ref1 = (1.0 - lam)[None, :, None, None] * v.numpy()
+    assert np.max(np.abs(o1 - ref1)) < 1e-13
+    i = torch.arange(41)[:, None]
+    j = torch.arange(41)[None, :]
+    for w in (2, 7, 16):
+        band = (j <= i) & (i - j < w)
+        r1 = F.scaled_dot_product_attention(q1, k1, v, attn_mask=band).numpy()
+        r2 = F.scaled_dot_product_attention(q2, k2, v, attn_mask=band).numpy()
+        o = oracle.diff_attention(q1, k1, q2, k2, v, lam, True, window=w)
+        assert np.max(np.abs(o - (r1 - lam[None, :, None, None] * r2))) < 1e-12
+
+
 ALL_CHECKS = [
     check_worked_example, check_library_attention, check_cancellation, check_row_sums,
     check_value_offset, check_first_row, check_lambda, check_lambda_init, check_head_norm,
     check_brute_force, check_decode, check_standard_attention, check_backward_autograd,
     check_backward_finite_diff, check_backward_identities, check_lambda_backward,
-    check_v2_library, check_v2_decode,
+    check_v2_library, check_v2_decode, check_window,
 ]

@@ -24,7 +24,7 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert "diffattn_fwd_reparam" in names and "diffattn_attention_fwd" in names
     assert "diffattn_v2_fwd" in names and "diffattn_v2_decode" in names
     assert "diffattn_fwd_train" in names and "diffattn_bwd" in names
@@ -162,6 +162,22 @@ def test_decode_validation(L):
     assert dec(L, ws=P(8, 8)) == UNSUPPORTED
     # workspace overlapping the value cache
     assert dec(L, ws=P(4, 64)) == INVALID
+
+
+def fwin(L, dtype=BF16, window=4, ptrs=None, T=8, D=64):
+    p = ptrs or [P(i) for i in range(7)]
+    return L.diffattn_fwd_window(dtype, 1, 2, T, D, p[0], p[1], p[2], p[3], p[4], p[5], window, 0,
+                                 ctypes.c_float(0.8), ctypes.c_float(1e-5), p[6], None)
+
+
+def test_fwd_window_validation(L):
+    assert fwin(L, window=0) == INVALID
+    assert fwin(L, window=-3) == INVALID
+    assert fwin(L, dtype=F32) == UNSUPPORTED
+    assert fwin(L, D=96) == UNSUPPORTED
+    assert fwin(L, T=0) == INVALID
+    assert fwin(L, ptrs=[P(0), P(1), P(2), P(3), P(4), None, P(6)]) == INVALID     # lambda
+    assert fwin(L, ptrs=[P(0), P(1), P(2), P(3), P(4), P(5), P(4, 64)]) == INVALID  # out over v
 
 
 def v2f(L, dtype=BF16, B=1, H=4, Hkv=2, T=8, D=64, ptrs=None):

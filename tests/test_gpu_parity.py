@@ -383,3 +383,42 @@ def test_workload_decode_l64k():
     del x
     torch.cuda.empty_cache()
     assert worst <= TOL["bf16"]
+
+
+# ---- sliding window (causal): row i sees keys i - W < j <= i ------------------
+
+@pytest.mark.parametrize("headnorm", [False, True])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_fwd_window_sweep(D, headnorm):
+    lam = torch.tensor([0.6, -0.2], dtype=torch.float32)
+    for i, (T, W) in enumerate(((1, 1), (33, 1), (130, 5), (130, 32), (300, 64), (300, 100),
+                                (300, 299), (300, 300), (1000, 257))):
+        x = prefill_inputs(1, 2, T, D, "bf16", seed=7000 + D + 13 * i)
+        say(f"fwd window bf16 D={D} T={T} W={W} headnorm={headnorm}")
+        out = da.diffattn_fwd_window(*(to_dev(x)[k] for k in ("q1", "k1", "q2", "k2", "v")), lam.to(DEV), W,
+                                     headnorm=headnorm, lambda_init=0.8, eps=1e-5)
+        torch.cuda.synchronize()
+        ref = oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, True, window=W)
+        if headnorm:
+            ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+        err = maxerr(out, ref)
+        assert err <= TOL["bf16"], (T, W, err)
+
+
+def test_fwd_window_long_rows():
+    # rows longer than 4096 take the two-maps-per-wave configuration; short
+    # rows over many heads the 192-row one: sampled rows, every key in range
+    lam = torch.tensor([0.8, 0.3, -0.1, 1.1], dtype=torch.float32)
+    for (B, H, T, W, seed) in ((1, 2, 5000, 700, 41), (2, 4, 3000, 1024, 42)):
+        x = prefill_inputs(B, H, T, 64, "bf16", seed=seed)
+        say(f"fwd window bf16 D=64 B={B} H={H} T={T} W={W}")
+        lh = lam[:H]
+        out = da.diffattn_fwd_window(*(to_dev(x)[k] for k in ("q1", "k1", "q2", "k2", "v")), lh.to(DEV), W)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([np.arange(40), np.arange(T - 40, T), np.arange(W - 5, W + 5),
+                                         np.random.default_rng(seed).choice(T, 150, replace=False)]))
+        for b in range(B):
+            for h in range(H):
+                ref = oracle.diff_attention_rows(x["q1"][b, h], x["k1"][b, h], x["q2"][b, h], x["k2"][b, h],
+                                                 x["v"][b, h], float(lh[h]), True, rows, window=W)
+                assert maxerr(out[b, h, rows], ref) <= TOL["bf16"], (T, W, b, h)

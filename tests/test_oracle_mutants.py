@@ -19,12 +19,13 @@ _REAL_ATTENTION = od.attention  # the real functions, wrapped by mutants below
 _REAL_BACKWARD = od.diff_attention_backward
 _REAL_LAMBDA_BACKWARD = od.reparam_lambda_backward
 _REAL_V2 = od.diff_attention_v2
+_REAL_SCORES = od._scores
 _REAL_V2_DECODE = od.diff_attention_v2_decode
 
 
 
 def _make_scores(scale_fn=None, mask_fn=None, transpose=False):
-    def _scores(q, k, rows, causal):
+    def _scores(q, k, rows, causal, window=None):
         d = q.shape[-1]
         if rows is None:
             rows = np.arange(q.shape[0])
@@ -33,8 +34,15 @@ def _make_scores(scale_fn=None, mask_fn=None, transpose=False):
         if causal:
             keys = np.arange(k.shape[0])
             s = np.where(mask_fn(keys[None, :], rows[:, None]), -np.inf, s)
+            if window is not None:
+                s = np.where(rows[:, None] - keys[None, :] >= window, -np.inf, s)
         return s
     return _scores
+
+
+def _scores_window_off_by_one(q, k, rows, causal, window=None):
+    # window read as i - W <= j <= i (one key too many)
+    return _REAL_SCORES(q, k, rows, causal, None if window is None else window + 1)
 
 
 def _softmax_axis0(s):
@@ -48,27 +56,27 @@ def _softmax_no_norm(s):
     return np.exp(s - m)
 
 
-def _rows_branch1_mask_only(q1, k1, q2, k2, v, lam, causal, rows, row_block=512):
+def _rows_branch1_mask_only(q1, k1, q2, k2, v, lam, causal, rows, row_block=512, window=None):
     q1, k1, q2, k2, v = (od._f64(t) for t in (q1, k1, q2, k2, v))
     rows = np.asarray(rows)
-    a1 = od._softmax_rows(od._scores(q1, k1, rows, causal))
+    a1 = od._softmax_rows(od._scores(q1, k1, rows, causal, window))
     a2 = od._softmax_rows(od._scores(q2, k2, rows, False))
     return (a1 - float(lam) * a2) @ v
 
 
-def _rows_lam_on_a1(q1, k1, q2, k2, v, lam, causal, rows, row_block=512):
+def _rows_lam_on_a1(q1, k1, q2, k2, v, lam, causal, rows, row_block=512, window=None):
     q1, k1, q2, k2, v = (od._f64(t) for t in (q1, k1, q2, k2, v))
     rows = np.asarray(rows)
-    a1 = od._softmax_rows(od._scores(q1, k1, rows, causal))
-    a2 = od._softmax_rows(od._scores(q2, k2, rows, causal))
+    a1 = od._softmax_rows(od._scores(q1, k1, rows, causal, window))
+    a2 = od._softmax_rows(od._scores(q2, k2, rows, causal, window))
     return (float(lam) * a1 - a2) @ v
 
 
-def _rows_swapped_branches(q1, k1, q2, k2, v, lam, causal, rows, row_block=512):
+def _rows_swapped_branches(q1, k1, q2, k2, v, lam, causal, rows, row_block=512, window=None):
     q1, k1, q2, k2, v = (od._f64(t) for t in (q1, k1, q2, k2, v))
     rows = np.asarray(rows)
-    a1 = od._softmax_rows(od._scores(q1, k2, rows, causal))
-    a2 = od._softmax_rows(od._scores(q2, k1, rows, causal))
+    a1 = od._softmax_rows(od._scores(q1, k2, rows, causal, window))
+    a2 = od._softmax_rows(od._scores(q2, k1, rows, causal, window))
     return (a1 - float(lam) * a2) @ v
 
 
@@ -214,6 +222,7 @@ MUTANTS = {
     "lambda_bwd_own_vector": ("reparam_lambda_backward", _lambda_bwd_self),
     "lambda_bwd_second_sign": ("reparam_lambda_backward", _lambda_bwd_plus),
     "v2_group_modulo": ("diff_attention_v2", _v2_group_modulo),
+    "window_off_by_one": ("_scores", _scores_window_off_by_one),
     "v2_first_query_twice": ("diff_attention_v2", _v2_first_query_twice),
     "v2_decode_wrong_group": ("diff_attention_v2_decode", _v2_decode_wrong_group),
 }
