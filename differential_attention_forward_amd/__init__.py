@@ -25,6 +25,7 @@ __all__ = [
     "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
     "diffattn_fwd_reparam", "diffattn_fwd_window", "diffattn_attention_fwd",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
+    "diffattn_decode_ragged",
     "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_bwd_workspace_bytes",
     "diffattn_bwd", "diffattn_v2_fwd", "diffattn_v2_decode_workspace_bytes", "diffattn_v2_decode",
 ]
@@ -54,6 +55,8 @@ _SIGS = {
     "diffattn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "diffattn_decode": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F, _I,
                              _VP, ctypes.c_size_t, _VP, _VP]),
+    "diffattn_decode_ragged": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F,
+                                    _I, _VP, ctypes.c_size_t, _VP, _VP]),
     "diffattn_train_saved_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "diffattn_fwd_train": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
                                 _VP, _VP, ctypes.c_size_t, _VP]),
@@ -341,6 +344,33 @@ def diffattn_v2_decode(q1, q2, k, v, lam, num_splits: int = 0, workspace=None, o
                                     _ptr(v), _ptr(lamv), int(num_splits), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _ptr(out),
                                     _stream(stream)))
+    return out
+
+
+def diffattn_decode_ragged(q1, k1, q2, k2, v, lam, lengths, headnorm: bool = False,
+                           lambda_init: float = 0.8, eps: float = 1e-5, num_splits: int = 0,
+                           workspace=None, out=None, stream=None):
+    """Decode where sequence b sees only its first lengths[b] cache rows;
+    ``lengths``: [B] int32 device tensor (values in [0, L])."""
+    q1, k1, q2, k2, v = (_dev(t, n) for t, n in
+                         ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")))
+    b, h, l, d = k1.shape
+    if q1.shape != (b, h, d) or q2.shape != (b, h, d) or k2.shape != k1.shape or v.shape != (b, h, l, 2 * d):
+        raise ValueError("shapes: q* [B,H,D], k* [B,H,L,D], v [B,H,L,2D]")
+    lens = _dev(lengths, "lengths")
+    if lens.dtype != torch.int32 or lens.shape != (b,):
+        raise ValueError("lengths must be an int32 tensor of shape [B]")
+    lamv = _lambda_vec(lam, h, q1.device)
+    need = diffattn_decode_workspace_bytes(b, h, l, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, device=q1.device, dtype=torch.float32)
+    if out is None:
+        out = torch.empty((b, h, 2 * d), device=q1.device, dtype=q1.dtype)
+    _check(lib().diffattn_decode_ragged(_dtype_code(q1), b, h, l, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                                        _ptr(k2), _ptr(v), _ptr(lamv), _ptr(lens), int(bool(headnorm)),
+                                        float(lambda_init), float(eps), int(num_splits), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(out),
+                                        _stream(stream)))
     return out
 
 

@@ -388,11 +388,13 @@ size_t diffattn_decode_workspace_bytes(int B, int H, int L, int D, int num_split
   return (size_t)B * H * s * 2 * (2 * (size_t)D + 2) * sizeof(float);
 }
 
-diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const void* q1,
-                                const void* k1, const void* q2, const void* k2, const void* v,
-                                const float* lambda, int headnorm, float lambda_init, float eps,
-                                int num_splits, void* workspace, size_t workspace_bytes,
-                                void* out, hipStream_t stream) {
+namespace {
+
+diffattn_status decode_impl(int dtype, int B, int H, int L, int D, const void* q1, const void* k1,
+                            const void* q2, const void* k2, const void* v, const float* lambda,
+                            const int* lengths, int headnorm, float lambda_init, float eps,
+                            int num_splits, void* workspace, size_t workspace_bytes, void* out,
+                            hipStream_t stream) {
   if (!q1 || !k1 || !q2 || !k2 || !v || !lambda || !out) return DIFFATTN_ERR_INVALID;
   if (B < 1 || H < 1 || L < 1) return DIFFATTN_ERR_INVALID;
   if (headnorm && !(eps > 0.0f)) return DIFFATTN_ERR_INVALID;
@@ -421,8 +423,15 @@ diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const voi
   if (overlaps(out, nout, workspace, need) || overlaps(out, nout, lambda, (size_t)H * 4) ||
       overlaps(workspace, need, lambda, (size_t)H * 4))
     return DIFFATTN_ERR_INVALID;
+  if (lengths) {
+    if (!aligned(lengths, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+    const size_t nl = (size_t)B * sizeof(int);
+    if (overlaps(out, nout, lengths, nl) || overlaps(workspace, need, lengths, nl))
+      return DIFFATTN_ERR_INVALID;
+  }
 
   diffattn::DecodeArgs a;
+  a.lens = lengths;
   a.q1 = q1;
   a.k1 = k1;
   a.q2 = q2;
@@ -440,6 +449,28 @@ diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const voi
   a.out_scale = 1.0f - lambda_init;
   a.eps = eps;
   return from_hip(diffattn::launch_decode(a, dtype, D, headnorm != 0, stream));
+}
+
+}  // namespace
+
+diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const void* q1,
+                                const void* k1, const void* q2, const void* k2, const void* v,
+                                const float* lambda, int headnorm, float lambda_init, float eps,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                void* out, hipStream_t stream) {
+  return decode_impl(dtype, B, H, L, D, q1, k1, q2, k2, v, lambda, nullptr, headnorm, lambda_init,
+                     eps, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+diffattn_status diffattn_decode_ragged(int dtype, int B, int H, int L, int D, const void* q1,
+                                       const void* k1, const void* q2, const void* k2,
+                                       const void* v, const float* lambda, const int* lengths,
+                                       int headnorm, float lambda_init, float eps, int num_splits,
+                                       void* workspace, size_t workspace_bytes, void* out,
+                                       hipStream_t stream) {
+  if (!lengths) return DIFFATTN_ERR_INVALID;
+  return decode_impl(dtype, B, H, L, D, q1, k1, q2, k2, v, lambda, lengths, headnorm, lambda_init,
+                     eps, num_splits, workspace, workspace_bytes, out, stream);
 }
 
 // ---- DIFF V2: two query heads per differential head, K/V shared per group ----
@@ -523,6 +554,7 @@ diffattn_status diffattn_v2_decode(int dtype, int B, int H, int Hkv, int L, int 
       overlaps(workspace, need, lambda, (size_t)H * 4))
     return DIFFATTN_ERR_INVALID;
   diffattn::DecodeArgs a;
+  a.lens = nullptr;
   a.q1 = q1;
   a.k1 = k;
   a.q2 = q2;

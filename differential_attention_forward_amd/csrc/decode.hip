@@ -91,9 +91,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   const int split = blockIdx.x % S;
   const int bh = blockIdx.x / S;
   const int L = a.L;
-  const int chunk = (L + S - 1) / S;
-  const int kb = min(L, split * chunk);
-  const int ke = min(L, kb + chunk);
+  // ragged caches: sequence b uses its first lens[b] rows (clamped to [0, L])
+  const int Lb = a.lens ? min(max(a.lens[bh / a.H], 0), L) : L;
+  const int chunk = (Lb + S - 1) / S;
+  const int kb = min(Lb, split * chunk);
+  const int ke = min(Lb, kb + chunk);
 
   const E* __restrict__ K1 = (const E*)a.k1 + (size_t)bh * L * D;
   const E* __restrict__ K2 = (const E*)a.k2 + (size_t)bh * L * D;
@@ -302,8 +304,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     const float* r = rec + (size_t)s * RS;
     const float m1 = s < kMaxSplitsLds ? sm[0][s] : r[0];
     const float m2 = s < kMaxSplitsLds ? sm[1][s] : r[DV + 2];
-    const float f1 = __builtin_amdgcn_exp2f(m1 - M1);  // empty chunk: m = -inf -> 0
-    const float f2 = __builtin_amdgcn_exp2f(m2 - M2);
+    // empty chunk: m = -inf -> 0; no key at all (M = -inf): nothing to add
+    const float f1 = M1 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m1 - M1);
+    const float f2 = M2 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m2 - M2);
     L1 = fmaf(f1, r[1], L1);
     A1 = fmaf(f1, r[2 + c], A1);
     L2 = fmaf(f2, r[DV + 3], L2);
@@ -325,8 +328,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
       L2 += part[g][2][c];
       A2 += part[g][3][c];
     }
-    const float t1 = A1 * (1.0f / L1);
-    const float t2 = A2 * (1.0f / L2);
+    // a sequence with no cached row (length 0) gives a zero row
+    const float t1 = L1 > 0.0f ? A1 * (1.0f / L1) : 0.0f;
+    const float t2 = L2 > 0.0f ? A2 * (1.0f / L2) : 0.0f;
     const float lt2 = a.lam[bh % a.H] * t2;
     o = t1 - lt2;
   }

@@ -44,6 +44,7 @@ struct DecodeArgs {
   const float* lam;   // [H]
   float* ws;          // [B,H,S, 2*(2D+2)] fp32 partial states
   void* out;          // [B,H,2D]
+  const int* lens;    // [B] filled cache rows per sequence, or null (all L)
   int B, H, L, S;
   int Hkv;            // V2 only: KV heads; head h reads KV head h / (H / Hkv)
   float score_scale;

@@ -202,6 +202,26 @@ diffattn_status diffattn_decode(int dtype, int B, int H, int L, int D, const voi
                                 void* out, hipStream_t stream);
 
 /*
+ * Decode over caches filled to different lengths per sequence (a serving
+ * batch in which every sequence has its own context length): sequence b
+ * attends to its first lengths[b] cached rows only.
+ *
+ *   lengths   [B] int32, DEVICE memory, each in [0, L] (values outside are
+ *             clamped to that range, so no row past L is ever read); a length
+ *             of 0 gives a zero output row (no key to attend to)
+ *   other arguments as for diffattn_decode (L is the cache capacity, the
+ *   row stride of k1, k2, v)
+ * Errors: as diffattn_decode, plus ERR_INVALID for a null `lengths` or one
+ * overlapping the output or workspace, ERR_UNSUPPORTED for a misaligned one.
+ */
+diffattn_status diffattn_decode_ragged(int dtype, int B, int H, int L, int D, const void* q1,
+                                       const void* k1, const void* q2, const void* k2,
+                                       const void* v, const float* lambda, const int* lengths,
+                                       int headnorm, float lambda_init, float eps, int num_splits,
+                                       void* workspace, size_t workspace_bytes, void* out,
+                                       hipStream_t stream);
+
+/*
  * ---- DIFF V2 (the French lesson page "Attention différentielle (V2)",
  *      "V1 contre V2") ----
  *

@@ -10,6 +10,7 @@ from .diffattn_oracle import (  # noqa: F401
     diff_attention_backward,
     diff_attention_backward_dq_rows,
     diff_attention_decode,
+    diff_attention_decode_ragged,
     diff_attention_rows,
     diff_attention_v2,
     diff_attention_v2_decode,

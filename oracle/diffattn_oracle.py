@@ -78,6 +78,7 @@ __all__ = [
     "diff_attention_rows",
     "head_rmsnorm",
     "diff_attention_decode",
+    "diff_attention_decode_ragged",
     "attention",
     "diff_attention_v2",
     "diff_attention_v2_decode",
@@ -268,6 +269,29 @@ def diff_attention_decode(q1, k1, q2, k2, v, lam):
             out[bi, hi] = diff_attention_rows(
                 q1[bi, hi][None, :], k1s, q2[bi, hi][None, :], k2s, vs,
                 lam_h[hi], False, np.array([0]))[0]
+    return out
+
+
+def diff_attention_decode_ragged(q1, k1, q2, k2, v, lam, lengths):
+    """Decode against caches of different filled lengths per sequence.
+
+    Same as ``diff_attention_decode`` with sequence b seeing only its first
+    lengths[b] cached rows (the French page's serving setting: each sequence
+    in a decode batch has its own context length).  Reading taken: a length of
+    0 leaves no key to attend to and gives a zero output row.
+    q*: [B, H, D]; k*: [B, H, L, D]; v: [B, H, L, 2D]; lengths: [B] ints in
+    [0, L].  Returns [B, H, 2D] float64.
+    """
+    q1, q2 = _f64(q1), _f64(q2)
+    b, h, _ = q1.shape
+    lengths = [int(x) for x in np.asarray(lengths).reshape(-1)]
+    out = np.zeros((b, h, v.shape[-1]))
+    for bi in range(b):
+        n = lengths[bi]
+        if n <= 0:
+            continue
+        out[bi] = diff_attention_decode(q1[bi:bi + 1], _f64(k1[bi:bi + 1, :, :n]), q2[bi:bi + 1],
+                                        _f64(k2[bi:bi + 1, :, :n]), _f64(v[bi:bi + 1, :, :n]), lam)[0]
     return out
 
 

@@ -41,6 +41,8 @@ What pins what:
                    the row-wise dQ function equals the full backward's rows
   lambda grads     the four lambda-vector gradients against autograd and
                    central finite differences of the closed form
+  ragged decode    sequence b with n_b cached rows = the last row of a causal
+                   forward of length n_b; n_b = 0 gives zeros; n_b = L is decode
   sliding window   a window covering all keys is the causal mask; window 1
                    gives (1 - lam) V_i; torch SDPA with the explicit band mask
   DIFF V2          grouped-query form (shared K/V per group, V as wide as Q):
@@ -342,10 +344,35 @@ def check_window():
         assert np.max(np.abs(o - (r1 - lam[None, :, None, None] * r2))) < 1e-12
 
 
+def check_decode_ragged():
+    """Ragged decode: sequence b against its first n_b cached rows equals the
+    last row of a causal forward of length n_b whose final query is the decode
+    query (that row sees exactly those keys); n_b = 0 gives zeros; all n_b = L
+    is the plain decode."""
+    q1, k1, _, k2, v = _case(3, 2, 29, 8, seed=601)
+    lam = np.array([0.7, -0.2])
+    qd1, qd2 = _rand((3, 2, 8), 611), _rand((3, 2, 8), 612)
+    lengths = [17, 0, 29]
+    o = oracle.diff_attention_decode_ragged(qd1, k1, qd2, k2, v, lam, lengths)
+    assert np.all(o[1] == 0.0)
+    for b, n in enumerate(lengths):
+        if n == 0:
+            continue
+        qq1 = q1[b:b + 1, :, :n].clone()
+        qq2 = torch.zeros_like(qq1)
+        qq1[:, :, -1] = qd1[b]
+        qq2[:, :, -1] = qd2[b]
+        full = oracle.diff_attention(qq1, k1[b:b + 1, :, :n], qq2, k2[b:b + 1, :, :n], v[b:b + 1, :, :n],
+                                     lam, causal=True)
+        assert np.max(np.abs(o[b] - full[0, :, -1])) < 1e-13
+    plain = oracle.diff_attention_decode(qd1, k1, qd2, k2, v, lam)
+    assert np.max(np.abs(oracle.diff_attention_decode_ragged(qd1, k1, qd2, k2, v, lam, [29] * 3) - plain)) < 1e-15
+
+
 ALL_CHECKS = [
     check_worked_example, check_library_attention, check_cancellation, check_row_sums,
     check_value_offset, check_first_row, check_lambda, check_lambda_init, check_head_norm,
     check_brute_force, check_decode, check_standard_attention, check_backward_autograd,
     check_backward_finite_diff, check_backward_identities, check_lambda_backward,
-    check_v2_library, check_v2_decode, check_window,
+    check_v2_library, check_v2_decode, check_window, check_decode_ragged,
 ]

@@ -24,7 +24,7 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert "diffattn_fwd_reparam" in names and "diffattn_attention_fwd" in names
     assert "diffattn_v2_fwd" in names and "diffattn_v2_decode" in names
     assert "diffattn_fwd_train" in names and "diffattn_bwd" in names
@@ -218,6 +218,20 @@ def test_v2_decode_validation(L):
     assert v2d(L, splits=4, wsb=need - 1) == WORKSPACE
     assert v2d(L, ws=P(3, 64)) == INVALID                                # workspace over v
     assert da.diffattn_v2_decode_workspace_bytes(1, 4, 2, 0, 64) == 0
+
+
+def test_decode_ragged_validation(L):
+    p = [P(i) for i in range(7)]
+
+    def rag(lens, ws=None, wsb=1 << 20):
+        return L.diffattn_decode_ragged(BF16, 2, 2, 64, 64, p[0], p[1], p[2], p[3], p[4], p[5], lens, 0,
+                                        ctypes.c_float(0.8), ctypes.c_float(1e-5), 0,
+                                        ws if ws is not None else P(8), wsb, p[6], None)
+    assert rag(None) == INVALID
+    assert rag(P(9, 2)) == UNSUPPORTED           # misaligned lengths
+    assert rag(P(6, 4)) == INVALID               # lengths inside the output
+    assert rag(P(8, 16)) == INVALID              # lengths inside the workspace
+    assert rag(P(9), ws=ctypes.c_void_p(0)) == WORKSPACE
 
 
 def test_lambda_validation(L):

@@ -422,3 +422,35 @@ def test_fwd_window_long_rows():
                 ref = oracle.diff_attention_rows(x["q1"][b, h], x["k1"][b, h], x["q2"][b, h], x["k2"][b, h],
                                                  x["v"][b, h], float(lh[h]), True, rows, window=W)
                 assert maxerr(out[b, h, rows], ref) <= TOL["bf16"], (T, W, b, h)
+
+
+# ---- ragged decode: sequence b sees its first lengths[b] cache rows -----------
+
+@pytest.mark.parametrize("headnorm", [False, True])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_ragged(dtype, headnorm):
+    lam = torch.tensor([0.8, -0.3], dtype=torch.float32)
+    Lcap = 1500
+    x = decode_inputs(5, 2, Lcap, 64, dtype, seed=9100)
+    lengths = torch.tensor([0, 1, 777, 1500, 33], dtype=torch.int32)
+    xd = to_dev(x)
+    for splits in (0, 1, 7, 64):
+        say(f"decode ragged {dtype} headnorm={headnorm} splits={splits}")
+        out = da.diffattn_decode_ragged(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV),
+                                        lengths.to(DEV), headnorm=headnorm, lambda_init=0.8, eps=1e-5,
+                                        num_splits=splits)
+        torch.cuda.synchronize()
+        ref = oracle.diff_attention_decode_ragged(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam,
+                                                  lengths.numpy())
+        if headnorm:
+            ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+        assert torch.count_nonzero(out[0]).item() == 0          # length 0: zero row
+        assert maxerr(out, ref) <= TOL[dtype], splits
+    # every length equal to the capacity is the plain decode, bit for bit
+    full = torch.full((5,), Lcap, dtype=torch.int32, device=DEV)
+    a = da.diffattn_decode_ragged(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV), full,
+                                  headnorm=headnorm, num_splits=16)
+    b = da.diffattn_decode(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV),
+                           headnorm=headnorm, num_splits=16)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -20,6 +20,7 @@ _REAL_BACKWARD = od.diff_attention_backward
 _REAL_LAMBDA_BACKWARD = od.reparam_lambda_backward
 _REAL_V2 = od.diff_attention_v2
 _REAL_SCORES = od._scores
+_REAL_RAGGED = od.diff_attention_decode_ragged
 _REAL_V2_DECODE = od.diff_attention_v2_decode
 
 
@@ -43,6 +44,12 @@ def _make_scores(scale_fn=None, mask_fn=None, transpose=False):
 def _scores_window_off_by_one(q, k, rows, causal, window=None):
     # window read as i - W <= j <= i (one key too many)
     return _REAL_SCORES(q, k, rows, causal, None if window is None else window + 1)
+
+
+def _ragged_off_by_one(q1, k1, q2, k2, v, lam, lengths):
+    # one cached row too many per sequence (the row at position n_b)
+    lengths = [min(int(n) + 1, od._f64(k1).shape[2]) for n in lengths]
+    return _REAL_RAGGED(q1, k1, q2, k2, v, lam, lengths)
 
 
 def _softmax_axis0(s):
@@ -223,6 +230,7 @@ MUTANTS = {
     "lambda_bwd_second_sign": ("reparam_lambda_backward", _lambda_bwd_plus),
     "v2_group_modulo": ("diff_attention_v2", _v2_group_modulo),
     "window_off_by_one": ("_scores", _scores_window_off_by_one),
+    "ragged_off_by_one": ("diff_attention_decode_ragged", _ragged_off_by_one),
     "v2_first_query_twice": ("diff_attention_v2", _v2_first_query_twice),
     "v2_decode_wrong_group": ("diff_attention_v2_decode", _v2_decode_wrong_group),
 }
