@@ -213,7 +213,7 @@ def bench_workload(torch, da, name, steps, warmup):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"],
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm_gbs"], 4),
                 "traffic": measured_traffic("decode", name) if w.kind == "decode" else None,
-                "kernel": KERNEL_NAME["decode"] if w.kind == "decode" else "decode_v2_partial_kernel",
+                "kernel": KERNEL_NAME["decode"] if w.kind == "decode" else "decode_v2_mma_kernel",
                 "algorithmic_per_launch": work}
         unit = "GB/s"
     res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),

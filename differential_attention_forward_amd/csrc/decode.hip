@@ -552,11 +552,217 @@ __global__ __launch_bounds__(kThreads) void decode_v2_partial_kernel(DecodeArgs 
   }
 }
 
+// DIFF V2 decode partial on the matrix cores.  With G differential heads per
+// KV head there are NR = 2G query rows per cache row, and at D = 128 the
+// VALU form above needs more VALU time per key than HBM takes to deliver it.
+// Here the scores of all NR rows come from one MFMA chain S^T = K Q^T (keys x
+// query columns: column c < G is map 1 of head c, G <= c < 2G map 2 of head
+// c - G; the other columns hold zero queries and are dropped), and the
+// weighted sums from O^T = V^T P^T, exactly the prefill's formulation
+// (scores in base-2 units with the reference as the accumulator input, lazy
+// rescale).  Each wave streams its own 32-key blocks (blocks w, w + 4, ...)
+// through a private double-buffered LDS slot filled by global -> LDS DMA,
+// waits on its own loads only (no workgroup barrier in the loop), and the
+// four waves' states are merged at the end into one record per (head, map).
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_v2_mma_kernel(DecodeArgs a) {
+  constexpr int NR = 2 * G;
+  constexpr int KSTEPS = D / 16;
+  constexpr int CB = D / 32;
+  constexpr int KB = 32 * D * 2;      // bytes of one 32-key block of K (or V)
+  constexpr int CK = D / 8;           // 16-byte chunks per row
+  constexpr int RK = 64 / CK;         // rows per 1-KiB DMA segment
+  constexpr int NSEG = KB / 1024;     // segments per block, per tensor
+  constexpr int RS = 2 * (D + 2);
+  constexpr float kTauSum = 256.0f;   // rescale trigger (p <= 2^8)
+  static_assert(NR <= 32, "query columns");
+  __shared__ __attribute__((aligned(1024))) char smem[kWaves][2][2 * KB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = a.S;
+  const int split = blockIdx.x % S;
+  const int bg = blockIdx.x / S;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int head0 = b * a.H + g * G;
+  const int L = a.L;
+  const int chunk = (L + S - 1) / S;
+  const int kb = min(L, split * chunk);
+  const int ke = min(L, kb + chunk);
+  const int nblk = (ke - kb + 31) / 32;
+  const bf16* __restrict__ K = scalar_ptr((const bf16*)a.k1 + (size_t)bg * L * D);
+  const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + (size_t)bg * L * D);
+
+  // query fragments (B operand), scaled to base-2 units and rounded once
+  const float sc = a.score_scale;
+  bf16x8 qf[KSTEPS];
+  {
+    const bool ok = l32 < NR;
+    const bf16* src = (const bf16*)(l32 < G ? a.q1 : a.q2) + (size_t)(head0 + (ok ? l32 % G : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
+      raw = ok ? raw : u32x4{0u, 0u, 0u, 0u};
+      const bf16x8 q = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)q[e] * sc);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): q before the DMA starts
+
+  // DMA of block j (keys kb + 32 j ..) into buffer `buf` of this wave's slot;
+  // rows past the chunk end load row ke - 1 (in bounds) and are masked
+  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
+    const int key0 = kb + 32 * j;
+    char* sk = smem[wave][buf];
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg) {
+      const int r = sg * RK + lane / CK;
+      const uint32_t row = (uint32_t)min(key0 + r, ke - 1);
+      dma16(K, row * (D * 2) + (((lane % CK) ^ swz_k<D>(r)) << 4), sk + sg * 1024);
+      dma16(V, row * (D * 2) + (((lane % CK) ^ swz_v<D>(r)) << 4), sk + KB + sg * 1024);
+    }
+  };
+
+  floatx16 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = splat16(0.0f);
+  floatx16 negmu = splat16(0.0f);
+  float mu = 0.0f, lsum = 0.0f;
+  bool started = false;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  const int k_rd = l32 * (2 * D);
+  const int swk = swz_k<D>(l32);
+  const int vq = lane & 3, vkq = (lane >> 2) & 3;
+  const int v_row = 4 * hi + vkq;
+  const int v_chunk = 2 * ((lane >> 4) & 1) + (vq >> 1);
+  const int v_sw = swz_v<D>(vkq);
+  const int v_byte = (vq & 1) * 8;
+
+  if (wave < nblk) issue(wave, 0);
+  int buf = 0;
+  for (int j = wave; j < nblk; j += kWaves) {
+    const bool more = j + kWaves < nblk;
+    if (more) issue(j + kWaves, buf ^ 1);
+    asm volatile("" ::: "memory");
+    if (more) __builtin_amdgcn_s_waitcnt(((2 * NSEG) & 15) | ((((2 * NSEG) >> 4) & 3) << 14) | (7 << 4));
+    else __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0)
+    asm volatile("" ::: "memory");
+    const char* sk = smem[wave][buf];
+    const char* sv = sk + KB;
+
+    floatx16 s;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 kf = *(const bf16x8*)(sk + k_rd + (((2 * ks + hi) ^ swk) << 4));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? negmu : s, 0, 0, 0);
+    }
+    const int key0 = kb + 32 * j;
+    if (key0 + 32 > ke) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[r] = key >= ke ? kNegInf : s[r];
+      }
+    }
+    bf16x8 pk[2];
+    float bs = 0.0f;
+    auto expo = [&]() __attribute__((always_inline)) {
+      bs = 0.0f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pa = __builtin_amdgcn_exp2f(s[8 * kh + 2 * e]);
+          const float pb = __builtin_amdgcn_exp2f(s[8 * kh + 2 * e + 1]);
+          const bf16x2 pw = {(bf16)pa, (bf16)pb};
+          bs = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, bs, false);
+          pk[kh][2 * e] = pw[0];
+          pk[kh][2 * e + 1] = pw[1];
+        }
+    };
+    expo();
+    // lazy rescale as in the prefill: the wave's first block sets the
+    // reference to the exact column max; later only a partial sum above 2^8
+    if (__any(!started || bs > kTauSum)) {
+      float m = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
+      m = swap_halves_max(m);
+      const float delta = started ? fmaxf(m, 0.0f) : m;  // the first block always has a visible key
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      mu += delta;
+      lsum *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] -= delta;
+      negmu = splat16(-mu);
+      expo();
+    }
+    started = true;
+    lsum += bs;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char* base = sv + (16 * ks + v_row) * (2 * D) + (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * D)));
+        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[ks], acc[cb], 0, 0, 0);
+      }
+    buf ^= 1;
+  }
+
+  // ---- merge the four waves' states; one record per (head, map) -------------
+  const float ltot = swap_halves_sum(lsum);
+  if (!started) mu = kNegInf;  // a wave with no block contributes nothing
+  __syncthreads();              // every wave is done with its LDS slot
+  float* mw = (float*)&smem[0][0][0];  // [wave][column][D + 2]
+  if (l32 < NR) {
+    float* row = mw + (wave * NR + l32) * (D + 2);
+    if (hi == 0) {
+      row[0] = mu;
+      row[1] = ltot;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) row[2 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)] = acc[cb][r];
+  }
+  __syncthreads();
+  for (int i = tid; i < NR * D; i += kThreads) {
+    const int c = i / D, ch = i % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[(w * NR + c) * (D + 2)]);
+    float Lsum = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* row = mw + (w * NR + c) * (D + 2);
+      const float f = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(row[0] - M);
+      Lsum = fmaf(f, row[1], Lsum);
+      A = fmaf(f, row[2 + ch], A);
+    }
+    float* rec = a.ws + ((size_t)(head0 + c % G) * S + split) * RS + (c / G) * (D + 2);
+    rec[2 + ch] = A;
+    if (ch == 0) {
+      rec[0] = M;
+      rec[1] = Lsum;
+    }
+  }
+}
+
 template <int D, int G>
 hipError_t launch_v2_d(const DecodeArgs& a, hipStream_t stream) {
   const long nblk = (long)a.B * a.Hkv * a.S;
   if (nblk > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  decode_v2_partial_kernel<D, G><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
+  decode_v2_mma_kernel<D, G><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_reduce_kernel<D, false, false><<<dim3((unsigned)(a.B * a.H)), dim3(256), 0, stream>>>(a);

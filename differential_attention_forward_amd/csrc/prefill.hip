@@ -466,25 +466,6 @@ struct CfgB {
   static_assert(SMEM <= 160 * 1024, "LDS budget exceeded");
 };
 
-// 16-byte column swizzles.  gfx950's LDS has 64 banks of 4 bytes (256 bytes
-// per clock): a ds_read_b128 serves 16 lanes per cycle and a
-// ds_read_b64_tr_b16 32 lanes, so those lanes must cover 256 distinct bytes
-// modulo 256.
-//  K (row pitch 2D bytes): lanes 0..15 read rows r..r+15 at one logical
-//  chunk; the swizzle makes (row mod (256 / pitch), physical chunk) distinct
-//  over those 16 rows.
-//  V (row pitch 2 DV bytes): the 32 lanes of a transposing read cover four
-//  rows (keys) and one 64-byte group of four chunks per row; the swizzle
-//  moves each of the four rows to its own 64-byte quarter of the banks.
-template <int D>
-__device__ inline int swz_k(int row) {
-  return D == 32 ? ((row >> 2) & 3) : D == 64 ? ((row >> 1) & 7) : (row & 15);
-}
-template <int DV>
-__device__ inline int swz_v(int row) {
-  return DV >= 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
-}
-
 template <int D, int NQB, int NW, int NSTAGE, bool SPLIT, bool CAUSAL, bool HEADNORM, int MAPS = 2,
           bool SHKV = false, bool WIN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 ? 2 : NW / 4, NW < 8 ? 2 : NW / 4))) void fwd_bf16_kernel(FwdArgs a) {
