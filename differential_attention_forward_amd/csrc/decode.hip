@@ -360,201 +360,11 @@ hipError_t launch_d(const DecodeArgs& a, bool headnorm, hipStream_t stream) {
 // DIFF V2 decode partial (the French lesson page, "V1 contre V2": the two
 // queries of a differential head read one shared K/V cache, so the cache is
 // read once per step and the arithmetic per cache byte rises).  One workgroup
-// per (b, KV head g, split) serves all G differential heads of the group: NR =
-// 2G query rows (q1 and q2 of each head) against one read of the chunk's K
-// and V rows.  Same sub-chunk structure as decode_partial_kernel; the records
-// it writes have the first version's layout with value width D, one per
-// (b, head, split), so decode_reduce_kernel<D> finishes them.
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_v2_partial_kernel(DecodeArgs a) {
-  constexpr int NR = 2 * G;           // query rows: row 2j + m is map m of head j
-  constexpr int EPC = 8;              // bf16 elements per 16-byte chunk
-  constexpr int LPK = D / EPC;        // lanes per K row
-  constexpr int KPR = kThreads / LPK; // key rows per pass (score phase)
-  constexpr int LPV = D / EPC;        // lanes per V row
-  constexpr int VPR = kThreads / LPV; // V rows per pass
-  constexpr int RS = 2 * (D + 2);     // floats per (b, head, split) record
-  static_assert(LPK <= 64, "row must fit in one wave");
-
-  __shared__ float sp[kSub][NR];      // per key and row: score, then probability
-  __shared__ float red[kWaves][NR];
-  __shared__ float accred[kWaves][NR][D];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int S = a.S;
-  const int split = blockIdx.x % S;
-  const int bg = blockIdx.x / S;       // b * Hkv + g
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int head0 = b * a.H + g * G;   // first (b, head) index of the group
-  const int L = a.L;
-  const int chunk = (L + S - 1) / S;
-  const int kb = min(L, split * chunk);
-  const int ke = min(L, kb + chunk);
-
-  const bf16* __restrict__ K = (const bf16*)a.k1 + (size_t)bg * L * D;
-  const bf16* __restrict__ V = (const bf16*)a.v + (size_t)bg * L * D;
-  const float sc = a.score_scale;
-
-  const int ksub = tid % LPK;
-  float qf[NR][EPC];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const bf16* qp = (const bf16*)(r & 1 ? a.q2 : a.q1) + (size_t)(head0 + r / 2) * D + ksub * EPC;
-    unpack16<false>(*(const u32x4*)qp, qf[r]);
-  }
-  const int vsub = tid % LPV;
-
-  float m[NR], l[NR], acc[NR][EPC];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    m[r] = kNegInf;
-    l[r] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[r][e] = 0.0f;
-  }
-
-  for (int base = kb; base < ke; base += kSub) {
-    const int n = min(kSub, ke - base);
-
-    // ---- scores of every query row against each key, one read per key ----------
-    for (int k0 = tid / LPK; k0 < n; k0 += KPR * kUnroll) {
-      u32x4 w[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int kk = min(k0 + u * KPR, n - 1);  // clamped: always in bounds
-        w[u] = __builtin_nontemporal_load((const u32x4*)(K + (size_t)(base + kk) * D + ksub * EPC));
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float kf[EPC];
-        unpack16<false>(w[u], kf);
-        float d[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          d[r] = 0.0f;
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) d[r] = fmaf(qf[r][e], kf[e], d[r]);
-#pragma unroll
-          for (int o = 1; o < LPK; o <<= 1) d[r] += __shfl_xor(d[r], o);
-        }
-        const int kk = k0 + u * KPR;
-        if (ksub == 0 && kk < n) {
-#pragma unroll
-          for (int r = 0; r < NR; ++r) sp[kk][r] = d[r] * sc;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- block max per row, rescale the running state ---------------------------
-    float bm[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) bm[r] = kNegInf;
-    for (int kk = tid; kk < n; kk += kThreads) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) bm[r] = fmaxf(bm[r], sp[kk][r]);
-    }
-#pragma unroll
-    for (int r = 0; r < NR; ++r) bm[r] = wave_max(bm[r]);
-    if (lane == 0) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) red[wave][r] = bm[r];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      float mx = red[0][r];
-#pragma unroll
-      for (int wv = 1; wv < kWaves; ++wv) mx = fmaxf(mx, red[wv][r]);
-      const float nm = fmaxf(m[r], mx);
-      const float al = __builtin_amdgcn_exp2f(m[r] - nm);  // m = -inf -> 0
-      m[r] = nm;
-      l[r] *= al;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[r][e] *= al;
-    }
-    for (int kk = tid; kk < n; kk += kThreads) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sp[kk][r] - m[r]);
-        l[r] += p;
-        sp[kk][r] = p;
-      }
-    }
-    __syncthreads();
-
-    // ---- V pass: every row's weighted sum from one read of each V row ------------
-    for (int k0 = tid / LPV; k0 < n; k0 += VPR * kUnroll) {
-      u32x4 wv[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int kk = min(k0 + u * VPR, n - 1);
-        wv[u] = __builtin_nontemporal_load((const u32x4*)(V + (size_t)(base + kk) * D + vsub * EPC));
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int kk = k0 + u * VPR;
-        if (kk < n) {
-          float vf[EPC];
-          unpack16<false>(wv[u], vf);
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const float p = sp[kk][r];
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[r][e] = fmaf(p, vf[e], acc[r][e]);
-          }
-        }
-      }
-    }
-    __syncthreads();  // sp and red are rewritten by the next sub-chunk
-  }
-
-  // ---- reduce the per-thread shares and write one record per (head, split) -------
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    l[r] = wave_sum(l[r]);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-#pragma unroll
-      for (int o = LPV; o < 64; o <<= 1) acc[r][e] += __shfl_xor(acc[r][e], o);
-    }
-  }
-  if (lane < LPV) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) accred[wave][r][vsub * EPC + e] = acc[r][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) red[wave][r] = l[r];
-  }
-  __syncthreads();
-  for (int i = tid; i < NR * D; i += kThreads) {
-    const int r = i / D, c = i % D;
-    float t = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) t += accred[wv][r][c];
-    a.ws[((size_t)(head0 + r / 2) * S + split) * RS + (r & 1) * (D + 2) + 2 + c] = t;
-  }
-  if (tid < NR) {
-    float t = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) t += red[wv][tid];
-    float* rec = a.ws + ((size_t)(head0 + tid / 2) * S + split) * RS + (tid & 1) * (D + 2);
-    // each thread's own m is the row's block-wide running max (same in every thread)
-    float mrow = m[0];
-#pragma unroll
-    for (int r = 1; r < NR; ++r) mrow = r == tid ? m[r] : mrow;
-    rec[0] = mrow;
-    rec[1] = t;
-  }
-}
-
-// DIFF V2 decode partial on the matrix cores.  With G differential heads per
-// KV head there are NR = 2G query rows per cache row, and at D = 128 the
-// VALU form above needs more VALU time per key than HBM takes to deliver it.
+// per (b, KV head g, split) serves all G differential heads of the group; the
+// records it writes have the first version's layout with value width D, one
+// per (b, head, split), so decode_reduce_kernel<D> finishes them.  With NR =
+// 2G query rows per cache row a VALU form needs more VALU time per key than
+// HBM takes to deliver it at D = 128, so this runs on the matrix cores.
 // Here the scores of all NR rows come from one MFMA chain S^T = K Q^T (keys x
 // query columns: column c < G is map 1 of head c, G <= c < 2G map 2 of head
 // c - G; the other columns hold zero queries and are dropped), and the
