@@ -42,8 +42,9 @@ PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0
 PRIMARY = "prefill_t4k_causal"
 OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k", "v2_prefill_t4k", "v2_decode_l64k"]
 CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
-KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip"}
-KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel"}
+KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip", "v2_decode": "decode.hip"}
+KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel",
+               "v2_decode": "decode_v2_mma_kernel"}
 
 
 def log(*a):
@@ -212,8 +213,7 @@ def bench_workload(torch, da, name, steps, warmup):
         achieved = work / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"],
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm_gbs"], 4),
-                "traffic": measured_traffic("decode", name) if w.kind == "decode" else None,
-                "kernel": KERNEL_NAME["decode"] if w.kind == "decode" else "decode_v2_mma_kernel",
+                "traffic": measured_traffic(w.kind, name), "kernel": KERNEL_NAME[w.kind],
                 "algorithmic_per_launch": work}
         unit = "GB/s"
     res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
