@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 METRIC = "DiffAttn fwd TFLOP/s (bf16 causal T=4k/32k) & % MFMA peak; decode HBM GB/s"
 PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
 PRIMARY = "prefill_t4k_causal"
-OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k", "v2_prefill_t4k", "v2_decode_l64k"]
+OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k", "v2_prefill_t4k", "v2_decode_l64k",
+          "bwd_t4k_causal", "prefill_t32k_window4k", "decode_ragged_l64k"]
 CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
 KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip", "v2_decode": "decode.hip"}
 KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel",
@@ -72,22 +73,34 @@ def measured_traffic(kind, workload):
     return rec.get("bytes_per_launch")
 
 
+def visible_pairs(w):
+    """(query, key) pairs a head's mask allows: T^2 full, T(T+1)/2 causal,
+    sum_i min(i + 1, W) with a sliding window W."""
+    if w.window and w.window < w.T:
+        wn = w.window
+        return wn * (wn + 1) / 2.0 + (w.T - wn) * float(wn)
+    return w.T * (w.T + 1) / 2.0 if w.causal else float(w.T) * w.T
+
+
 def prefill_flops(w):
     """Per visible (query, key) pair and head: two D-wide score dot products
     and one signed weighted sum over the value row (2D wide in the first
-    version, D wide in V2), 2 flops per multiply-add."""
-    t_eff = (w.T + 1) / 2.0 if w.causal else float(w.T)
-    per_pair = 6.0 * w.D if w.kind == "v2_prefill" else 8.0 * w.D
-    return per_pair * t_eff * w.T * w.B * w.H
+    version, D wide in V2), 2 flops per multiply-add.  Backward: the two
+    score recomputations (4D), dP = dOpre V^T (4D), dV from the signed map
+    (4D), dQ1 and dQ2 (4D), dK1 and dK2 (4D): 20 D per pair."""
+    per_pair = {"v2_prefill": 6.0, "bwd": 20.0}.get(w.kind, 8.0) * w.D
+    return per_pair * visible_pairs(w) * w.B * w.H
 
 
-def decode_bytes(w):
+def decode_bytes(w, lengths=None):
     """Cache bytes one step must read: K1, K2 (D) and V (2D) per key and head;
-    V2: one K and one V (D each) per key and KV head."""
+    V2: one K and one V (D each) per key and KV head; ragged: the filled rows
+    of each sequence only."""
     es = 2 if w.dtype == "bf16" else 4
     if w.kind == "v2_decode":
         return float(w.B * w.Hkv * w.T * 2 * w.D * es)
-    return float(w.B * w.H * w.T * 4 * w.D * es)
+    keys = float(sum(int(n) for n in lengths)) if lengths is not None else float(w.B * w.T)
+    return keys * w.H * 4 * w.D * es
 
 
 SETTLE_S = 0.4
@@ -149,7 +162,31 @@ def bench_workload(torch, da, name, steps, warmup):
         da.diffattn_lambda_init(w.layer) if w.layer else 0.0)  # V2 has no lambda_init-scaled norm
     lam = x.get("lam")
     lam_buf = torch.empty(w.H, device="cuda", dtype=torch.float32)
-    if w.kind == "v2_prefill":
+    if w.kind == "bwd":
+        lamv, out = x["lam"], None
+        _, saved = da.diffattn_fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lamv, causal=w.causal,
+                                         headnorm=w.headnorm, lambda_init=li, eps=w.eps)
+        ws = torch.empty(max(da.diffattn_bwd_workspace_bytes(w.B, w.H, w.T, w.D), 16), device="cuda",
+                         dtype=torch.uint8)
+
+        def kernel():
+            da.diffattn_bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lamv, x["dout"], saved,
+                            causal=w.causal, headnorm=w.headnorm, lambda_init=li, eps=w.eps, workspace=ws)
+    elif w.kind == "window_prefill":
+        out = torch.empty_like(x["v"])
+
+        def kernel():
+            da.diffattn_fwd_window(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, w.window,
+                                   headnorm=w.headnorm, lambda_init=li, eps=w.eps, out=out)
+    elif w.kind == "ragged_decode":
+        out = torch.empty((w.B, w.H, 2 * w.D), device="cuda", dtype=x["v"].dtype)
+        ws = torch.empty(da.diffattn_decode_workspace_bytes(w.B, w.H, w.T, w.D, w.num_splits) // 4,
+                         device="cuda", dtype=torch.float32)
+
+        def kernel():
+            da.diffattn_decode_ragged(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_buf, x["lengths"],
+                                      num_splits=w.num_splits, workspace=ws, out=out)
+    elif w.kind == "v2_prefill":
         out = torch.empty_like(x["q1"])
 
         def kernel():
@@ -188,7 +225,7 @@ def bench_workload(torch, da, name, steps, warmup):
                                workspace=ws, out=out)
 
     def step():
-        if lam is None and w.kind == "decode":
+        if lam is None and w.kind in ("decode", "ragged_decode"):
             da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], li, out=lam_buf)
         kernel()
 
@@ -196,7 +233,7 @@ def bench_workload(torch, da, name, steps, warmup):
     ms, wall = time_steps(torch, step, steps, warmup)
     kern_ms = time_kernel(torch, kernel, steps)
     log(f"[bench] {name}: {ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
-    if w.kind in ("prefill", "v2_prefill"):
+    if w.kind in ("prefill", "v2_prefill", "bwd", "window_prefill"):
         work = prefill_flops(w)
         value = work / (ms * 1e-3) / 1e12
         achieved = work / (kern_ms * 1e-3) / 1e12
@@ -204,23 +241,25 @@ def bench_workload(torch, da, name, steps, warmup):
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic("prefill", name) if w.kind == "prefill" else None,
-                "kernel": KERNEL_NAME["prefill"],
+                "kernel": "bwd_prep + bwd_kv + bwd_q + bwd_lambda kernels" if w.kind == "bwd" else KERNEL_NAME["prefill"],
                 "algorithmic_per_launch": work}
         unit = "TFLOP/s"
     else:
-        work = decode_bytes(w)
+        work = decode_bytes(w, x["lengths"].tolist() if "lengths" in x else None)
         value = work / (ms * 1e-3) / 1e9
         achieved = work / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"],
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm_gbs"], 4),
-                "traffic": measured_traffic(w.kind, name), "kernel": KERNEL_NAME[w.kind],
+                "traffic": measured_traffic(w.kind, name) if w.kind in KERNEL_NAME else None,
+                "kernel": KERNEL_NAME.get(w.kind, KERNEL_NAME["decode"]),
                 "algorithmic_per_launch": work}
         unit = "GB/s"
     res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
            "kernel_ms": round(kern_ms, 5), "wall_s": round(wall, 4), "roofline": roof,
-           "shape": {"B": w.B, "H": w.H, ("T" if w.kind.endswith("prefill") else "L"): w.T, "D": w.D,
-                     "causal": w.causal if w.kind.endswith("prefill") else False,
-                     "headnorm": w.headnorm, "dtype": w.dtype, **({"Hkv": w.Hkv} if w.Hkv else {})}}
+           "shape": {"B": w.B, "H": w.H, ("L" if w.kind.endswith("decode") else "T"): w.T, "D": w.D,
+                     "causal": False if w.kind.endswith("decode") else w.causal,
+                     "headnorm": w.headnorm, "dtype": w.dtype, **({"Hkv": w.Hkv} if w.Hkv else {}),
+                     **({"window": w.window} if w.window else {})}}
     del x, out
     torch.cuda.empty_cache()
     return res

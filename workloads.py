@@ -42,6 +42,18 @@ DIFF V2 workloads (the French lesson page, "V1 contre V2" and its exercise of
                             decode_l64k has per head)
 
 V2 draw order: Q1, Q2, K, V (caches one batch row at a time), then lambda.
+
+Workloads of the other rows next to the forward (measured, not part of the
+problem statement's configurations):
+
+  bwd_t4k_causal            backward of prefill_t4k_causal's shape (B2 H16
+                            T4096 D64 causal bf16, head norm, lambda_init 0.8),
+                            seed 8, lambda_h ~ U[0.2, 0.8], dL/dOut ~ N(0,1)
+  prefill_t32k_window4k     B1 H16 T32768 D64 causal bf16 with a 4096-key
+                            sliding window, seed 9, lambda = 0.8
+  decode_ragged_l64k        decode_l64k's shape with per-sequence lengths
+                            uniform in [1, 65536] (CPU generator, seed 11),
+                            seed 10, lambda = lambda_init(24) = zero vectors
 """
 
 from __future__ import annotations
@@ -78,6 +90,7 @@ class Workload:
     value_offset: bool = False
     num_splits: int = 0
     Hkv: int = 0              # DIFF V2: KV heads (0 = the first version)
+    window: int = 0           # causal sliding window (0 = none)
     extra: dict = field(default_factory=dict)
 
 
@@ -98,6 +111,12 @@ WORKLOADS = {
                  lam_uniform=(0.2, 0.8), Hkv=4),
         Workload("v2_decode_l64k", "v2_decode", 32, 32, 65536, 128, "bf16", 7,
                  lam_uniform=(0.2, 0.8), Hkv=8),
+        Workload("bwd_t4k_causal", "bwd", 2, 16, 4096, 64, "bf16", 8, causal=True,
+                 headnorm=True, lambda_init=0.8, lam_uniform=(0.2, 0.8)),
+        Workload("prefill_t32k_window4k", "window_prefill", 1, 16, 32768, 64, "bf16", 9,
+                 causal=True, lam_fixed=0.8, lambda_init=0.8, window=4096),
+        Workload("decode_ragged_l64k", "ragged_decode", 32, 16, 65536, 64, "bf16", 10,
+                 layer=24, lambda_dl=64, lambda_zero=True, num_splits=64),
     ]
 }
 
@@ -236,9 +255,27 @@ def v2_inputs(B, H, Hkv, T, D, dtype="bf16", seed=0, device="cpu", *, decode=Fal
     return out
 
 
+def ragged_lengths(B, L, seed):
+    """Per-sequence cache lengths uniform in [1, L] (CPU generator), int32."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    return torch.randint(1, L + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
 def make_workload(name: str, device="cpu"):
     """Inputs of a named workload, drawn on ``device`` with its recipe."""
     w = WORKLOADS[name]
+    if w.kind == "bwd":
+        x = prefill_inputs(w.B, w.H, w.T, w.D, w.dtype, w.seed, device, lam_uniform=w.lam_uniform)
+        x["dout"] = grad_output(x["v"].shape, seed=w.seed + 100, device=device, dtype=w.dtype)
+        return x
+    if w.kind == "window_prefill":
+        return prefill_inputs(w.B, w.H, w.T, w.D, w.dtype, w.seed, device, lam_fixed=w.lam_fixed)
+    if w.kind == "ragged_decode":
+        x = decode_inputs(w.B, w.H, w.T, w.D, w.dtype, w.seed, device, lambda_dl=w.lambda_dl,
+                          lambda_zero=w.lambda_zero)
+        x["lengths"] = ragged_lengths(w.B, w.T, w.seed + 1).to(device)
+        return x
     if w.kind in ("v2_prefill", "v2_decode"):
         return v2_inputs(w.B, w.H, w.Hkv, w.T, w.D, w.dtype, w.seed, device,
                          decode=w.kind == "v2_decode", lam_uniform=w.lam_uniform)
