@@ -15,11 +15,19 @@
 // The maps are never stored: A1, A2 are recomputed tile by tile from the
 // scores and the per-row log-sum-exp the training forward saved.
 //
+// Scores are formed in base-2 units as in the forward (one operand pre-scaled
+// by log2(e)/sqrt(D) and rounded to bf16), and the per-row statistics are
+// kept negated, [-lse1, -lse2, -D1, -(lam D1 + D2)], so that they enter the
+// score and dP products as the MFMA accumulator input: the products come out
+// as s - lse and dP - D1, and per element only
+//   p1 = 2^s1', p2 = 2^s2', dS1 = p1 dP', dS2 = p2 (-lam dP' - (lam D1 + D2))
+// remain (dP' = dP - D1).
+//
 // Kernels (in launch order):
 //  * prep: one pass over rows (HBM bound).  Head-norm vector-Jacobian product
-//    (if enabled) -> dOpre in bf16, D1 and D2 from the rounded dOpre, and a
-//    per-chunk partial of dlam from the fp32 dOpre (no atomics: summed later
-//    in a fixed order).
+//    (if enabled) -> dOpre in bf16, D1 and D2 from the rounded dOpre (stored
+//    negated as above), and a per-chunk partial of dlam from the fp32 dOpre
+//    (no atomics: summed later in a fixed order).
 //  * kv: one workgroup per block of keys, one wave per 32 keys, looping over
 //    query tiles staged in LDS.  Scores are computed as S = Q K^T so that a
 //    lane owns one key and sees 16 queries: the probabilities and dS are then
@@ -47,6 +55,16 @@ namespace {
 // first) of 4 consecutive rows starting at a multiple of 4 -> 8 distinct.
 __device__ inline int swz2(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
+// Eight bf16 values times c, each product rounded once to bf16 (the forward
+// forms its base-2 scores from operands rounded the same way).
+__device__ inline bf16x8 scaled8(u32x4 raw, float c) {
+  const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (bf16)((float)x[e] * c);
+  return y;
+}
+
 // ============================================================================
 // prep
 // ============================================================================
@@ -72,12 +90,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   bf16* __restrict__ dop = (bf16*)a.dopre + v_off;
   float* __restrict__ st = a.stats + (size_t)bh * 4 * a.Tp;
   float part = 0.0f;
-  // log-sum-exp of both maps into the padded statistics block (padding: 0,
-  // only ever read for masked queries)
+  // negated log-sum-exp of both maps into the padded statistics block
+  // (padding: 0, only ever read for masked queries)
   if (tid < 2 * kPrepRows) {
     const int br = tid / kPrepRows;
     const int q = chunk * kPrepRows + tid % kPrepRows;
-    st[(size_t)br * a.Tp + q] = q < T ? a.lse[((size_t)bh * 2 + br) * T + q] : 0.0f;
+    st[(size_t)br * a.Tp + q] = q < T ? -a.lse[((size_t)bh * 2 + br) * T + q] : 0.0f;
   }
   for (int r0 = 0; r0 < kPrepRows; r0 += RPP) {
     const int q = chunk * kPrepRows + r0 + tid / TPR;
@@ -149,8 +167,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
       dl += __shfl_xor(dl, o);
     }
     if (sub == 0) {
-      st[(size_t)2 * a.Tp + q] = d1;
-      st[(size_t)3 * a.Tp + q] = -lam * d2;
+      // -D1 and -(lam D1 + D2) with D2 = -lam rowsum(dOpre O2)
+      st[(size_t)2 * a.Tp + q] = -d1;
+      st[(size_t)3 * a.Tp + q] = lam * (d2 - d1);
       part += dl;
     }
   }
@@ -254,7 +273,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const float sc = a.score_scale;
   const float lam = a.lam[h];
 
-  // ---- K1, K2, V rows of the lane's key (B operands), clamped in bounds -----
+  // ---- K1, K2, V rows of the lane's key (B operands), clamped in bounds; ----
+  // K pre-scaled to base-2 score units
   bf16x8 kf[2][C::KSTEPS];
   bf16x8 vf[C::VSTEPS];
   {
@@ -264,8 +284,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const bf16* vv = (const bf16*)a.v + v_off + kr * DV;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      kf[0][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k1 + ks * 16 + hi * 8));
-      kf[1][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k2 + ks * 16 + hi * 8));
+      kf[0][ks] = scaled8(*(const u32x4*)(k1 + ks * 16 + hi * 8), sc);
+      kf[1][ks] = scaled8(*(const u32x4*)(k2 + ks * 16 + hi * 8), sc);
     }
 #pragma unroll
     for (int ks = 0; ks < C::VSTEPS; ++ks)
@@ -348,14 +368,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const char* tq2 = sb + C::QBYTES;
     const char* tdo = sb + 2 * C::QBYTES;
     const float* tst = (const float*)(sb + C::SOFF) + 32 * sub;
+    // accumulator inputs: -lse1, -lse2, -D1 of each row; e2 = -(lam D1 + D2)
     floatx16 s1, s2, dp;
+    floatx4 e2[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s1[r] = 0.0f;
-      s2[r] = 0.0f;
-      dp[r] = 0.0f;
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 l1 = *(const floatx4*)(tst + 8 * g + 4 * hi);
+      const floatx4 l2 = *(const floatx4*)(tst + BQ + 8 * g + 4 * hi);
+      const floatx4 e1 = *(const floatx4*)(tst + 2 * BQ + 8 * g + 4 * hi);
+      e2[g] = *(const floatx4*)(tst + 3 * BQ + 8 * g + 4 * hi);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s1[4 * g + i] = l1[i];
+        s2[4 * g + i] = l2[i];
+        dp[4 * g + i] = e1[i];
+      }
     }
-    // S = Q K^T (rows: queries, lane column: key) for both maps
+    // S - lse = Q K^T - lse (rows: queries, lane column: key) for both maps
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const int off = (32 * sub + l32) * (2 * D) + (((2 * ks + hi) ^ sw_row) << 4);
@@ -364,7 +393,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kf[0][ks], s1, 0, 0, 0);
       s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, kf[1][ks], s2, 0, 0, 0);
     }
-    // dP = dOpre V^T
+    // dP - D1 = dOpre V^T - D1
 #pragma unroll
     for (int ks = 0; ks < C::VSTEPS; ++ks) {
       const bf16x8 ao = *(const bf16x8*)(tdo + (32 * sub + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_row) << 4));
@@ -386,17 +415,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     bf16x8 pc[2], g1[2], g2[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const floatx4 l1 = *(const floatx4*)(tst + 8 * g + 4 * hi);
-      const floatx4 l2 = *(const floatx4*)(tst + BQ + 8 * g + 4 * hi);
-      const floatx4 e1 = *(const floatx4*)(tst + 2 * BQ + 8 * g + 4 * hi);
-      const floatx4 e2 = *(const floatx4*)(tst + 3 * BQ + 8 * g + 4 * hi);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], sc, -l1[i]));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(s2[r], sc, -l2[i]));
-        const float d1 = p1 * (dp[r] - e1[i]);
-        const float d2 = p2 * fmaf(-lam, dp[r], -e2[i]);
+        const float p1 = __builtin_amdgcn_exp2f(s1[r]);
+        const float p2 = __builtin_amdgcn_exp2f(s2[r]);
+        const float d1 = p1 * dp[r];
+        const float d2 = p2 * fmaf(-lam, dp[r], e2[g][i]);
         const float c = fmaf(-lam, p2, p1);
         pc[r >> 3][r & 7] = (bf16)c;
         g1[r >> 3][r & 7] = (bf16)d1;
@@ -531,10 +556,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const float sc = a.score_scale;
   const float lam = a.lam[h];
 
-  // ---- the lane's query: Q1, Q2, dOpre rows (B operands) and statistics -----
+  // ---- the lane's query: Q1, Q2 (pre-scaled to base-2 score units), dOpre --
+  // ---- rows (B operands) and its negated statistics ------------------------
   bf16x8 qf[2][C::KSTEPS];
   bf16x8 df[C::VSTEPS];
-  float lse1, lse2, e1, e2;
+  float nl1, nl2, ne1, e2;  // -lse1, -lse2, -D1, -(lam D1 + D2)
   {
     const size_t qr = (size_t)min(query, T - 1);
     const bf16* q1 = (const bf16*)a.q1 + qk_off + qr * D;
@@ -542,16 +568,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const bf16* go = (const bf16*)a.dopre + v_off + qr * DV;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      qf[0][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q1 + ks * 16 + hi * 8));
-      qf[1][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q2 + ks * 16 + hi * 8));
+      qf[0][ks] = scaled8(*(const u32x4*)(q1 + ks * 16 + hi * 8), sc);
+      qf[1][ks] = scaled8(*(const u32x4*)(q2 + ks * 16 + hi * 8), sc);
     }
 #pragma unroll
     for (int ks = 0; ks < C::VSTEPS; ++ks)
       df[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(go + ks * 16 + hi * 8));
     const float* st = a.stats + (size_t)bh * 4 * a.Tp + qr;
-    lse1 = st[0];
-    lse2 = st[a.Tp];
-    e1 = st[2 * (size_t)a.Tp];
+    nl1 = st[0];
+    nl2 = st[a.Tp];
+    ne1 = st[2 * (size_t)a.Tp];
     e2 = st[3 * (size_t)a.Tp];
   }
 
@@ -615,16 +641,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (int r = 0; r < 16; ++r) {
       s1[r] = 0.0f;
       s2[r] = 0.0f;
-      dp[r] = 0.0f;
+      dp[r] = ne1;
     }
-    // S^T = K Q^T (rows: keys, lane column: query)
+    // S^T = K Q^T (rows: keys, lane column: query); dP^T enters with -D1 as
+    // the accumulator input, the scores take -lse in the exponent (a
+    // per-lane value here, and 32 more live registers would spill)
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const int off = (kb * 32 + l32) * (2 * D) + (((2 * ks + hi) ^ sw_row) << 4);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(tk1 + off), qf[0][ks], s1, 0, 0, 0);
       s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(tk2 + off), qf[1][ks], s2, 0, 0, 0);
     }
-    // dP^T = V dOpre^T
+    // dP^T - D1 = V dOpre^T - D1
 #pragma unroll
     for (int ks = 0; ks < C::VSTEPS; ++ks) {
       const bf16x8 av = *(const bf16x8*)(tv + (kb * 32 + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_row) << 4));
@@ -645,10 +673,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     bf16x8 g1[2], g2[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], sc, -lse1));
-      const float p2 = __builtin_amdgcn_exp2f(fmaf(s2[r], sc, -lse2));
-      g1[r >> 3][r & 7] = (bf16)(p1 * (dp[r] - e1));
-      g2[r >> 3][r & 7] = (bf16)(p2 * fmaf(-lam, dp[r], -e2));
+      const float p1 = __builtin_amdgcn_exp2f(s1[r] + nl1);
+      const float p2 = __builtin_amdgcn_exp2f(s2[r] + nl2);
+      g1[r >> 3][r & 7] = (bf16)(p1 * dp[r]);
+      g2[r >> 3][r & 7] = (bf16)(p2 * fmaf(-lam, dp[r], e2));
     }
     // dQm^T += Km^T dSm^T
 #pragma unroll
