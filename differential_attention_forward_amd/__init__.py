@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "DIFFATTN_F32", "DIFFATTN_BF16", "library_path", "lib",
     "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
-    "diffattn_fwd_reparam", "diffattn_fwd_window", "diffattn_attention_fwd",
+    "diffattn_fwd_reparam", "diffattn_fwd_window", "diffattn_fwd_strided", "diffattn_attention_fwd",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
     "diffattn_decode_ragged",
     "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_bwd_workspace_bytes",
@@ -40,6 +40,7 @@ _lib = None
 _VP = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_LLP = ctypes.POINTER(ctypes.c_longlong)
 _SIGS = {
     "diffattn_status_string": (ctypes.c_char_p, [_I]),
     "diffattn_lambda_init": (_F, [_I]),
@@ -51,6 +52,8 @@ _SIGS = {
     "diffattn_attention_fwd": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _I, _VP, _VP]),
     "diffattn_fwd_window": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
                                  _VP, _VP]),
+    "diffattn_fwd_strided": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _LLP, _VP, _I, _I, _F,
+                                  _F, _VP, _VP]),
     "diffattn_decode_default_splits": (_I, [_I, _I, _I]),
     "diffattn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "diffattn_decode": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F, _I,
@@ -200,6 +203,46 @@ def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = F
                               _ptr(k2), _ptr(v), _ptr(lamv), int(bool(causal)),
                               int(bool(headnorm)), float(lambda_init), float(eps), _ptr(out),
                               _stream(stream)))
+    return out
+
+
+def _view4(t, name, width_of_last):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on a HIP device")
+    if t.dim() != 4 or t.shape[-1] != width_of_last:
+        raise ValueError(f"{name} must be 4-D with last dimension {width_of_last}")
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return t
+
+
+def diffattn_fwd_strided(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
+                         lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
+    """Prefill forward on strided views, without copies: q*, k* are [B,H,T,D]
+    views, v a [B,H,T,2D] view (each with a contiguous last dimension, e.g.
+    the halves of a fused projection); ``out`` may be a view too (default: a
+    new dense [B,H,T,2D] tensor)."""
+    if not isinstance(q1, torch.Tensor) or q1.dim() != 4:
+        raise ValueError("q1 must be [B, H, T, D]")
+    b, h, t, d = q1.shape
+    q1, k1, q2, k2 = (_view4(x, n, d) for x, n in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2")))
+    v = _view4(v, "v", 2 * d)
+    for x, n in ((k1, "k1"), (q2, "q2"), (k2, "k2")):
+        if x.shape != q1.shape or x.dtype != q1.dtype:
+            raise ValueError(f"{n} must match q1 in shape and dtype")
+    if v.shape != (b, h, t, 2 * d) or v.dtype != q1.dtype:
+        raise ValueError("v must be [B, H, T, 2D] with the dtype of q1")
+    lamv = _lambda_vec(lam, h, q1.device)
+    if out is None:
+        out = torch.empty((b, h, t, 2 * d), device=q1.device, dtype=q1.dtype)
+    out = _view4(out, "out", 2 * d)
+    if out.shape != v.shape or out.dtype != v.dtype:
+        raise ValueError("out must be [B, H, T, 2D] with the dtype of q1")
+    st = (ctypes.c_longlong * 18)(*[s for x in (q1, k1, q2, k2, v, out) for s in x.stride()[:3]])
+    _check(lib().diffattn_fwd_strided(_dtype_code(q1), b, h, t, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                                      _ptr(k2), _ptr(v), st, _ptr(lamv), int(bool(causal)),
+                                      int(bool(headnorm)), float(lambda_init), float(eps), _ptr(out),
+                                      _stream(stream)))
     return out
 
 

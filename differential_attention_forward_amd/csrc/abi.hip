@@ -22,6 +22,24 @@ bool supported_d(int D) { return D == 32 || D == 64 || D == 128; }
 
 diffattn_status from_hip(hipError_t e) { return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP; }
 
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// every span in outs must be disjoint from every span in ins and from the
+// other outs (null entries are skipped)
+bool disjoint(const Span* ins, int nin, const Span* outs, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    if (!outs[i].p) continue;
+    for (int j = 0; j < nin; ++j)
+      if (ins[j].p && overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return false;
+    for (int j = i + 1; j < nout; ++j)
+      if (outs[j].p && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +119,7 @@ diffattn_status check_fwd(int dtype, int B, int H, int T, int D, const void* q1,
   a.window = 0;
   a.T = T;
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
+  diffattn::dense_strides(a, H, H, T, D, 2 * D);
   out_bytes = nv;
   return DIFFATTN_OK;
 }
@@ -141,6 +160,105 @@ diffattn_status diffattn_fwd_window(int dtype, int B, int H, int T, int D, const
   a.out_scale = 1.0f - lambda_init;
   a.eps = eps;
   return from_hip(diffattn::launch_fwd(a, dtype, D, true, headnorm != 0, stream));
+}
+
+namespace {
+
+// Byte span [lo, hi) touched by a [B, H, T, width] tensor with element
+// strides sb, sh, sr (all >= 0) and 2-byte elements.
+Span strided_span(const void* p, int B, int H, int T, const long long* st, int width) {
+  const long long last = (long long)(B - 1) * st[0] + (long long)(H - 1) * st[1] + (long long)(T - 1) * st[2];
+  return {p, (size_t)(last + width) * 2};
+}
+
+// Whether distinct (b, h, t) rows of a [B, H, T, width] tensor with strides
+// st = (sb, sh, sr) never share an element: ordered by stride, every extent
+// must fit inside the next stride.
+bool rows_disjoint(int B, int H, int T, const long long* st, int width) {
+  long long s[3] = {st[0], st[1], st[2]};
+  long long n[3] = {B, H, T};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (s[j] < s[i] || (s[j] == s[i] && n[j] < n[i])) {
+        long long t = s[i]; s[i] = s[j]; s[j] = t;
+        t = n[i]; n[i] = n[j]; n[j] = t;
+      }
+  long long extent = width;  // elements covered by one row
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] == 1) continue;
+    if (s[i] < extent) return false;
+    extent = s[i] * (n[i] - 1) + extent;
+  }
+  return true;
+}
+
+}  // namespace
+
+diffattn_status diffattn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q1,
+                                     const void* k1, const void* q2, const void* k2, const void* v,
+                                     const long long* strides, const float* lambda, int causal,
+                                     int headnorm, float lambda_init, float eps, void* out,
+                                     hipStream_t stream) {
+  if (!q1 || !k1 || !q2 || !k2 || !v || !out || !strides || !lambda) return DIFFATTN_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1) return DIFFATTN_ERR_INVALID;
+  if (headnorm && !(eps > 0.0f)) return DIFFATTN_ERR_INVALID;
+  for (int i = 0; i < 18; ++i)
+    if (strides[i] < 0) return DIFFATTN_ERR_INVALID;
+  if (dtype != DIFFATTN_BF16 || !supported_d(D)) return DIFFATTN_ERR_UNSUPPORTED;
+  const void* ptr[6] = {q1, k1, q2, k2, v, out};
+  const int width[6] = {D, D, D, D, 2 * D, 2 * D};
+  for (int i = 0; i < 6; ++i) {
+    if (!aligned(ptr[i], 16)) return DIFFATTN_ERR_UNSUPPORTED;
+    // 128-bit row accesses: every stride a multiple of 8 bf16 elements
+    for (int j = 0; j < 3; ++j)
+      if (strides[3 * i + j] % 8) return DIFFATTN_ERR_UNSUPPORTED;
+  }
+  if (!aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H > 0x7fffffffLL || (long long)T * 2 * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  // K and V rows are fetched at 32-bit byte offsets from their (b, h) slice;
+  // query and output row strides are ints
+  for (int i = 0; i < 6; ++i) {
+    const long long rs = strides[3 * i + 2];
+    if (rs > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+    if ((i == 1 || i == 3 || i == 4) && ((long long)(T - 1) * rs + width[i]) * 2 > 0x7fffffffLL)
+      return DIFFATTN_ERR_UNSUPPORTED;
+  }
+  if (!rows_disjoint(B, H, T, strides + 15, 2 * D)) return DIFFATTN_ERR_INVALID;
+  Span ins[6];
+  for (int i = 0; i < 5; ++i) ins[i] = strided_span(ptr[i], B, H, T, strides + 3 * i, width[i]);
+  ins[5] = {lambda, (size_t)H * sizeof(float)};
+  const Span outs[1] = {strided_span(out, B, H, T, strides + 15, 2 * D)};
+  if (!disjoint(ins, 6, outs, 1)) return DIFFATTN_ERR_INVALID;
+
+  diffattn::FwdArgs a;
+  a.q1 = q1;
+  a.k1 = k1;
+  a.q2 = q2;
+  a.k2 = k2;
+  a.v = v;
+  a.lam = lambda;
+  for (int i = 0; i < 4; ++i) a.lvec[i] = nullptr;
+  a.Dl = 0;
+  a.lam_init = 0.0f;
+  a.lam_out = nullptr;
+  a.out = out;
+  a.save_o1 = nullptr;
+  a.save_o2 = nullptr;
+  a.save_lse = nullptr;
+  a.B = B;
+  a.H = H;
+  a.Hkv = H;
+  a.window = 0;
+  a.T = T;
+  a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
+  a.out_scale = 1.0f - lambda_init;
+  a.eps = eps;
+  for (int i = 0; i < 6; ++i) {
+    a.sb[i] = strides[3 * i];
+    a.sh[i] = strides[3 * i + 1];
+    a.sr[i] = (int)strides[3 * i + 2];
+  }
+  return from_hip(diffattn::launch_fwd(a, dtype, D, causal != 0, headnorm != 0, stream));
 }
 
 diffattn_status diffattn_fwd_reparam(int dtype, int B, int H, int T, int D, const void* q1,
@@ -218,6 +336,7 @@ diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, co
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   a.out_scale = 1.0f;
   a.eps = 1.0f;
+  diffattn::dense_strides(a, H, H, T, D, D);
   return from_hip(diffattn::launch_attention(a, D, causal != 0, stream));
 }
 
@@ -226,24 +345,6 @@ diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, co
 namespace {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-struct Span {
-  const void* p;
-  size_t n;
-};
-
-// every span in outs must be disjoint from every span in ins and from the
-// other outs (null entries are skipped)
-bool disjoint(const Span* ins, int nin, const Span* outs, int nout) {
-  for (int i = 0; i < nout; ++i) {
-    if (!outs[i].p) continue;
-    for (int j = 0; j < nin; ++j)
-      if (ins[j].p && overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return false;
-    for (int j = i + 1; j < nout; ++j)
-      if (outs[j].p && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return false;
-  }
-  return true;
-}
 
 bool train_sizes_ok(int B, int H, int T, int D) {
   if (B < 1 || H < 1 || T < 1 || D != 64) return false;
@@ -515,6 +616,7 @@ diffattn_status diffattn_v2_fwd(int dtype, int B, int H, int Hkv, int T, int D, 
   a.score_scale = (float)(1.4426950408889634 / sqrt((double)D));
   a.out_scale = 1.0f;
   a.eps = 1.0f;
+  diffattn::dense_strides(a, H, Hkv, T, D, D);
   return from_hip(diffattn::launch_v2(a, D, causal != 0, stream));
 }
 

@@ -40,20 +40,30 @@
 //    the B operand of dQ^T = K^T dS^T.  Q1, Q2 and dOpre stay in VGPRs.
 //  * lambda: dlam per head from the partials; with the re-parameterisation
 //    vectors, their gradients as well.
-// LDS tiles use one XOR swizzle of 16-byte columns (swz2) that keeps both the
-// row reads (A operands of S and dP) and the transposing reads (A operands
-// of the gradient products) free of bank conflicts.
+// LDS tiles use XOR swizzles of 16-byte columns (swzb, one per row pitch)
+// that keep both the row reads (A operands of S and dP) and the transposing
+// reads (A operands of the gradient products) free of bank conflicts.
 #include "common.h"
 #include "kernels.h"
 
 namespace diffattn {
 namespace {
 
-// 16-byte column swizzle for rows whose pitch is a multiple of 128 bytes.
-// Row reads: 8 lanes read one column of 8 consecutive rows -> 8 distinct
-// columns.  Transposing reads: 16 lanes read two adjacent columns (even
-// first) of 4 consecutive rows starting at a multiple of 4 -> 8 distinct.
-__device__ inline int swz2(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// 16-byte column swizzles for gfx950's 64 banks of 4 bytes (256 bytes per
+// clock).  A ds_read_b128 serves 16 lanes per cycle, a ds_read_b64_tr_b16 32.
+//  Row reads: lanes 0..15 read one logical column of rows r..r+15 (r a
+//  multiple of 16).  Transposing reads: 32 lanes read one 64-byte group of
+//  four columns of each of four rows r..r+3 (r a multiple of 4).
+//  128-byte rows (D = 64): a row covers half of the banks (row parity picks
+//  the half); bits 1..3 of the row give 8 distinct columns per parity for
+//  the row reads, and bit 1 moves rows r and r + 2 to different groups.
+//  256-byte rows (2D = 128): bits 2, 3 permute inside a group and bits 0, 1
+//  pick the group, so 16 rows give 16 columns and 4 rows 4 groups.
+template <int PITCH>
+__device__ inline int swzb(int row) {
+  static_assert(PITCH == 128 || PITCH == 256, "row pitch of 128 or 256 bytes");
+  return PITCH == 128 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : (((row & 3) << 2) | ((row >> 2) & 3));
+}
 
 // Eight bf16 values times c, each product rounded once to bf16 (the forward
 // forms its base-2 scores from operands rounded the same way).
@@ -308,13 +318,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const int which = seg / C::QSEG;
         const int g = seg % C::QSEG;
         const int r = g * RK + lane / CK;
-        const int c = (lane % CK) ^ swz2(r);
+        const int c = (lane % CK) ^ swzb<2 * D>(r);
         const uint32_t row = (uint32_t)min(q0 + r, T - 1);
         dma16(which ? Q2 : Q1, row * (D * 2) + c * 16, sb + which * C::QBYTES + g * 1024);
       } else if (seg < 2 * C::QSEG + C::OSEG) {
         const int g = seg - 2 * C::QSEG;
         const int r = g * RO + lane / CO;
-        const int c = (lane % CO) ^ swz2(r);
+        const int c = (lane % CO) ^ swzb<2 * DV>(r);
         const uint32_t row = (uint32_t)min(q0 + r, T - 1);
         dma16(dO, row * (DV * 2) + c * 16, sb + 2 * C::QBYTES + g * 1024);
       } else {
@@ -345,20 +355,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   }
 
   // per-lane LDS offsets
-  const int sw_row = swz2(l32);                          // row reads: row = 32 sub + l32
+  const int sw_q = swzb<2 * D>(l32);                     // row reads: row = 32 sub + l32
+  const int sw_o = swzb<2 * DV>(l32);
   const int tq = lane & 3;
   const int tk = (lane >> 2) & 3;
   const int t_row = 4 * hi + tk;                         // + 32 sub + 16 ks (+ 8 for the upper half)
   const int t_chunk = 2 * ((lane >> 4) & 1) + (tq >> 1); // + 4 cb
-  const int t_sw = (tk << 1) | hi;                       // swz2 of every transposed-read row
   const int t_byte = (tq & 1) * 8;
+  // swizzles of the transposed-read rows t_row and t_row + 8
+  const int tsw_q[2] = {swzb<2 * D>(t_row), swzb<2 * D>(t_row + 8)};
+  const int tsw_o[2] = {swzb<2 * DV>(t_row), swzb<2 * DV>(t_row + 8)};
 
   // A operand of a gradient product: 8 queries (in the lane's probability
   // order) of channel 32 cb + l32, from a tile with rows of RB bytes
-  auto tr_read = [&](const char* tile, int rb, int sub, int ks, int cb) __attribute__((always_inline)) {
-    const char* base = tile + (32 * sub + 16 * ks + t_row) * rb + (((4 * cb + t_chunk) ^ t_sw) << 4) + t_byte;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
-    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * rb));
+  auto tr_read = [&](const char* tile, int rb, const int (&tsw)[2], int sub, int ks, int cb) __attribute__((always_inline)) {
+    const char* row = tile + (32 * sub + 16 * ks + t_row) * rb + t_byte;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(row + (((4 * cb + t_chunk) ^ tsw[0]) << 4)));
+    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(row + 8 * rb + (((4 * cb + t_chunk) ^ tsw[1]) << 4)));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
   };
 
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // S - lse = Q K^T - lse (rows: queries, lane column: key) for both maps
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      const int off = (32 * sub + l32) * (2 * D) + (((2 * ks + hi) ^ sw_row) << 4);
+      const int off = (32 * sub + l32) * (2 * D) + (((2 * ks + hi) ^ sw_q) << 4);
       const bf16x8 a1 = *(const bf16x8*)(tq1 + off);
       const bf16x8 a2 = *(const bf16x8*)(tq2 + off);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kf[0][ks], s1, 0, 0, 0);
@@ -396,7 +409,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // dP - D1 = dOpre V^T - D1
 #pragma unroll
     for (int ks = 0; ks < C::VSTEPS; ++ks) {
-      const bf16x8 ao = *(const bf16x8*)(tdo + (32 * sub + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_row) << 4));
+      const bf16x8 ao = *(const bf16x8*)(tdo + (32 * sub + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_o) << 4));
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ks], dp, 0, 0, 0);
     }
     // masked elements: future keys (causal) and queries past the end
@@ -433,11 +446,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int cb = 0; cb < C::CBV; ++cb)
-        dvT[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tdo, 2 * DV, sub, ks, cb), pc[ks], dvT[cb], 0, 0, 0);
+        dvT[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tdo, 2 * DV, tsw_o, sub, ks, cb), pc[ks], dvT[cb], 0, 0, 0);
 #pragma unroll
       for (int cb = 0; cb < C::CBK; ++cb) {
-        dk1T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tq1, 2 * D, sub, ks, cb), g1[ks], dk1T[cb], 0, 0, 0);
-        dk2T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tq2, 2 * D, sub, ks, cb), g2[ks], dk2T[cb], 0, 0, 0);
+        dk1T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tq1, 2 * D, tsw_q, sub, ks, cb), g1[ks], dk1T[cb], 0, 0, 0);
+        dk2T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(tq2, 2 * D, tsw_q, sub, ks, cb), g2[ks], dk2T[cb], 0, 0, 0);
       }
     }
   };
@@ -581,7 +594,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     e2 = st[3 * (size_t)a.Tp];
   }
 
-  // ---- asynchronous key-tile loads (K1, K2, V; swizzled with swz2) ----------
+  // ---- asynchronous key-tile loads (K1, K2, V; swizzled with swzb) ----------
   constexpr int CK = D / 8, RK = 64 / CK, CV = DV / 8, RV = 64 / CV;
   auto issue_rt = [&](int kt, char* sb) __attribute__((always_inline)) {
     const int key0 = kt * BC;
@@ -593,13 +606,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const int which = seg / C::KSEG;
         const int g = seg % C::KSEG;
         const int r = g * RK + lane / CK;
-        const int c = (lane % CK) ^ swz2(r);
+        const int c = (lane % CK) ^ swzb<2 * D>(r);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
         dma16(which ? K2 : K1, row * (D * 2) + c * 16, sb + which * C::KBYTES + g * 1024);
       } else {
         const int g = seg - 2 * C::KSEG;
         const int r = g * RV + lane / CV;
-        const int c = (lane % CV) ^ swz2(r);
+        const int c = (lane % CV) ^ swzb<2 * DV>(r);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
         dma16(V, row * (DV * 2) + c * 16, sb + 2 * C::KBYTES + g * 1024);
       }
@@ -623,12 +636,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       dq2T[cb][r] = 0.0f;
     }
 
-  const int sw_row = swz2(l32);
+  const int sw_k = swzb<2 * D>(l32);
+  const int sw_v = swzb<2 * DV>(l32);
   const int tq = lane & 3;
   const int tk = (lane >> 2) & 3;
   const int t_row = 4 * hi + tk;
   const int t_chunk = 2 * ((lane >> 4) & 1) + (tq >> 1);
-  const int t_sw = (tk << 1) | hi;
+  const int tsw_lo = swzb<2 * D>(t_row), tsw_up = swzb<2 * D>(t_row + 8);
   const int t_byte = (tq & 1) * 8;
 
   auto compute_block = [&](int kt, int kb, const char* sb) __attribute__((always_inline)) {
@@ -648,14 +662,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // per-lane value here, and 32 more live registers would spill)
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      const int off = (kb * 32 + l32) * (2 * D) + (((2 * ks + hi) ^ sw_row) << 4);
+      const int off = (kb * 32 + l32) * (2 * D) + (((2 * ks + hi) ^ sw_k) << 4);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(tk1 + off), qf[0][ks], s1, 0, 0, 0);
       s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(tk2 + off), qf[1][ks], s2, 0, 0, 0);
     }
     // dP^T - D1 = V dOpre^T - D1
 #pragma unroll
     for (int ks = 0; ks < C::VSTEPS; ++ks) {
-      const bf16x8 av = *(const bf16x8*)(tv + (kb * 32 + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_row) << 4));
+      const bf16x8 av = *(const bf16x8*)(tv + (kb * 32 + l32) * (2 * DV) + (((2 * ks + hi) ^ sw_v) << 4));
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[ks], dp, 0, 0, 0);
     }
     const bool need_mask = CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T);
@@ -683,11 +697,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int cb = 0; cb < C::CBK; ++cb) {
-        const int boff = (kb * 32 + 16 * ks + t_row) * (2 * D) + (((4 * cb + t_chunk) ^ t_sw) << 4) + t_byte;
-        const bf16x4 lo1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk1 + boff));
-        const bf16x4 up1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk1 + boff + 8 * (2 * D)));
-        const bf16x4 lo2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk2 + boff));
-        const bf16x4 up2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk2 + boff + 8 * (2 * D)));
+        const int rowb = (kb * 32 + 16 * ks + t_row) * (2 * D) + t_byte;
+        const int blo = rowb + (((4 * cb + t_chunk) ^ tsw_lo) << 4);
+        const int bup = rowb + 8 * (2 * D) + (((4 * cb + t_chunk) ^ tsw_up) << 4);
+        const bf16x4 lo1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk1 + blo));
+        const bf16x4 up1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk1 + bup));
+        const bf16x4 lo2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk2 + blo));
+        const bf16x4 up2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tk2 + bup));
         const bf16x8 a1 = {lo1[0], lo1[1], lo1[2], lo1[3], up1[0], up1[1], up1[2], up1[3]};
         const bf16x8 a2 = {lo2[0], lo2[1], lo2[2], lo2[3], up2[0], up2[1], up2[2], up2[3]};
         dq1T[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, g1[ks], dq1T[cb], 0, 0, 0);

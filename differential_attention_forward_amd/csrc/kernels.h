@@ -33,7 +33,24 @@ struct FwdArgs {
   float score_scale;  // log2(e) / sqrt(D)
   float out_scale;    // 1 - lambda_init (head norm only)
   float eps;
+  // bf16 kernel: element strides of q1, k1, q2, k2, v, out (in that order)
+  // between batches, heads and rows; each row is contiguous.  K and V index
+  // KV heads.  Dense layouts get them from dense_strides().
+  long long sb[6], sh[6];
+  int sr[6];
 };
+
+// Strides of densely packed [B, H, T, D] queries, [B, Hkv, T, D] keys,
+// [B, Hkv, T, DV] values and a [B, H, T, DV] output.
+inline void dense_strides(FwdArgs& a, int H, int Hkv, int T, int D, int DV) {
+  const long long w[6] = {D, D, D, D, DV, DV};
+  const long long heads[6] = {H, Hkv, H, Hkv, Hkv, H};
+  for (int i = 0; i < 6; ++i) {
+    a.sr[i] = (int)w[i];
+    a.sh[i] = (long long)T * w[i];
+    a.sb[i] = heads[i] * T * w[i];
+  }
+}
 
 struct DecodeArgs {
   const void* q1;     // [B,H,D]

@@ -490,17 +490,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
   const int h = bh % a.H;
 
-  // V2: head h of batch b reads KV head h / (H / Hkv) of that batch
-  const int kvbh = SHKV ? (bh / a.H) * a.Hkv + h / (a.H / a.Hkv) : bh;
-  const size_t qk_off = (size_t)bh * T * D;
-  const size_t kv_off = (size_t)kvbh * T * D;
-  const size_t v_off = (size_t)kvbh * T * C::DV;
-  const size_t o_off = (size_t)bh * T * C::DV;
-  const bf16* __restrict__ Q1 = (const bf16*)a.q1 + qk_off;
-  const bf16* __restrict__ Q2 = (const bf16*)a.q2 + qk_off;
-  const bf16* __restrict__ K1 = scalar_ptr((const bf16*)a.k1 + kv_off);
-  const bf16* __restrict__ K2 = SHKV ? K1 : scalar_ptr((const bf16*)a.k2 + kv_off);
-  const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + v_off);
+  // V2: head h of batch b reads KV head h / (H / Hkv) of that batch.  Each
+  // tensor is addressed through its own batch, head and row strides.
+  const int bb = bh / a.H;
+  const int kvh = SHKV ? h / (a.H / a.Hkv) : h;
+  const size_t o_off = (size_t)bh * T * C::DV;  // the saved training maps are dense
+  const bf16* __restrict__ Q1 = (const bf16*)a.q1 + (bb * a.sb[0] + h * a.sh[0]);
+  const bf16* __restrict__ Q2 = (const bf16*)a.q2 + (bb * a.sb[2] + h * a.sh[2]);
+  const bf16* __restrict__ K1 = scalar_ptr((const bf16*)a.k1 + (bb * a.sb[1] + kvh * a.sh[1]));
+  const bf16* __restrict__ K2 =
+      SHKV ? K1 : scalar_ptr((const bf16*)a.k2 + (bb * a.sb[3] + kvh * a.sh[3]));
+  const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + (bb * a.sb[4] + kvh * a.sh[4]));
+  // row strides: queries and output in elements, K and V rows in bytes
+  const int rq[2] = {a.sr[0], a.sr[2]};
+  const uint32_t rk_b[2] = {2u * (uint32_t)a.sr[1], 2u * (uint32_t)a.sr[3]};
+  const uint32_t rv_b = 2u * (uint32_t)a.sr[4];
 
   const int wbr = SPLIT ? wave / C::NWQ : 0;
   const int wq = SPLIT ? wave % C::NWQ : wave;
@@ -542,13 +546,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
         const int r = g * RK + rl_k;
         const int c = (lane % CK) ^ swz_k<D>(r);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
-        dma16(which ? K2 : K1, row * (D * 2) + c * 16, sb + which * C::KBYTES + g * 1024);
+        dma16(which ? K2 : K1, row * rk_b[which] + c * 16, sb + which * C::KBYTES + g * 1024);
       } else {
         const int g = seg - C::KT * C::KSEG;
         const int r = g * RV + rl_v;
         const int c = (lane % CV) ^ swz_v<C::DV>(r);
         const uint32_t row = (uint32_t)min(key0 + r, T - 1);
-        dma16(V, row * (C::DV * 2) + c * 16, sb + C::KT * C::KBYTES + g * 1024);
+        dma16(V, row * rv_b + c * 16, sb + C::KT * C::KBYTES + g * 1024);
       }
     }
   };
@@ -564,7 +568,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
     for (int qb = 0; qb < NQB; ++qb) {
       const int query = q0 + qb * 32 + l32;
       const bool ok = query < T;
-      const bf16* src = ((br + wbr) ? Q2 : Q1) + (size_t)min(query, T - 1) * D;
+      const bf16* src = ((br + wbr) ? Q2 : Q1) + (size_t)min(query, T - 1) * rq[br + wbr];
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks) {
         u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
@@ -858,7 +862,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   if (!wave_active) return;
 
   // ---- epilogue: combine the maps, optional head norm, store -----------------
-  bf16* __restrict__ O = (bf16*)a.out + o_off;
+  bf16* __restrict__ O = (bf16*)a.out + (bb * a.sb[5] + h * a.sh[5]);
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int query = q0 + qb * 32 + l32;
@@ -903,7 +907,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
         for (int r = 0; r < 16; ++r) o[cb][r] *= f;
     }
     if (query < T) {
-      bf16* dst = O + (size_t)query * C::DV;
+      bf16* dst = O + (size_t)query * a.sr[5];
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll

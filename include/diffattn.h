@@ -103,6 +103,36 @@ diffattn_status diffattn_fwd(int dtype, int B, int H, int T, int D, const void* 
                              float eps, void* out, hipStream_t stream);
 
 /*
+ * Prefill on strided views, read and written in place (no copies): the
+ * aifetchly page ("Differential Transformer: Canceling LLM Attention Noise",
+ * its numpy forward, step 1) cuts Q1, Q2 (and K1, K2) out of one projection
+ * of width 2D along the feature axis, and the paperleet page's interface
+ * section allows strided inputs.  Q1 = Q[..., :D] and Q2 = Q[..., D:] of a
+ * fused [B, T, H, 2D] projection, for instance, are views with row stride
+ * 2HD, head stride 2D and batch stride 2THD elements.
+ *
+ *   strides  HOST array of 18 int64: for q1, k1, q2, k2, v, out in turn the
+ *            batch, head and row stride in elements (the tensors keep their
+ *            logical [B, H, T, D] / [B, H, T, 2D] shapes; the last dimension
+ *            is contiguous).  Every stride >= 0 and a multiple of 8 elements
+ *            (16 bytes); input strides may be 0 (a tensor shared across
+ *            batches or heads).  Read during the call only.
+ *   out      distinct (b, h, t) rows must not overlap, and the whole address
+ *            range the output spans must not overlap the range of any input
+ *            or of lambda
+ *   other arguments as for diffattn_fwd; bf16 only
+ * Errors: as diffattn_fwd, plus ERR_INVALID for a null `strides`, a negative
+ * stride or overlapping output rows, ERR_UNSUPPORTED for fp32, a stride that
+ * is not a multiple of 8, or a K1, K2 or V row stride that puts a row 2 GiB
+ * or more past the start of its (b, h) slice.
+ */
+diffattn_status diffattn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q1,
+                                     const void* k1, const void* q2, const void* k2, const void* v,
+                                     const long long* strides, const float* lambda, int causal,
+                                     int headnorm, float lambda_init, float eps, void* out,
+                                     hipStream_t stream);
+
+/*
  * Prefill with a causal sliding window (the French lesson page, "Utilisez-le":
  * hybrid stacks that alternate differential attention with sliding-window
  * attention).  Row i sees the `window` most recent positions including itself,

@@ -24,7 +24,7 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert "diffattn_fwd_reparam" in names and "diffattn_attention_fwd" in names
     assert "diffattn_v2_fwd" in names and "diffattn_v2_decode" in names
     assert "diffattn_fwd_train" in names and "diffattn_bwd" in names
@@ -178,6 +178,58 @@ def test_fwd_window_validation(L):
     assert fwin(L, T=0) == INVALID
     assert fwin(L, ptrs=[P(0), P(1), P(2), P(3), P(4), None, P(6)]) == INVALID     # lambda
     assert fwin(L, ptrs=[P(0), P(1), P(2), P(3), P(4), P(5), P(4, 64)]) == INVALID  # out over v
+
+
+def dense_strides(B, H, T, D):
+    """(batch, head, row) element strides of dense q1, k1, q2, k2, v, out."""
+    out = []
+    for w in (D, D, D, D, 2 * D, 2 * D):
+        out += [H * T * w, T * w, w]
+    return out
+
+
+def fstr(L, dtype=BF16, B=1, H=2, T=8, D=64, strides=None, ptrs=None, headnorm=0, eps=1e-5):
+    p = ptrs or [P(i) for i in range(7)]
+    st = strides if strides is not None else dense_strides(B, H, T, D)
+    arr = (ctypes.c_longlong * 18)(*st) if st is not None else None
+    return L.diffattn_fwd_strided(dtype, B, H, T, D, p[0], p[1], p[2], p[3], p[4], arr, p[5], 1,
+                                  headnorm, ctypes.c_float(0.8), ctypes.c_float(eps), p[6], None)
+
+
+def test_fwd_strided_validation(L):
+    B, H, T, D = 1, 2, 8, 64
+    st = dense_strides(B, H, T, D)
+    assert L.diffattn_fwd_strided(BF16, B, H, T, D, P(0), P(1), P(2), P(3), P(4), None, P(5), 1, 0,
+                                  ctypes.c_float(0.8), ctypes.c_float(1e-5), P(6), None) == INVALID
+    assert fstr(L, ptrs=[P(0), None, P(2), P(3), P(4), P(5), P(6)]) == INVALID
+    assert fstr(L, ptrs=[P(0), P(1), P(2), P(3), P(4), None, P(6)]) == INVALID   # lambda
+    assert fstr(L, T=0) == INVALID
+    assert fstr(L, headnorm=1, eps=0.0) == INVALID
+    assert fstr(L, dtype=F32) == UNSUPPORTED
+    assert fstr(L, D=96, strides=dense_strides(B, H, T, 96)) == UNSUPPORTED
+    bad = list(st)
+    bad[2] = -64                                                  # negative row stride
+    assert fstr(L, strides=bad) == INVALID
+    bad = list(st)
+    bad[5] = 68                                                   # k1 row stride not 16-byte
+    assert fstr(L, strides=bad) == UNSUPPORTED
+    bad = list(st)
+    bad[17] = 64                                                  # out rows of 128 overlap
+    assert fstr(L, strides=bad) == INVALID
+    bad = list(st)
+    bad[16] = 0                                                   # both heads write one slice
+    assert fstr(L, strides=bad) == INVALID
+    bad = list(st)
+    bad[14] = 1 << 27                                             # v row stride past 2 GiB
+    assert fstr(L, T=64, strides=bad) == UNSUPPORTED
+    # out's span reaches into v's
+    assert fstr(L, ptrs=[P(0), P(1), P(2), P(3), P(4), P(5), P(4, 64)]) == INVALID
+    # interleaved halves of one fused projection: q1 and q2 overlap as inputs (allowed);
+    # the output may not land inside the fused buffer
+    fused = [H * T * 2 * D, 2 * D, 2 * H * D]                     # a [B, T, H, 2D] view's strides
+    st2 = fused + fused + fused + fused + [H * T * 2 * D, T * 2 * D, 2 * D] * 2
+    ptrs = [P(0), P(1), P(0, 2 * D), P(1, 2 * D), P(4), P(5), P(0, 32)]
+    assert fstr(L, strides=st2, ptrs=ptrs) == INVALID
 
 
 def v2f(L, dtype=BF16, B=1, H=4, Hkv=2, T=8, D=64, ptrs=None):
