@@ -46,6 +46,9 @@ CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
 KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip", "v2_decode": "decode.hip"}
 KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel",
                "v2_decode": "decode_v2_mma_kernel"}
+# which kernel dominates each workload kind (the backward has four of comparable weight)
+KIND_KERNEL = {"prefill": "prefill", "v2_prefill": "prefill", "window_prefill": "prefill",
+               "decode": "decode", "ragged_decode": "decode", "v2_decode": "v2_decode"}
 
 
 def log(*a):
@@ -240,7 +243,7 @@ def bench_workload(torch, da, name, steps, warmup):
         peak = PEAK["bf16_mfma_tflops"] if w.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic("prefill", name) if w.kind == "prefill" else None,
+                "traffic": measured_traffic("prefill", name) if w.kind in KIND_KERNEL else None,
                 "kernel": "bwd_prep + bwd_kv + bwd_q + bwd_lambda kernels" if w.kind == "bwd" else KERNEL_NAME["prefill"],
                 "algorithmic_per_launch": work}
         unit = "TFLOP/s"
@@ -250,8 +253,8 @@ def bench_workload(torch, da, name, steps, warmup):
         achieved = work / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"],
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm_gbs"], 4),
-                "traffic": measured_traffic(w.kind, name) if w.kind in KERNEL_NAME else None,
-                "kernel": KERNEL_NAME.get(w.kind, KERNEL_NAME["decode"]),
+                "traffic": measured_traffic(KIND_KERNEL[w.kind], name),
+                "kernel": KERNEL_NAME[KIND_KERNEL[w.kind]],
                 "algorithmic_per_launch": work}
         unit = "GB/s"
     res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
