@@ -59,10 +59,15 @@ namespace {
 //  the row reads, and bit 1 moves rows r and r + 2 to different groups.
 //  256-byte rows (2D = 128): bits 2, 3 permute inside a group and bits 0, 1
 //  pick the group, so 16 rows give 16 columns and 4 rows 4 groups.
+//  64-byte rows (D = 32): a row is one group of four columns and the row
+//  modulo 4 picks its quarter of the banks; bits 2, 3 give the four rows of a
+//  quarter distinct columns (transposing reads cover four whole rows).
 template <int PITCH>
 __device__ inline int swzb(int row) {
-  static_assert(PITCH == 128 || PITCH == 256, "row pitch of 128 or 256 bytes");
-  return PITCH == 128 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : (((row & 3) << 2) | ((row >> 2) & 3));
+  static_assert(PITCH == 64 || PITCH == 128 || PITCH == 256, "row pitch of 64, 128 or 256 bytes");
+  return PITCH == 64    ? ((row >> 2) & 3)
+         : PITCH == 128 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3))
+                        : (((row & 3) << 2) | ((row >> 2) & 3));
 }
 
 // Eight bf16 values times c, each product rounded once to bf16 (the forward
@@ -780,6 +785,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, bool headnorm, hipStream_t stream) {
+  if (D == 32) return causal ? launch_bwd_d<32, true>(a, headnorm, stream) : launch_bwd_d<32, false>(a, headnorm, stream);
   if (D == 64) return causal ? launch_bwd_d<64, true>(a, headnorm, stream) : launch_bwd_d<64, false>(a, headnorm, stream);
   return hipErrorInvalidValue;
 }

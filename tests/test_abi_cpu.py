@@ -309,7 +309,8 @@ def test_training_sizes(L):
     tp = 128
     ws = (b * h * t * 2 * d * 2 + 255) // 256 * 256 + (b * h * 4 * tp * 4 + 255) // 256 * 256 + b * h * 2 * 4
     assert da.diffattn_bwd_workspace_bytes(b, h, t, d) == ws
-    for args in ((0, 1, 8, 64), (1, 1, 0, 64), (1, 1, 8, 32), (1, 1, 8, 128)):
+    assert da.diffattn_train_saved_bytes(1, 1, 8, 32) == 2 * 8 * 64 * 4 + 2 * 8 * 4
+    for args in ((0, 1, 8, 64), (1, 1, 0, 64), (1, 1, 8, 16), (1, 1, 8, 128)):
         assert da.diffattn_train_saved_bytes(*args) == 0
         assert da.diffattn_bwd_workspace_bytes(*args) == 0
 
@@ -326,7 +327,7 @@ def test_fwd_train_validation(L):
     assert fwdt(L, ptrs=[P(0), None] + [P(i) for i in range(2, 8)]) == INVALID
     assert fwdt(L, T=0) == INVALID
     assert fwdt(L, dtype=F32) == UNSUPPORTED
-    for d in (32, 128):
+    for d in (16, 128):
         assert fwdt(L, D=d) == UNSUPPORTED
     assert fwdt(L, saved_bytes=da.diffattn_train_saved_bytes(1, 2, 8, 64) - 1) == WORKSPACE
     bad = [P(i) for i in range(8)]
