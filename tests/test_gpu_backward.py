@@ -31,7 +31,7 @@ import torch
 
 import differential_attention_forward_amd as da
 import oracle
-from workloads import grad_output, make_workload, prefill_inputs
+from workloads import WORKLOADS, grad_output, make_workload, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -220,3 +220,37 @@ def test_bwd_key_gradient_identity_long(D, T):
         for got, ref in ((g[0][0, h, rows], r1), (g[2][0, h, rows], r2)):
             err = float(np.max(np.abs(_np(got) - ref)))
             assert err <= REL * float(np.max(np.abs(ref))), (h, err)
+
+
+def test_workload_bwd_t4k_causal():
+    """The bench's backward workload (B2 H16 T4096 D64, causal, head norm,
+    lambda_init 0.8) in its launch configuration: dQ1, dQ2 on sampled rows of
+    sampled heads against the oracle, and the per-map key-gradient identity
+    (sum over keys of dK = 0) on every head."""
+    w = WORKLOADS["bwd_t4k_causal"]
+    x = make_workload("bwd_t4k_causal", DEV)
+    say("workload bwd_t4k_causal: launching")
+    _, saved = da.diffattn_fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lam"], causal=True,
+                                     headnorm=True, lambda_init=w.lambda_init, eps=w.eps)
+    g = da.diffattn_bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lam"], x["dout"], saved, causal=True,
+                        headnorm=True, lambda_init=w.lambda_init, eps=w.eps)
+    torch.cuda.synchronize()
+    for t in g[:5]:
+        assert torch.isfinite(t.float()).all()
+    for dk in (g[1], g[3]):
+        s = dk.float().sum(dim=2)
+        scale = dk.float().abs().sum(dim=2)
+        assert float((s.abs() / scale).max()) <= 1e-2
+    lam = x["lam"].cpu().numpy()
+    rng = np.random.default_rng(w.seed)
+    for (b, h) in ((0, 0), (1, 9)):
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, w.T - 1], rng.integers(0, w.T, 9)]))
+        sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v", "dout")}
+        r1, r2 = oracle.diff_attention_backward_dq_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"],
+                                                        float(lam[h]), sl["dout"], rows, True, True,
+                                                        w.lambda_init, w.eps)
+        for got, ref in ((g[0][b, h, rows], r1), (g[2][b, h, rows], r2)):
+            err = float(np.max(np.abs(_np(got) - ref)))
+            assert err <= REL * float(np.max(np.abs(ref))) + ABS, (b, h, err)
+    del x, g, saved
+    torch.cuda.empty_cache()

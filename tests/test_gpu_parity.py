@@ -454,3 +454,57 @@ def test_decode_ragged(dtype, headnorm):
                            headnorm=headnorm, num_splits=16)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---- the measured workloads of the other rows, at their bench sizes -----------
+
+def test_workload_prefill_t32k_window4k():
+    """B1 H16 T32768 D64, 4096-key window: sampled rows of three heads."""
+    name = "prefill_t32k_window4k"
+    w = WORKLOADS[name]
+    x = make_workload(name, DEV)
+    say(f"workload {name}: launching")
+    out = da.diffattn_fwd_window(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lam"], w.window,
+                                 headnorm=w.headnorm, lambda_init=w.lambda_init, eps=w.eps)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(w.seed)
+    lam_ref = x["lam"].cpu().double().numpy()
+    worst = 0.0
+    for h in (0, 6, 15):
+        rows = _sample_rows(w.T, rng, [w.window - 2, w.window - 1, w.window, w.window + 1])
+        sl = {k: x[k][0, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
+        ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], lam_ref[h],
+                                         True, rows, window=w.window)
+        worst = max(worst, maxerr(out[0, h, rows], ref))
+    say(f"workload {name}: max err {worst:.3e}")
+    del x, out
+    torch.cuda.empty_cache()
+    assert worst <= TOL[w.dtype]
+
+
+def test_workload_decode_ragged_l64k():
+    """B32 H16 L65536 D64 with the bench's seeded lengths: sampled (b, h)."""
+    name = "decode_ragged_l64k"
+    w = WORKLOADS[name]
+    x = make_workload(name, DEV)
+    li = da.diffattn_lambda_init(w.layer)
+    lam = da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], li)
+    say(f"workload {name}: launching")
+    out = da.diffattn_decode_ragged(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, x["lengths"],
+                                    num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    lam_ref = oracle.reparam_lambda(x["lq1"].cpu(), x["lk1"].cpu(), x["lq2"].cpu(), x["lk2"].cpu(),
+                                    oracle.lambda_init_schedule(w.layer))
+    lengths = x["lengths"].cpu().numpy()
+    worst = 0.0
+    for (b, h) in ((0, 0), (3, 9), (17, 15), (int(np.argmin(lengths)), 4), (int(np.argmax(lengths)), 11)):
+        n = int(lengths[b])
+        sl = {k: x[k][b:b + 1, h:h + 1].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
+        ref = oracle.diff_attention_decode_ragged(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"],
+                                                  lam_ref[h:h + 1], np.array([n]))
+        worst = max(worst, maxerr(out[b:b + 1, h:h + 1], ref))
+    say(f"workload {name}: max err {worst:.3e}")
+    del x, out
+    torch.cuda.empty_cache()
+    assert worst <= TOL[w.dtype]
