@@ -41,7 +41,7 @@ METRIC = "DiffAttn fwd TFLOP/s (bf16 causal T=4k/32k) & % MFMA peak; decode HBM 
 PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
 PRIMARY = "prefill_t4k_causal"
 OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k", "v2_prefill_t4k", "v2_decode_l64k",
-          "bwd_t4k_causal", "prefill_t32k_window4k", "decode_ragged_l64k"]
+          "bwd_t4k_causal", "bwd_t4k_d128", "prefill_t32k_window4k", "decode_ragged_l64k"]
 CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
 KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip", "v2_decode": "decode.hip"}
 KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel",

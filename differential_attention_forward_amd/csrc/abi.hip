@@ -347,7 +347,7 @@ namespace {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool train_sizes_ok(int B, int H, int T, int D) {
-  if (B < 1 || H < 1 || T < 1 || (D != 32 && D != 64)) return false;
+  if (B < 1 || H < 1 || T < 1 || (D != 32 && D != 64 && D != 128)) return false;
   return (long long)B * H <= 0x7fffffffLL && (long long)T * 2 * D <= 0x7fffffffLL;
 }
 

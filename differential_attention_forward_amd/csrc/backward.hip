@@ -63,9 +63,12 @@ namespace {
 //  64-byte rows (D = 32): a row is one group of four columns and the row
 //  modulo 4 picks its quarter of the banks; bits 2, 3 give the four rows of a
 //  quarter distinct columns (transposing reads cover four whole rows).
+//  512-byte rows (2D = 256): a row spans the banks twice; the 256-byte
+//  pattern applied to the low four bits of the column index.
 template <int PITCH>
 __device__ inline int swzb(int row) {
-  static_assert(PITCH == 64 || PITCH == 128 || PITCH == 256, "row pitch of 64, 128 or 256 bytes");
+  static_assert(PITCH == 64 || PITCH == 128 || PITCH == 256 || PITCH == 512,
+                "row pitch of 64, 128, 256 or 512 bytes");
   return PITCH == 64    ? ((row >> 2) & 3)
          : PITCH == 128 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3))
                         : (((row & 3) << 2) | ((row >> 2) & 3));
@@ -539,7 +542,7 @@ __device__ __forceinline__ void kv_body(const BwdArgs& a, char* smem, int w) {
 // workgroups 2w (dK1, dK2) and 2w + 1 (dV), on the same XCD (they stage the
 // same query tiles).
 template <int D, int NW, int NSTAGE, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2))) void bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[CfgKV<D, NW, NSTAGE>::SMEM];
   const int nkt = (a.T + CfgKV<D, NW, NSTAGE>::BK - 1) / CfgKV<D, NW, NSTAGE>::BK;
   const int w2 = xcd_remap(blockIdx.x, 2 * a.B * a.H * nkt);
@@ -800,9 +803,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
   else bwd_prep_kernel<D, false><<<gp, 256, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int KNW = 4, QNW = 8;
+  // D = 128: a q wave holds 128 accumulators and 128 fragment registers, one
+  // wave per SIMD (four-wave workgroups); LDS stages of 64-65 KiB, two of them
+  constexpr int KNW = 4, QNW = D >= 128 ? 4 : 8;
   constexpr int KST = 2;  // two stages: two kv workgroups per CU
-  constexpr int QST = 3;
+  constexpr int QST = D >= 128 ? 2 : 3;
   const int nkt = (a.T + 32 * KNW - 1) / (32 * KNW);
   bwd_kv_kernel<D, KNW, KST, CAUSAL><<<2 * a.B * a.H * nkt, KNW * 64, 0, stream>>>(a);
   e = hipGetLastError();
@@ -820,6 +825,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, bool headnorm, hipStream_t stream) {
   if (D == 32) return causal ? launch_bwd_d<32, true>(a, headnorm, stream) : launch_bwd_d<32, false>(a, headnorm, stream);
   if (D == 64) return causal ? launch_bwd_d<64, true>(a, headnorm, stream) : launch_bwd_d<64, false>(a, headnorm, stream);
+  if (D == 128) return causal ? launch_bwd_d<128, true>(a, headnorm, stream) : launch_bwd_d<128, false>(a, headnorm, stream);
   return hipErrorInvalidValue;
 }
 

@@ -312,7 +312,7 @@ diffattn_status diffattn_v2_decode(int dtype, int B, int H, int Hkv, int L, int 
  * The paperleet page "Differential Transformer Attention" asks for gradients
  * through both Q/K branches, the value and the coefficient lambda, and
  * through the four re-parameterisation vectors of lambda.  These entry points
- * support bf16 tensors with D = 32 or 64.
+ * support bf16 tensors with D = 32, 64 or 128.
  *
  * Bytes of the saved-state buffer diffattn_fwd_train fills and diffattn_bwd
  * reads: 2 * B*H*T*2D*4 + B*H*2*T*4 (fp32 per-map outputs A1 V and A2 V, then
@@ -322,11 +322,11 @@ diffattn_status diffattn_v2_decode(int dtype, int B, int H, int Hkv, int L, int 
 size_t diffattn_train_saved_bytes(int B, int H, int T, int D);
 
 /*
- * diffattn_fwd (same arguments and output, bf16 only, D = 32 or 64) that also
+ * diffattn_fwd (same arguments and output, bf16 only, D = 32, 64 or 128) that also
  * writes the saved state the backward pass needs into `saved` (at least
  * diffattn_train_saved_bytes bytes, 16-byte aligned, disjoint from every
  * input and from out).  The output is identical to diffattn_fwd's.
- * Errors: as diffattn_fwd; ERR_UNSUPPORTED for fp32 or D other than 32, 64;
+ * Errors: as diffattn_fwd; ERR_UNSUPPORTED for fp32 or D other than 32, 64, 128;
  * ERR_WORKSPACE when saved_bytes is too small.
  */
 diffattn_status diffattn_fwd_train(int dtype, int B, int H, int T, int D, const void* q1,
@@ -367,7 +367,7 @@ size_t diffattn_bwd_workspace_bytes(int B, int H, int T, int D);
  * Errors: ERR_INVALID (null tensor pointer, B/H/T < 1, headnorm with eps <= 0,
  * only some of the vector pointers, Dl < 1 with vectors, any output
  * overlapping an input, another output or the workspace), ERR_UNSUPPORTED
- * (dtype other than bf16, D other than 32 or 64, misalignment, sizes),
+ * (dtype other than bf16, D other than 32, 64 or 128, misalignment, sizes),
  * ERR_WORKSPACE (saved_bytes or workspace too small), ERR_HIP.
  */
 diffattn_status diffattn_bwd(int dtype, int B, int H, int T, int D, const void* q1, const void* k1,

@@ -310,7 +310,7 @@ def test_training_sizes(L):
     ws = (b * h * t * 2 * d * 2 + 255) // 256 * 256 + (b * h * 4 * tp * 4 + 255) // 256 * 256 + b * h * 2 * 4
     assert da.diffattn_bwd_workspace_bytes(b, h, t, d) == ws
     assert da.diffattn_train_saved_bytes(1, 1, 8, 32) == 2 * 8 * 64 * 4 + 2 * 8 * 4
-    for args in ((0, 1, 8, 64), (1, 1, 0, 64), (1, 1, 8, 16), (1, 1, 8, 128)):
+    for args in ((0, 1, 8, 64), (1, 1, 0, 64), (1, 1, 8, 16), (1, 1, 8, 96)):
         assert da.diffattn_train_saved_bytes(*args) == 0
         assert da.diffattn_bwd_workspace_bytes(*args) == 0
 
@@ -327,7 +327,7 @@ def test_fwd_train_validation(L):
     assert fwdt(L, ptrs=[P(0), None] + [P(i) for i in range(2, 8)]) == INVALID
     assert fwdt(L, T=0) == INVALID
     assert fwdt(L, dtype=F32) == UNSUPPORTED
-    for d in (16, 128):
+    for d in (16, 96):
         assert fwdt(L, D=d) == UNSUPPORTED
     assert fwdt(L, saved_bytes=da.diffattn_train_saved_bytes(1, 2, 8, 64) - 1) == WORKSPACE
     bad = [P(i) for i in range(8)]
@@ -364,7 +364,7 @@ def test_bwd_validation(L):
     assert bwd(L, vecs=vecs, dvecs=[P(24), P(25), None, P(27)]) == INVALID   # some, not all
     assert bwd(L, vecs=vecs, dvecs=dvecs, Dl=0) == INVALID
     assert bwd(L, dtype=F32) == UNSUPPORTED
-    assert bwd(L, D=128) == UNSUPPORTED
+    assert bwd(L, D=96) == UNSUPPORTED
     assert bwd(L, ins=[P(0), P(1, 8)] + [P(k) for k in range(2, 8)]) == UNSUPPORTED
     assert bwd(L, vecs=[P(20), P(21, 2), P(22), P(23)], dvecs=dvecs) == UNSUPPORTED
     assert bwd(L, saved_bytes=da.diffattn_train_saved_bytes(1, 2, 8, 64) - 1) == WORKSPACE

@@ -22,7 +22,8 @@ the head norm with lambda > 1 it can be far smaller than its terms, so the
 bf16-weighted outputs can reach a few percent of max |dQ|.  The draw of the
 T = 2 causal head-norm case with seed 3065 shows dQ1 at 3.6% of its maximum
 (0.0045 of 0.126), with these kernels and with the earlier ones alike; the
-sweep's D = 64 draws are seeds 3000 + i, its D = 32 draws 3032 + i.
+sweep's D = 64 draws are seeds 3000 + i, its D = 32 and D = 128 draws
+3032 + i and 3128 + i.
 """
 
 import numpy as np
@@ -103,14 +104,14 @@ def check_grads(got, ref, tag, dl_rss=None):
 SWEEP_T = [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 257]
 
 
-@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("headnorm", [False, True])
 @pytest.mark.parametrize("causal", [True, False])
 def test_bwd_sweep(causal, headnorm, D):
     lam = torch.tensor([0.35, 1.3], dtype=torch.float32)
     for i, T in enumerate(SWEEP_T):
         say(f"bwd D={D} T={T} causal={causal} headnorm={headnorm}")
-        off = 32 if D == 32 else 0
+        off = {32: 32, 64: 0, 128: 128}[D]
         x = prefill_inputs(1, 2, T, D, "bf16", seed=3000 + i + off)
         dout = grad_output((1, 2, T, 2 * D), seed=3100 + i + off)
         out, _, got = run_train(x, lam, dout, causal, headnorm, lambda_init=0.6)
@@ -120,7 +121,7 @@ def test_bwd_sweep(causal, headnorm, D):
         check_grads(got, ref, f"  T={T}", rss)
 
 
-@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("D", [32, 64, 128])
 def test_fwd_train_output_and_saved_state(D):
     """The training forward's output is the inference forward's, bit for bit;
     the saved per-map outputs and log-sum-exp match the oracle's maps."""
@@ -196,7 +197,7 @@ def test_bwd_repeatable_bitwise():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("D,T", [(64, 8192), (32, 4096)])
+@pytest.mark.parametrize("D,T", [(64, 8192), (32, 4096), (128, 2048)])
 def test_bwd_key_gradient_identity_long(D, T):
     """At a size the oracle cannot materialise: sum over keys of dK is zero per
     map (softmax is unchanged by a per-row score shift), up to the bf16

@@ -49,6 +49,8 @@ problem statement's configurations):
   bwd_t4k_causal            backward of prefill_t4k_causal's shape (B2 H16
                             T4096 D64 causal bf16, head norm, lambda_init 0.8),
                             seed 8, lambda_h ~ U[0.2, 0.8], dL/dOut ~ N(0,1)
+  bwd_t4k_d128              the same flop count at head width 128 (B2 H8
+                            T4096 D128), seed 12
   prefill_t32k_window4k     B1 H16 T32768 D64 causal bf16 with a 4096-key
                             sliding window, seed 9, lambda = 0.8
   decode_ragged_l64k        decode_l64k's shape with per-sequence lengths
@@ -112,6 +114,8 @@ WORKLOADS = {
         Workload("v2_decode_l64k", "v2_decode", 32, 32, 65536, 128, "bf16", 7,
                  lam_uniform=(0.2, 0.8), Hkv=8),
         Workload("bwd_t4k_causal", "bwd", 2, 16, 4096, 64, "bf16", 8, causal=True,
+                 headnorm=True, lambda_init=0.8, lam_uniform=(0.2, 0.8)),
+        Workload("bwd_t4k_d128", "bwd", 2, 8, 4096, 128, "bf16", 12, causal=True,
                  headnorm=True, lambda_init=0.8, lam_uniform=(0.2, 0.8)),
         Workload("prefill_t32k_window4k", "window_prefill", 1, 16, 32768, 64, "bf16", 9,
                  causal=True, lam_fixed=0.8, lambda_init=0.8, window=4096),
