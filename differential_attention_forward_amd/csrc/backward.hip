@@ -18,7 +18,8 @@
 // Scores are formed in base-2 units as in the forward (one operand pre-scaled
 // by log2(e)/sqrt(D) and rounded to bf16), and the per-row statistics are
 // kept negated, [-lse1, -lse2, -D1, -(lam D1 + D2)], so that they enter the
-// score and dP products as the MFMA accumulator input: the products come out
+// score and dP products as the MFMA accumulator input (the q kernel adds -lse
+// in the exponent instead, one value per lane there): the products come out
 // as s - lse and dP - D1, and per element only
 //   p1 = 2^s1', p2 = 2^s2', dS1 = p1 dP', dS2 = p2 (-lam dP' - (lam D1 + D2))
 // remain (dP' = dP - D1).
