@@ -141,8 +141,8 @@ def time_steps(torch, step, steps, warmup):
 
 
 def time_kernel(torch, launch, steps):
-    """Average duration of one launch, from events recorded around each launch
-    on the current (launch) stream."""
+    """Mean, median and minimum duration of one launch, from events recorded
+    around each launch on the current (launch) stream."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     torch.cuda.synchronize()
@@ -151,7 +151,8 @@ def time_kernel(torch, launch, steps):
         launch()
         b.record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(t) / steps, t[len(t) // 2], t[0]
 
 
 def bench_workload(torch, da, name, steps, warmup):
@@ -234,7 +235,7 @@ def bench_workload(torch, da, name, steps, warmup):
 
     log(f"[bench] {name}: {warmup} warmup + {steps} timed steps")
     ms, wall = time_steps(torch, step, steps, warmup)
-    kern_ms = time_kernel(torch, kernel, steps)
+    kern_ms, kern_med, kern_min = time_kernel(torch, kernel, steps)
     log(f"[bench] {name}: {ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
     if w.kind in ("prefill", "v2_prefill", "bwd", "window_prefill"):
         work = prefill_flops(w)
@@ -258,7 +259,8 @@ def bench_workload(torch, da, name, steps, warmup):
                 "algorithmic_per_launch": work}
         unit = "GB/s"
     res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
-           "kernel_ms": round(kern_ms, 5), "wall_s": round(wall, 4), "roofline": roof,
+           "kernel_ms": round(kern_ms, 5), "kernel_ms_median": round(kern_med, 5),
+           "kernel_ms_min": round(kern_min, 5), "wall_s": round(wall, 4), "roofline": roof,
            "shape": {"B": w.B, "H": w.H, ("L" if w.kind.endswith("decode") else "T"): w.T, "D": w.D,
                      "causal": False if w.kind.endswith("decode") else w.causal,
                      "headnorm": w.headnorm, "dtype": w.dtype, **({"Hkv": w.Hkv} if w.Hkv else {}),
@@ -321,8 +323,14 @@ def cpu_baseline(torch, name, budget_s=12.0):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     del x
     torch.cuda.empty_cache()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{heads} of {w.B * w.H} (b,h) heads of {name}, all {w.T} query rows, "
                       f"float64 numpy, {dt:.1f} s wall, host os.cpu_count()={os.cpu_count()}"}
 
