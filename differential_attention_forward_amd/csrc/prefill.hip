@@ -1025,7 +1025,16 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
   if (dtype == 1 && a.window > 0) {  // causal sliding window (bf16)
     switch (D) {
       case 32: return launch_window<32, 1, 8, 3, false>(a, headnorm, stream);
-      case 64: return launch_window<64, 1, 8, 3, true>(a, headnorm, stream);
+      case 64: {
+        // Every row sees up to `window` keys, so workgroups carry nearly equal
+        // work: with enough 256-row workgroups to fill the chip twice, both
+        // maps per wave (each V fragment feeds two P.V products) win, 6.7%
+        // at T = 32768, W = 4096, 16 heads; with few, the finer one-map
+        // 128-row workgroups.
+        const long wg256 = (long)a.B * a.H * ((a.T + 255) / 256);
+        if (wg256 >= 2 * compute_units()) return launch_window<64, 1, 8, 3, false>(a, headnorm, stream);
+        return launch_window<64, 1, 8, 3, true>(a, headnorm, stream);
+      }
       case 128: return launch_window<128, 1, 8, 2, true>(a, headnorm, stream);
     }
     return hipErrorInvalidValue;

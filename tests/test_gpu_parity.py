@@ -424,6 +424,25 @@ def test_fwd_window_long_rows():
                 assert maxerr(out[b, h, rows], ref) <= TOL["bf16"], (T, W, b, h)
 
 
+def test_fwd_window_many_heads():
+    # enough 256-row workgroups (4 x 32 x 4 = 512) for the two-maps-per-wave
+    # window configuration: whole heads against the oracle, a ragged T
+    B, H, T, W = 4, 32, 1000, 300
+    x = prefill_inputs(B, H, T, 64, "bf16", seed=43)
+    lam = torch.linspace(-0.2, 1.2, H)
+    say(f"fwd window bf16 D=64 B={B} H={H} T={T} W={W}")
+    for headnorm in (False, True):
+        out = da.diffattn_fwd_window(*(to_dev(x)[k] for k in ("q1", "k1", "q2", "k2", "v")), lam.to(DEV), W,
+                                     headnorm=headnorm, lambda_init=0.8, eps=1e-5)
+        torch.cuda.synchronize()
+        for (b, h) in ((0, 0), (1, 17), (3, 31)):
+            ref = oracle.diff_attention_rows(x["q1"][b, h], x["k1"][b, h], x["q2"][b, h], x["k2"][b, h],
+                                             x["v"][b, h], float(lam[h]), True, np.arange(T), window=W)
+            if headnorm:
+                ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+            assert maxerr(out[b, h], ref) <= TOL["bf16"], (b, h, headnorm)
+
+
 # ---- ragged decode: sequence b sees its first lengths[b] cache rows -----------
 
 @pytest.mark.parametrize("headnorm", [False, True])
