@@ -295,6 +295,49 @@ def bench_same_size_attention(torch, da, name, steps, warmup, diff_ms):
             "differential_over_standard_time": round(diff_ms / ms, 4)}
 
 
+def bench_fused_views(torch, da, name, steps, warmup):
+    """The named causal workload with Q1|Q2 and K1|K2 as the halves of fused
+    token-major [B, T, H, 2D] projections, V read from and the output written
+    to token-major [B, T, H, 2D] buffers, through the strided entry point (no
+    copies), against what the dense entry point costs once the four views are
+    copied out to dense tensors first."""
+    from workloads import WORKLOADS, make_workload
+
+    w = WORKLOADS[name]
+    x = make_workload(name, "cuda")
+    li = w.lambda_init if w.lambda_init is not None else da.diffattn_lambda_init(w.layer)
+    lam = da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], li) if "lam" not in x else x["lam"]
+
+    def fused(a, b):
+        buf = torch.cat([a.permute(0, 2, 1, 3), b.permute(0, 2, 1, 3)], dim=-1).contiguous()
+        return buf[..., :w.D].permute(0, 2, 1, 3), buf[..., w.D:].permute(0, 2, 1, 3)
+
+    q1, q2 = fused(x["q1"], x["q2"])
+    k1, k2 = fused(x["k1"], x["k2"])
+    v = x["v"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    out = torch.empty((w.B, w.T, w.H, 2 * w.D), device="cuda", dtype=x["v"].dtype).permute(0, 2, 1, 3)
+    dense_out = torch.empty_like(x["v"])
+    del x
+
+    def strided():
+        da.diffattn_fwd_strided(q1, k1, q2, k2, v, lam, causal=w.causal, headnorm=w.headnorm,
+                                lambda_init=li, eps=w.eps, out=out)
+
+    def copy_then_dense():
+        da.diffattn_fwd(q1, k1, q2, k2, v, lam, causal=w.causal, headnorm=w.headnorm, lambda_init=li,
+                        eps=w.eps, out=dense_out)  # the binding makes the inputs contiguous first
+
+    ms, _ = time_steps(torch, strided, steps, warmup)
+    ms_copy, _ = time_steps(torch, copy_then_dense, steps, warmup)
+    work = prefill_flops(w)
+    log(f"[bench] fused-projection views for {name}: {ms:.4f} ms/step strided, {ms_copy:.4f} with copies")
+    del q1, q2, k1, k2, v, out, dense_out
+    torch.cuda.empty_cache()
+    return {"workload": f"{name} on token-major fused-projection views (strided entry point)",
+            "value": round(work / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+            "ms_per_step_copy_then_dense": round(ms_copy, 5)}
+
+
 def cpu_baseline(torch, name, budget_s=12.0):
     """The float64 oracle, as it stands, on the host cores: whole heads of the
     workload (every query row of each sampled (b, h)) until ~budget_s seconds."""
@@ -382,6 +425,8 @@ def main():
             diff_ms = (primary if name == args.workload else also[name])["ms_per_step"]
             also[f"same_size_attention_{name}"] = bench_same_size_attention(
                 torch, da, name, args.steps, args.warmup, diff_ms)
+        also["fused_views_prefill_t4k_causal"] = bench_fused_views(
+            torch, da, "prefill_t4k_causal", args.steps, args.warmup)
     cpu = None
     w = WORKLOADS[args.workload]
     if not args.no_cpu_baseline and w.kind == "prefill":
