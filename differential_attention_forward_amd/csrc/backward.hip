@@ -575,7 +575,7 @@ struct CfgQ {
 };
 
 template <int D, int NW, int NSTAGE, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void bwd_q_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2))) void bwd_q_kernel(BwdArgs a) {
   using C = CfgQ<D, NW, NSTAGE>;
   constexpr int BC = C::BC;
   constexpr int DV = C::DV;
@@ -804,11 +804,13 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
   else bwd_prep_kernel<D, false><<<gp, 256, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // D = 128: a q wave holds 128 accumulators and 128 fragment registers, one
-  // wave per SIMD (four-wave workgroups); LDS stages of 64-65 KiB, two of them
-  constexpr int KNW = 4, QNW = D >= 128 ? 4 : 8;
+  // Four-wave workgroups with two LDS stages: two kv or q workgroups per CU
+  // (the q pass takes 16% less time than with one eight-wave workgroup at
+  // D = 64).  D = 128: a q wave holds 128 accumulators and 128 fragment
+  // registers, one wave per SIMD; LDS stages of 64-65 KiB.
+  constexpr int KNW = 4, QNW = 4;
   constexpr int KST = 2;  // two stages: two kv workgroups per CU
-  constexpr int QST = D >= 128 ? 2 : 3;
+  constexpr int QST = 2;
   const int nkt = (a.T + 32 * KNW - 1) / (32 * KNW);
   bwd_kv_kernel<D, KNW, KST, CAUSAL><<<2 * a.B * a.H * nkt, KNW * 64, 0, stream>>>(a);
   e = hipGetLastError();
