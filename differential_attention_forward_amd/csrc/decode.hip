@@ -370,10 +370,12 @@ hipError_t launch_d(const DecodeArgs& a, bool headnorm, hipStream_t stream) {
 // c - G; the other columns hold zero queries and are dropped), and the
 // weighted sums from O^T = V^T P^T, exactly the prefill's formulation
 // (scores in base-2 units with the reference as the accumulator input, lazy
-// rescale).  Each wave streams its own 32-key blocks (blocks w, w + 4, ...)
-// through a private double-buffered LDS slot filled by global -> LDS DMA,
-// waits on its own loads only (no workgroup barrier in the loop), and the
-// four waves' states are merged at the end into one record per (head, map).
+// rescale).  Each wave streams its own 32-key blocks (blocks w, w + 4, ...):
+// nontemporal 16-byte register loads run kPf blocks ahead, and each block is
+// written to a private LDS slot just before its fragments are read (the V
+// fragments need the transposing LDS read).  No workgroup barrier in the
+// loop; the four waves' states are merged at the end into one record per
+// (head, map).
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_v2_mma_kernel(DecodeArgs a) {
@@ -382,12 +384,13 @@ void decode_v2_mma_kernel(DecodeArgs a) {
   constexpr int CB = D / 32;
   constexpr int KB = 32 * D * 2;      // bytes of one 32-key block of K (or V)
   constexpr int CK = D / 8;           // 16-byte chunks per row
-  constexpr int RK = 64 / CK;         // rows per 1-KiB DMA segment
+  constexpr int RK = 64 / CK;         // rows per 1-KiB load segment
   constexpr int NSEG = KB / 1024;     // segments per block, per tensor
   constexpr int RS = 2 * (D + 2);
   constexpr float kTauSum = 256.0f;   // rescale trigger (p <= 2^8)
+  constexpr int kPf = 2;              // blocks in flight per wave, in registers
   static_assert(NR <= 32, "query columns");
-  __shared__ __attribute__((aligned(1024))) char smem[kWaves][2][2 * KB];
+  __shared__ __attribute__((aligned(1024))) char smem[kWaves][2 * KB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -401,7 +404,8 @@ void decode_v2_mma_kernel(DecodeArgs a) {
   const int chunk = (L + S - 1) / S;
   const int kb = min(L, split * chunk);
   const int ke = min(L, kb + chunk);
-  const int nblk = (ke - kb + 31) / 32;
+  // (uniform: every loop bound and branch below stays scalar)
+  const int nblk = __builtin_amdgcn_readfirstlane((ke - kb + 31) / 32);
   const bf16* __restrict__ K = scalar_ptr((const bf16*)a.k1 + (size_t)bg * L * D);
   const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + (size_t)bg * L * D);
 
@@ -420,19 +424,34 @@ void decode_v2_mma_kernel(DecodeArgs a) {
       for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)q[e] * sc);
     }
   }
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): q before the DMA starts
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): q before the cache loads start
 
-  // DMA of block j (keys kb + 32 j ..) into buffer `buf` of this wave's slot;
-  // rows past the chunk end load row ke - 1 (in bounds) and are masked
-  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
+  // Block j (keys kb + 32 j ..) is read with coalesced 16-byte loads: load
+  // sg of a lane takes row sg RK + lane / CK, 16-byte chunk
+  // (lane % CK) ^ swizzle(row), and stage() stores it at byte 16 lane of
+  // segment sg of the wave's slot, so the slot holds each row with its chunks
+  // permuted by the same swizzle the fragment reads undo.  Rows past the
+  // chunk end load row ke - 1 (in bounds) and are masked.
+  // (global address space: loads that the compiler counts on vmcnt alone)
+  typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+  u32x4 kr[kPf][NSEG], vr[kPf][NSEG];
+  auto load = [&](int j, u32x4 (&kk)[NSEG], u32x4 (&vv)[NSEG]) __attribute__((always_inline)) {
     const int key0 = kb + 32 * j;
-    char* sk = smem[wave][buf];
 #pragma unroll
     for (int sg = 0; sg < NSEG; ++sg) {
       const int r = sg * RK + lane / CK;
       const uint32_t row = (uint32_t)min(key0 + r, ke - 1);
-      dma16(K, row * (D * 2) + (((lane % CK) ^ swz_k<D>(r)) << 4), sk + sg * 1024);
-      dma16(V, row * (D * 2) + (((lane % CK) ^ swz_v<D>(r)) << 4), sk + KB + sg * 1024);
+      kk[sg] = __builtin_nontemporal_load((gu32x4*)(K + row * D + (((lane % CK) ^ swz_k<D>(r)) << 3)));
+      vv[sg] = __builtin_nontemporal_load((gu32x4*)(V + row * D + (((lane % CK) ^ swz_v<D>(r)) << 3)));
+    }
+  };
+  char* const sk = smem[wave];
+  const char* const sv = sk + KB;
+  auto stage = [&](const u32x4 (&kk)[NSEG], const u32x4 (&vv)[NSEG]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg) {
+      *(u32x4*)(sk + sg * 1024 + lane * 16) = kk[sg];
+      *(u32x4*)(sk + KB + sg * 1024 + lane * 16) = vv[sg];
     }
   };
 
@@ -451,18 +470,20 @@ void decode_v2_mma_kernel(DecodeArgs a) {
   const int v_sw = swz_v<D>(vkq);
   const int v_byte = (vq & 1) * 8;
 
-  if (wave < nblk) issue(wave, 0);
-  int buf = 0;
-  for (int j = wave; j < nblk; j += kWaves) {
-    const bool more = j + kWaves < nblk;
-    if (more) issue(j + kWaves, buf ^ 1);
+  // One block of the loop below: stage it, refill its registers kPf blocks
+  // ahead, compute.  Loads are issued whether or not their block exists (one
+  // past the chunk reads row ke - 1 again, from cache) so that every path
+  // issues them in the same order and each wait counts only the loads
+  // issued after the block's own.
+  auto block = [&](int j, u32x4 (&kk)[NSEG], u32x4 (&vv)[NSEG]) __attribute__((always_inline)) {
+    // the previous block's fragment reads are issued before these writes (a
+    // wave's LDS operations run in order), and these writes before the reads
+    // below
     asm volatile("" ::: "memory");
-    if (more) __builtin_amdgcn_s_waitcnt(((2 * NSEG) & 15) | ((((2 * NSEG) >> 4) & 3) << 14) | (7 << 4));
-    else __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0)
+    stage(kk, vv);
     asm volatile("" ::: "memory");
-    const char* sk = smem[wave][buf];
-    const char* sv = sk + KB;
-
+    load(j + kWaves * kPf, kk, vv);
+    if (j >= nblk) return;
     floatx16 s;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -526,14 +547,20 @@ void decode_v2_mma_kernel(DecodeArgs a) {
         const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
         acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[ks], acc[cb], 0, 0, 0);
       }
-    buf ^= 1;
+  };
+
+#pragma unroll
+  for (int p = 0; p < kPf; ++p) load(wave + kWaves * p, kr[p], vr[p]);
+  for (int j = wave; j < nblk; j += kWaves * kPf) {
+#pragma unroll
+    for (int p = 0; p < kPf; ++p) block(j + kWaves * p, kr[p], vr[p]);
   }
 
   // ---- merge the four waves' states; one record per (head, map) -------------
   const float ltot = swap_halves_sum(lsum);
   if (!started) mu = kNegInf;  // a wave with no block contributes nothing
   __syncthreads();              // every wave is done with its LDS slot
-  float* mw = (float*)&smem[0][0][0];  // [wave][column][D + 2]
+  float* mw = (float*)&smem[0][0];  // [wave][column][D + 2]
   if (l32 < NR) {
     float* row = mw + (wave * NR + l32) * (D + 2);
     if (hi == 0) {
