@@ -43,6 +43,12 @@ def test_lambda_init_matches_oracle(L):
         got = da.diffattn_lambda_init(layer)
         assert abs(got - oracle.lambda_init_schedule(layer)) <= 6e-8
     assert math.isnan(da.diffattn_lambda_init(0))
+    # the same hand-computed values that pin the oracle (fp32 result)
+    from tests.oracle_pins import LAMBDA_INIT_ROUNDED, LAMBDA_INIT_VALUES
+    for layer, val in LAMBDA_INIT_VALUES.items():
+        assert abs(da.diffattn_lambda_init(layer) - val) <= 1.5e-7, (layer, val)
+    for layer, val in LAMBDA_INIT_ROUNDED.items():
+        assert round(da.diffattn_lambda_init(layer), 3) == val
 
 
 def test_decode_split_helpers(L):

@@ -108,6 +108,16 @@ def _lambda_init_zero_based(layer):
     return 0.8 - 0.6 * math.exp(-0.3 * layer)
 
 
+def _lambda_init_decay_02(layer):
+    # decay rate 0.2 instead of 0.3
+    return 0.8 - 0.6 * math.exp(-0.2 * (layer - 1))
+
+
+def _lambda_init_amplitude_05(layer):
+    # amplitude 0.5 instead of 0.6 (l = 1 would give 0.3)
+    return 0.8 - 0.5 * math.exp(-0.3 * (layer - 1))
+
+
 def _norm_no_scale(o, lambda_init, eps):
     o = od._f64(o)
     return o / np.sqrt(np.mean(o * o, -1, keepdims=True) + eps)
@@ -214,6 +224,8 @@ MUTANTS = {
     "lambda_plus": ("reparam_lambda", _lambda_plus),
     "lambda_drops_init": ("reparam_lambda", _lambda_no_init),
     "lambda_init_zero_based": ("lambda_init_schedule", _lambda_init_zero_based),
+    "lambda_init_decay_02": ("lambda_init_schedule", _lambda_init_decay_02),
+    "lambda_init_amplitude_05": ("lambda_init_schedule", _lambda_init_amplitude_05),
     "norm_without_scale": ("head_rmsnorm", _norm_no_scale),
     "norm_with_mean": ("head_rmsnorm", _norm_layernorm),
     "norm_eps_outside_sqrt": ("head_rmsnorm", _norm_eps_outside),
