@@ -135,6 +135,32 @@ __device__ inline floatx16 splat16(float x) {
   return v;
 }
 
+// Probabilities 2^s of one 32x32 score block as a lane holds it (16 keys of
+// one query), rounded to bf16 into the B-operand layout of the P.V MFMA, and
+// the lane's fp32 sum of the unrounded values (a pairwise tree).  The sum is
+// formed with plain fp32 adds: v_dot2c_f32_bf16 over the rounded values would
+// take one instruction per pair but shares the matrix pipe, and stalls for
+// the length of the other wave's MFMA stream on the same SIMD.
+__device__ inline float expo16(const floatx16& s, bf16x8 (&pk)[2]) {
+  float a[4];  // four running partial sums, so few values stay live
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float pa = __builtin_amdgcn_exp2f(s[2 * j]);
+    const float pb = __builtin_amdgcn_exp2f(s[2 * j + 1]);
+    const bf16x2 pw = {(bf16)pa, (bf16)pb};
+    pk[j >> 2][2 * (j & 3)] = pw[0];
+    pk[j >> 2][2 * (j & 3) + 1] = pw[1];
+    if (j < 2) {
+      a[2 * j] = pa;
+      a[2 * j + 1] = pb;
+    } else {
+      a[(2 * j) & 3] += pa;
+      a[(2 * j + 1) & 3] += pb;
+    }
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
 __device__ inline float swap_halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -628,7 +628,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   const int v_chunk = 2 * ((lane >> 4) & 1) + (vq >> 1);  // + 4*cb
   const int v_sw = swz_v<C::DV>(vkq);  // rows 16 ks + 4 hi + vkq (+ 8): same swizzle
   const int v_byte = (vq & 1) * 8;
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
   // A 32-key block kb of tile kt takes part only if it holds a key this wave
   // may attend to.
@@ -676,22 +675,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   };
 
   // probabilities 2^(s - mu) rounded to bf16 (the B operand of the P.V
-  // product) and each lane's sum of those rounded values over its 16 keys;
+  // product) and each lane's sum over its 16 keys.  One-map waves sum the
+  // fp32 values with adds (expo16); two-map waves, whose registers are
+  // short, sum the rounded pairs with v_dot2 as they are produced.
   auto expo_one = [&](const floatx16& s, bf16x8 (&pk)[2], float& bsum) __attribute__((always_inline)) {
-    float b = 0.0f;
+    if constexpr (C::NBR * NQB == 1) {
+      bsum = expo16(s, pk);
+    } else {
+      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+      float b = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pa = __builtin_amdgcn_exp2f(s[8 * ks + 2 * j]);
-        const float pb = __builtin_amdgcn_exp2f(s[8 * ks + 2 * j + 1]);
-        const bf16x2 pw = {(bf16)pa, (bf16)pb};
-        b = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, b, false);
-        pk[ks][2 * j] = pw[0];
-        pk[ks][2 * j + 1] = pw[1];
-      }
+        for (int j = 0; j < 4; ++j) {
+          const float pa = __builtin_amdgcn_exp2f(s[8 * ks + 2 * j]);
+          const float pb = __builtin_amdgcn_exp2f(s[8 * ks + 2 * j + 1]);
+          const bf16x2 pw = {(bf16)pa, (bf16)pb};
+          b = __builtin_amdgcn_fdot2_f32_bf16(pw, ones, b, false);
+          pk[ks][2 * j] = pw[0];
+          pk[ks][2 * j + 1] = pw[1];
+        }
+      bsum = b;
     }
-    bsum = b;
   };
   auto expo = [&](floatx16 (&s)[C::NBR][NQB], bf16x8 (&pk)[C::NBR][NQB][2], float (&bsum)[C::NBR][NQB])
       __attribute__((always_inline)) {
@@ -920,6 +925,450 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   }
 }
 
+// ============================================================================
+// bf16 two-map prefill with the two waves of each SIMD in opposite phases
+// ============================================================================
+//
+// Per 32-key block a wave has a matrix phase (the P.V products of the previous
+// block, then the score products of this block: 24 MFMAs at D = 64) and a
+// vector phase (mask, exponentials, bf16 rounding, row sums, the rare
+// rescale, then the V fragments of this block read ahead for the next matrix
+// phase).  Eight waves share a compute unit, two per SIMD.  If both waves of a
+// SIMD reach their vector phase together, the matrix core idles meanwhile;
+// here the second wave of each SIMD starts one phase late (one extra barrier
+// before its first phase, the first wave one extra after its last) and a
+// workgroup barrier separates consecutive phases, so while one wave issues
+// MFMAs the other runs its exponentials.  The matrix-phase wave runs at raised
+// issue priority.
+//
+// Tiles of 64 keys (K1, K2, V) go global -> LDS by DMA into a four-stage ring.
+// Block b reads its K tile in its matrix phase and its V tile at the end of
+// its vector phase, so tile t is read in the wave's phases 4t .. 4t+3, i.e.
+// between barriers 4t and 4t+5 counting both wave groups.  A wave's share of
+// tile u is issued in two halves at the start of the vector phases of blocks
+// 2u-5 and 2u-4 (phases 4u-9 and 4u-7) into stage u % 4, after every read of
+// tile u-4; the vector phase has slack, the matrix phase none, and spreading
+// the issue keeps four waves from queueing all their loads at one moment.
+// Each wave waits for its own loads of tile u at the end of the matrix phase
+// of block 2u-1 (phase 4u-2), before the barrier that publishes it for phase
+// 4u.
+template <int D, bool CAUSAL, bool HEADNORM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(FwdArgs a) {
+  constexpr int NW = 8, NSTAGE = 4;
+  using C = CfgB<D, 1, NW, NSTAGE, false>;
+  constexpr int BC = C::BC;
+  constexpr int SEGW = C::NSEG / NW;
+  static_assert(C::NSEG % NW == 0 && SEGW % 2 == 0 && SEGW <= 4, "every wave issues the same even number of tile loads");
+  static_assert(2 * SEGW <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  __shared__ int simd_of[NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int T = a.T;
+
+  const int nqt = (T + C::BR - 1) / C::BR;
+  const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
+  const int bh = __builtin_amdgcn_readfirstlane(w / nqt);
+  const int qi = __builtin_amdgcn_readfirstlane(w % nqt);
+  const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
+  const int h = bh % a.H;
+  const int bb = bh / a.H;
+  const size_t o_off = (size_t)bh * T * C::DV;
+  const bf16* __restrict__ Q1 = (const bf16*)a.q1 + (bb * a.sb[0] + h * a.sh[0]);
+  const bf16* __restrict__ Q2 = (const bf16*)a.q2 + (bb * a.sb[2] + h * a.sh[2]);
+  const bf16* __restrict__ K1 = scalar_ptr((const bf16*)a.k1 + (bb * a.sb[1] + h * a.sh[1]));
+  const bf16* __restrict__ K2 = scalar_ptr((const bf16*)a.k2 + (bb * a.sb[3] + h * a.sh[3]));
+  const bf16* __restrict__ V = scalar_ptr((const bf16*)a.v + (bb * a.sb[4] + h * a.sh[4]));
+  const int rq[2] = {a.sr[0], a.sr[2]};
+  const uint32_t rk_b[2] = {2u * (uint32_t)a.sr[1], 2u * (uint32_t)a.sr[3]};
+  const uint32_t rv_b = 2u * (uint32_t)a.sr[4];
+
+  const int q_tile0 = qt * C::BR;
+  const int q0 = q_tile0 + wave * 32;
+  const int q_last = min(q0 + 32, T) - 1;
+  const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
+  const int ntiles = (k_end + BC - 1) / BC;
+  const int nblk = (k_end + 31) / 32;
+  const float sc = a.score_scale;
+  const float lamv = head_lambda(a, h, qt, bh);
+  asm volatile("" ::"v"(lamv));
+
+  // ---- tile loads (as in fwd_bf16_kernel) -------------------------------------
+  constexpr int CK = D / 8, RK = 64 / CK, CV = C::DV / 8, RV = 64 / CV;
+  const int rl_k = lane / CK, rl_v = lane / CV;
+  // this wave's load slot i of tile kt: segment wave + i NW of the stage,
+  // K1 and K2 segments first, then V.  When every wave's slot i is of the
+  // same kind (the K segment count a multiple of NW), the kind is known at
+  // compile time and the issue has no branches.
+  auto issue_slot = [&](int kt, auto slot) __attribute__((always_inline)) {
+    constexpr int i = decltype(slot)::value;
+    char* sb = smem + (kt & (NSTAGE - 1)) * C::STAGE;
+    const int key0 = kt * BC;
+    const int seg = wave + i * NW;
+    constexpr bool uniform_kind = C::KSEG % NW == 0;
+    const bool isk = uniform_kind ? (i * NW < 2 * C::KSEG) : (seg < 2 * C::KSEG);
+    if (isk) {
+      const int which = uniform_kind ? (i * NW) / C::KSEG : seg / C::KSEG;
+      const int g = seg % C::KSEG;
+      const int r = g * RK + rl_k;
+      const int c = (lane % CK) ^ swz_k<D>(r);
+      const uint32_t row = (uint32_t)min(key0 + r, T - 1);
+      dma16(which ? K2 : K1, row * rk_b[which] + c * 16, sb + which * C::KBYTES + g * 1024);
+    } else {
+      const int g = seg - 2 * C::KSEG;
+      const int r = g * RV + rl_v;
+      const int c = (lane % CV) ^ swz_v<C::DV>(r);
+      const uint32_t row = (uint32_t)min(key0 + r, T - 1);
+      dma16(V, row * rv_b + c * 16, sb + 2 * C::KBYTES + g * 1024);
+    }
+  };
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    issue_slot(kt, std::integral_constant<int, 0>{});
+    if constexpr (SEGW > 1) issue_slot(kt, std::integral_constant<int, 1>{});
+    if constexpr (SEGW > 2) issue_slot(kt, std::integral_constant<int, 2>{});
+    if constexpr (SEGW > 3) issue_slot(kt, std::integral_constant<int, 3>{});
+  };
+  // wait until at most n (0, 1 or 2) tiles of this wave's loads are in flight
+  auto wait_tiles = [&](int n) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    if (n >= 2) __builtin_amdgcn_s_waitcnt(((2 * SEGW) & 15) | ((((2 * SEGW) >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+    else if (n == 1) __builtin_amdgcn_s_waitcnt((SEGW & 15) | (((SEGW >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+  };
+  auto phase_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T), pre-scaled by log2(e)/sqrt(D) --
+  bf16x8 qf[2][C::KSTEPS];
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    const int query = q0 + l32;
+    const bool ok = query < T;
+    const bf16* src = (br ? Q2 : Q1) + (size_t)min(query, T - 1) * rq[br];
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
+      raw = ok ? raw : u32x4{0u, 0u, 0u, 0u};
+      const bf16x8 q = __builtin_bit_cast(bf16x8, raw);
+      bf16x8 qs;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qs[e] = (bf16)((float)q[e] * sc);
+      qf[br][ks] = qs;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): Q in registers
+
+  // prologue: tiles 0, 1, 2; tile 0 is published by the barrier below, which
+  // also publishes each wave's SIMD number
+  issue(0);
+  if (1 < ntiles) issue(1);
+  if (2 < ntiles) issue(2);
+  if (lane == 0) simd_of[wave] = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3;  // HW_ID.SIMD_ID
+  wait_tiles(min(ntiles, 3) - 1);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only: the SIMD number is in LDS
+  phase_barrier();
+  // the later of the two waves on this SIMD (by wave number) runs one phase late
+  int late = 0;
+  {
+    const int mine = simd_of[wave];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) late += (j < wave && simd_of[j] == mine) ? 1 : 0;
+    late = __builtin_amdgcn_readfirstlane(late & 1);
+  }
+
+  floatx16 acc[2][C::CB];
+  float mu[2], lsum[2];
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    mu[br] = 0.0f;
+    lsum[br] = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[br][cb][r] = 0.0f;
+  }
+
+  const int k_rd = l32 * (2 * D);
+  const int swk = swz_k<D>(l32);
+  const int vq = lane & 3;
+  const int vkq = (lane >> 2) & 3;
+  const int v_row = 4 * hi + vkq;
+  const int v_chunk = 2 * ((lane >> 4) & 1) + (vq >> 1);
+  const int v_sw = swz_v<C::DV>(vkq);
+  const int v_byte = (vq & 1) * 8;
+
+  auto stage_of = [&](int b) __attribute__((always_inline)) -> const char* {
+    return smem + ((b >> 1) & (NSTAGE - 1)) * C::STAGE + (b & 1) * 32 * (2 * D);
+  };
+  auto vstage_of = [&](int b) __attribute__((always_inline)) -> const char* {
+    return smem + ((b >> 1) & (NSTAGE - 1)) * C::STAGE + 2 * C::KBYTES + (b & 1) * 32 * (2 * C::DV);
+  };
+
+  auto mask_block = [&](int b, floatx16 (&s)[2]) __attribute__((always_inline)) {
+    const int key0 = b * 32;
+    const int query = q0 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const bool masked = CAUSAL ? (key > query) : (key >= T);
+#pragma unroll
+      for (int br = 0; br < 2; ++br) s[br][r] = masked ? kNegInf : s[br][r];
+    }
+  };
+  auto expo_one = [&](const floatx16& s, bf16x8 (&pk)[2], float& bsum) __attribute__((always_inline)) {
+    bsum = expo16(s, pk);
+  };
+  // lazy rescale (as in fwd_bf16_kernel): the reference moves only when a
+  // probability of the block could exceed 2^kTau, or on the first block
+  auto settle = [&](bool first, floatx16 (&s)[2], bf16x8 (&pk)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
+    bool need = first;
+#pragma unroll
+    for (int br = 0; br < 2; ++br) need |= bsum[br] > kRescaleSum;
+    if (__any(need)) {
+#pragma unroll
+      for (int br = 0; br < 2; ++br) {
+        float m = s[br][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][r]);
+        m = swap_halves_max(m);
+        const float delta = first ? (m == kNegInf ? 0.0f : m) : fmaxf(m, 0.0f);
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        mu[br] += delta;
+        lsum[br] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[br][cb][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[br][r] -= delta;
+        expo_one(s[br], pk[br], bsum[br]);
+      }
+    }
+#pragma unroll
+    for (int br = 0; br < 2; ++br) lsum[br] += bsum[br];
+  };
+  auto load_vf = [&](int b, bf16x8 (&vf)[C::CB][2]) __attribute__((always_inline)) {
+    const char* vb = vstage_of(b) + v_row * (2 * C::DV) + v_byte;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char* base = vb + 16 * ks * (2 * C::DV) + (((4 * cb + v_chunk) ^ v_sw) << 4);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
+        vf[cb][ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+      }
+  };
+  auto pv = [&](int cb0, int ncb, const bf16x8 (&vf)[C::CB][2], const bf16x8 (&pk)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = cb0; cb < cb0 + ncb; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int br = 0; br < 2; ++br)
+          acc[br][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][ks], pk[br][ks], acc[br][cb], 0, 0, 0);
+  };
+  // matrix phase: the P.V product of the previous block in two halves, the
+  // first half's freed registers taking the K fragments of the first half of
+  // the score product, then the score products, the second half's K
+  // fragments read into the first half's registers.  The order is pinned so
+  // that the reads fly behind independent MFMAs and no more than 48
+  // registers of fragments, probabilities and scores are live at once (the
+  // budget of two waves per SIMD).
+  bf16x8 kf[C::KSTEPS / 2][2];
+  constexpr int KH = C::KSTEPS / 2, CH = C::CB / 2;
+  auto qk_half = [&](int b, int ks0, floatx16 (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+#pragma unroll
+      for (int br = 0; br < 2; ++br) {
+        const int ks = ks0 + k;
+        s[br] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k][br], qf[br][ks], ks > 0 ? s[br] : splat16(-mu[br]), 0, 0, 0);
+      }
+  };
+  auto load_kf_half = [&](int b, int ks0) __attribute__((always_inline)) {
+    const char* kb = stage_of(b) + k_rd;
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+#pragma unroll
+      for (int br = 0; br < 2; ++br)
+        kf[k][br] = *(const bf16x8*)(kb + br * C::KBYTES + (((2 * (ks0 + k) + hi) ^ swk) << 4));
+  };
+  auto matrix_phase = [&](int b, bool do_pv, bool do_qk, const bf16x8 (&vf)[C::CB][2],
+                          const bf16x8 (&pk)[2][2], floatx16 (&s)[2]) __attribute__((always_inline)) {
+    if (do_pv) pv(0, CH, vf, pk);
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_qk) load_kf_half(b, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_pv) pv(CH, C::CB - CH, vf, pk);
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_qk) {
+      qk_half(b, 0, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_kf_half(b, KH);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_half(b, KH, s);
+    }
+  };
+
+  // ---- main loop: phase 2b = matrix phase of block b, 2b+1 = its vector phase
+  // Every wave of the workgroup runs the phases of all nblk blocks; a wave's
+  // live blocks (keys it may see) are a prefix [0, n_live), after which it
+  // only issues its share of the tile loads and joins the barriers.
+  const int n_live = q0 < T ? (CAUSAL ? q_last / 32 + 1 : nblk) : 0;
+  // vector phase of block b: half of this wave's share of tile (b+5)/2
+  auto dma_issue = [&](int b) __attribute__((always_inline)) {
+    const int u = (b + 5) >> 1;
+    if (u >= 3 && u < ntiles) {
+      if (b & 1) {
+        issue_slot(u, std::integral_constant<int, 0>{});
+        if constexpr (SEGW == 4) issue_slot(u, std::integral_constant<int, 1>{});
+      } else {
+        issue_slot(u, std::integral_constant<int, SEGW / 2>{});
+        if constexpr (SEGW == 4) issue_slot(u, std::integral_constant<int, 3>{});
+      }
+    }
+  };
+  // end of the matrix phase of block b (odd): tile (b+1)/2 complete for this
+  // wave; tile (b+3)/2, issued since, stays in flight
+  auto dma_wait = [&](int b) __attribute__((always_inline)) {
+    if (b & 1) {
+      const int u = (b + 1) >> 1;
+      if (u < ntiles) wait_tiles(u + 1 < ntiles ? 1 : 0);
+    }
+  };
+  bf16x8 pk[2][2];
+  bf16x8 vf[C::CB][2];
+  floatx16 s[2];
+  auto vector_phase = [&](int b, bool first) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(0);
+    dma_issue(b);
+    const int key0 = b * 32;
+    if (CAUSAL ? (key0 + 31 > q0) : (key0 + 32 > T)) mask_block(b, s);
+    float bs[2];
+    expo_one(s[0], pk[0], bs[0]);
+    expo_one(s[1], pk[1], bs[1]);
+    settle(first, s, pk, bs);
+    __builtin_amdgcn_sched_barrier(0);
+    load_vf(b, vf);
+  };
+  if (late) phase_barrier();
+  int b = 0;
+  if (n_live > 0) {
+    __builtin_amdgcn_s_setprio(1);
+    matrix_phase(0, false, true, vf, pk, s);
+    phase_barrier();
+    vector_phase(0, true);
+    phase_barrier();
+    for (b = 1; b < n_live; ++b) {
+      __builtin_amdgcn_s_setprio(1);
+      matrix_phase(b, true, true, vf, pk, s);
+      dma_wait(b);
+      phase_barrier();
+      vector_phase(b, false);
+      phase_barrier();
+    }
+    // matrix phase n_live: the last block's P.V product only
+    __builtin_amdgcn_s_setprio(1);
+    matrix_phase(b, true, false, vf, pk, s);
+    dma_wait(b);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  // the rest of the workgroup's phases: tile loads and barriers only
+  for (int c = b; c < nblk; ++c) {
+    phase_barrier();  // end of matrix phase c
+    dma_issue(c);     // vector phase c
+    phase_barrier();
+    dma_wait(c + 1);  // matrix phase c+1
+  }
+  if (!late) phase_barrier();
+  if (q0 >= T) return;
+
+  // ---- epilogue: combine the maps, optional head norm, store -----------------
+  auto save_map = [&](int br, int query, float m, float l, float inv, const floatx16 (&ac)[C::CB])
+      __attribute__((always_inline)) {
+    if (a.save_o1 == nullptr || query >= T) return;
+    float* dst = (br ? a.save_o2 : a.save_o1) + o_off + (size_t)query * C::DV;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 t = {ac[cb][4 * g] * inv, ac[cb][4 * g + 1] * inv, ac[cb][4 * g + 2] * inv,
+                           ac[cb][4 * g + 3] * inv};
+        *(floatx4*)(dst + cb * 32 + 8 * g + 4 * hi) = t;
+      }
+    if (hi == 0) a.save_lse[((size_t)bh * 2 + br) * T + query] = m + __log2f(l);
+  };
+  bf16* __restrict__ O = (bf16*)a.out + (bb * a.sb[5] + h * a.sh[5]);
+  const int query = q0 + l32;
+  const float l1 = swap_halves_sum(lsum[0]);
+  const float l2 = swap_halves_sum(lsum[1]);
+  const float inv1 = 1.0f / l1;
+  const float inv2 = 1.0f / l2;
+  save_map(0, query, mu[0], l1, inv1, acc[0]);
+  save_map(1, query, mu[1], l2, inv2, acc[1]);
+  float o[C::CB][16];
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // t1 - lam * t2 with both maps rounded identically (no contraction)
+      const float t1 = acc[0][cb][r] * inv1;
+      const float t2 = acc[1][cb][r] * inv2;
+      const float lt2 = lamv * t2;
+      o[cb][r] = t1 - lt2;
+    }
+  if constexpr (HEADNORM) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss = fmaf(o[cb][r], o[cb][r], ss);
+    ss = swap_halves_sum(ss);
+    const float f = rsqrtf(ss * (1.0f / C::DV) + a.eps) * a.out_scale;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[cb][r] *= f;
+  }
+  if (query < T) {
+    bf16* dst = O + (size_t)query * a.sr[5];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x4 v4 = {(bf16)o[cb][4 * g], (bf16)o[cb][4 * g + 1], (bf16)o[cb][4 * g + 2],
+                           (bf16)o[cb][4 * g + 3]};
+        *(bf16x4*)(dst + cb * 32 + 8 * g + 4 * hi) = v4;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_pp(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
+  using C = CfgB<D, 1, 8, 4, false>;
+  const long nqt = (a.T + C::BR - 1) / C::BR;
+  const long grid = (long)a.B * a.H * nqt;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), b(C::NT);
+  if (causal) {
+    if (headnorm) fwd_pp_kernel<D, true, true><<<g, b, 0, stream>>>(a);
+    else fwd_pp_kernel<D, true, false><<<g, b, 0, stream>>>(a);
+  } else {
+    if (headnorm) fwd_pp_kernel<D, false, true><<<g, b, 0, stream>>>(a);
+    else fwd_pp_kernel<D, false, false><<<g, b, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int NQB, int NW, int NSTAGE, bool SPLIT>
 hipError_t launch_bf16(const FwdArgs& a, bool causal, bool headnorm, hipStream_t stream) {
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
@@ -1048,8 +1497,8 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
         // balance the causal triangle better; otherwise 192-row workgroups
         // with three waves per SIMD hide more latency (measured on MI355X
         // over T = 2048 / 4096 and 8 .. 64 heads).  Long causal rows run both
-        // maps per wave (less LDS traffic per MFMA); full attention runs one
-        // map and 64 rows per wave.
+        // maps per wave with the two waves of each SIMD in opposite phases
+        // (fwd_pp_kernel); full attention runs one map and 64 rows per wave.
         if (causal && a.T <= 4096) {
           const long wg128 = (long)a.B * a.H * ((a.T + 127) / 128);
           const long cus = compute_units();
@@ -1057,7 +1506,7 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
             return launch_bf16<64, 1, 8, 3, true>(a, causal, headnorm, stream);
           return launch_bf16<64, 1, 12, 3, true>(a, causal, headnorm, stream);
         }
-        if (causal) return launch_bf16<64, 1, 8, 3, false>(a, causal, headnorm, stream);
+        if (causal) return launch_pp<64>(a, causal, headnorm, stream);
         return launch_bf16<64, 2, 8, 3, true>(a, causal, headnorm, stream);
       case 128: return launch_bf16<128, 1, 8, 2, true>(a, causal, headnorm, stream);
     }
