@@ -14,7 +14,9 @@ with Q/K [B, H, T, D] and V, O [B, H, T, 2D].
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 import re
 
@@ -75,7 +77,9 @@ _SIGS = {
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree libdiffattn.so, or the file DIFFATTN_LIBRARY names (used to
+    run the CPU ABI tests against a sanitizer-instrumented host build)."""
+    return os.environ.get("DIFFATTN_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def lib() -> ctypes.CDLL:
@@ -117,6 +121,35 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+@contextlib.contextmanager
+def _on_stream(stream):
+    """Makes ``stream`` (a torch stream or a raw HIP stream handle) current for
+    the body: it first waits for the work queued so far on the caller's current
+    stream (which produced the inputs), and every temporary the body allocates
+    (contiguous copies, the lambda vector, a default output or workspace)
+    belongs to it, so the caching allocator does not hand that memory out
+    while the launch still reads it.  Tensors the caller passes in stay the
+    caller's to keep alive until the stream has finished with them."""
+    if stream is None:
+        yield
+        return
+    target = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    current = torch.cuda.current_stream(target.device)
+    if current.cuda_stream != target.cuda_stream:
+        target.wait_stream(current)
+    with torch.cuda.stream(target):
+        yield
+
+
+def _streamed(fn):
+    """Runs ``fn`` with its ``stream`` argument made current (see _on_stream)."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        with _on_stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return DIFFATTN_F32
@@ -155,6 +188,7 @@ def diffattn_lambda_init(layer: int) -> float:
     return float(lib().diffattn_lambda_init(int(layer)))
 
 
+@_streamed
 def diffattn_lambda(lq1, lk1, lq2, lk2, lambda_init: float, out=None, stream=None):
     """lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init, per head.
 
@@ -188,6 +222,7 @@ def _fwd_inputs(q1, k1, q2, k2, v):
     return q1, k1, q2, k2, v
 
 
+@_streamed
 def diffattn_fwd(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
                  lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
     """Prefill forward; q*, k* [B,H,T,D], v [B,H,T,2D] -> out [B,H,T,2D].
@@ -216,6 +251,7 @@ def _view4(t, name, width_of_last):
     return t
 
 
+@_streamed
 def diffattn_fwd_strided(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
                          lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
     """Prefill forward on strided views, without copies: q*, k* are [B,H,T,D]
@@ -246,6 +282,7 @@ def diffattn_fwd_strided(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: 
     return out
 
 
+@_streamed
 def diffattn_fwd_window(q1, k1, q2, k2, v, lam, window: int, headnorm: bool = False,
                         lambda_init: float = 0.8, eps: float = 1e-5, out=None, stream=None):
     """Causal prefill with a sliding window: row i sees keys i - window < j <= i."""
@@ -260,6 +297,7 @@ def diffattn_fwd_window(q1, k1, q2, k2, v, lam, window: int, headnorm: bool = Fa
     return out
 
 
+@_streamed
 def diffattn_fwd_reparam(q1, k1, q2, k2, v, lq1, lk1, lq2, lk2, lambda_init: float,
                          causal: bool = True, headnorm: bool = False, eps: float = 1e-5,
                          lambda_out=None, out=None, stream=None):
@@ -285,6 +323,7 @@ def diffattn_fwd_reparam(q1, k1, q2, k2, v, lq1, lk1, lq2, lk2, lambda_init: flo
     return out
 
 
+@_streamed
 def diffattn_attention_fwd(q, k, v, causal: bool = True, out=None, stream=None):
     """Standard softmax attention (bf16); q, k, v [B,H,T,D], D in {64, 128} ->
     out [B,H,T,D].  The comparison kernel for differential heads of width D/2."""
@@ -309,6 +348,7 @@ def diffattn_decode_workspace_bytes(B: int, H: int, L: int, D: int, num_splits: 
     return int(lib().diffattn_decode_workspace_bytes(B, H, L, D, num_splits))
 
 
+@_streamed
 def diffattn_decode(q1, k1, q2, k2, v, lam, headnorm: bool = False, lambda_init: float = 0.8,
                     eps: float = 1e-5, num_splits: int = 0, workspace=None, out=None,
                     stream=None):
@@ -353,6 +393,7 @@ def _v2_inputs(q1, q2, k, v, tdim):
     return q1, q2, k, v
 
 
+@_streamed
 def diffattn_v2_fwd(q1, q2, k, v, lam, causal: bool = True, out=None, stream=None):
     """DIFF V2 prefill; q1, q2 [B,H,T,D], k, v [B,Hkv,T,D] -> out [B,H,T,D]."""
     q1, q2, k, v = _v2_inputs(q1, q2, k, v, 4)
@@ -372,6 +413,7 @@ def diffattn_v2_decode_workspace_bytes(B: int, H: int, Hkv: int, L: int, D: int,
     return int(lib().diffattn_v2_decode_workspace_bytes(B, H, Hkv, L, D, num_splits))
 
 
+@_streamed
 def diffattn_v2_decode(q1, q2, k, v, lam, num_splits: int = 0, workspace=None, out=None, stream=None):
     """DIFF V2 decode; q1, q2 [B,H,D], caches k, v [B,Hkv,L,D] -> out [B,H,D]."""
     q1, q2, k, v = _v2_inputs(q1, q2, k, v, 3)
@@ -390,6 +432,7 @@ def diffattn_v2_decode(q1, q2, k, v, lam, num_splits: int = 0, workspace=None, o
     return out
 
 
+@_streamed
 def diffattn_decode_ragged(q1, k1, q2, k2, v, lam, lengths, headnorm: bool = False,
                            lambda_init: float = 0.8, eps: float = 1e-5, num_splits: int = 0,
                            workspace=None, out=None, stream=None):
@@ -429,10 +472,11 @@ def _nbytes(t: torch.Tensor) -> int:
     return t.numel() * t.element_size()
 
 
+@_streamed
 def diffattn_fwd_train(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bool = False,
                        lambda_init: float = 0.8, eps: float = 1e-5, out=None, saved=None,
                        stream=None):
-    """Training forward (bf16, D = 64): the output of diffattn_fwd plus the
+    """Training forward (bf16, D = 32, 64 or 128): the output of diffattn_fwd plus the
     saved state diffattn_bwd reads.  Returns (out, saved); ``saved`` is an
     opaque uint8 device tensor of diffattn_train_saved_bytes bytes."""
     q1, k1, q2, k2, v = _fwd_inputs(q1, k1, q2, k2, v)
@@ -450,6 +494,7 @@ def diffattn_fwd_train(q1, k1, q2, k2, v, lam, causal: bool = True, headnorm: bo
     return out, saved
 
 
+@_streamed
 def diffattn_bwd(q1, k1, q2, k2, v, lam, dout, saved, causal: bool = True,
                  headnorm: bool = False, lambda_init: float = 0.8, eps: float = 1e-5,
                  lvecs=None, workspace=None, stream=None):

@@ -60,6 +60,46 @@ def build_library(verbose: bool = True) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that ships with ROCm's LLVM, or ''."""
+    root = "/opt/rocm/llvm/lib/clang"
+    if os.path.isdir(root):
+        for ver in sorted(os.listdir(root), reverse=True):
+            path = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+            if os.path.exists(path):
+                return path
+    return ""
+
+
+def build_sanitized_host(out_dir: str) -> str:
+    """Host-only build of the C ABI (abi.hip) with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with stand-ins for the kernel launchers
+    (tests/abi_san_stubs.cpp), as libdiffattn_san.so in ``out_dir``.  It serves
+    the CPU tests of argument validation, which never launch a kernel; the GPU
+    code is not built or instrumented."""
+    os.makedirs(out_dir, exist_ok=True)
+    clangxx = "/opt/rocm/llvm/bin/clang++"
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer"]
+    abi_o = os.path.join(out_dir, "abi.o")
+    stub_o = os.path.join(out_dir, "stubs.o")
+    lib = os.path.join(out_dir, "libdiffattn_san.so")
+    steps = [
+        [hipcc(), "--offload-arch=gfx950", "--cuda-host-only", "-O1", "-g", "-std=c++17", "-fPIC",
+         "-ffp-contract=off", *san, "-c", os.path.join(CSRC, "abi.hip"), "-o", abi_o],
+        [clangxx, "-O1", "-g", "-std=c++17", "-fPIC", "-fsanitize=address,undefined",
+         "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c",
+         os.path.join(ROOT, "tests", "abi_san_stubs.cpp"), "-o", stub_o],
+        [clangxx, "-shared", "-fsanitize=address,undefined", "-shared-libasan", "-o", lib, abi_o, stub_o,
+         "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"],
+    ]
+    for cmd in steps:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"sanitizer build step failed: {' '.join(cmd[:2])}\n{res.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build_library()
     sys.exit(0)

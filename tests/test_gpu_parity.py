@@ -184,6 +184,32 @@ def test_repeatable_bitwise():
     assert torch.equal(a, b)
 
 
+def test_side_stream_launch():
+    """A launch given stream= waits for the inputs the current stream is still
+    producing, keeps its own temporaries (a scalar lambda's vector, contiguous
+    copies, a default workspace) on that stream, and gives the same bits as a
+    launch on the current stream."""
+    x = to_dev(prefill_inputs(2, 3, 700, 64, "bf16", seed=23))
+    ref = run_fwd(x, 0.6, True, True)
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        # inputs produced by kernels queued on the current stream just before
+        # the side-stream launch; q1 non-contiguous so the binding copies it
+        q1 = (x["q1"].transpose(2, 3) * 1).transpose(2, 3)
+        k1, q2, k2, v = (x[n] * 1 for n in ("k1", "q2", "k2", "v"))
+        out = da.diffattn_fwd(q1, k1, q2, k2, v, 0.6, causal=True, headnorm=True, stream=side)
+        side.synchronize()
+        assert torch.equal(out, ref)
+    xd = to_dev(decode_inputs(2, 3, 900, 64, "bf16", seed=24))
+    dref = da.diffattn_decode(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], 0.7, num_splits=5)
+    torch.cuda.synchronize()
+    k1 = xd["k1"] * 1
+    dout = da.diffattn_decode(xd["q1"], k1, xd["q2"], xd["k2"], xd["v"], 0.7, num_splits=5,
+                              stream=side.cuda_stream)
+    side.synchronize()
+    assert torch.equal(dout, dref)
+
+
 def test_fwd_rejects_empty():
     x = to_dev(prefill_inputs(1, 1, 4, 32, "bf16", seed=1))
     e = {k: v[:, :, :0] for k, v in x.items() if k in ("q1", "k1", "q2", "k2", "v")}
