@@ -155,7 +155,9 @@ def time_kernel(torch, launch, steps):
     return sum(t) / steps, t[len(t) // 2], t[0]
 
 
-def bench_workload(torch, da, name, steps, warmup):
+def bench_workload(torch, da, name, steps, warmup, keep=False):
+    """Times the named workload.  With ``keep``, also returns its inputs and
+    the output of the timed launches (for the oracle comparison)."""
     from workloads import WORKLOADS, make_workload
 
     w = WORKLOADS[name]
@@ -265,6 +267,8 @@ def bench_workload(torch, da, name, steps, warmup):
                      "causal": False if w.kind.endswith("decode") else w.causal,
                      "headnorm": w.headnorm, "dtype": w.dtype, **({"Hkv": w.Hkv} if w.Hkv else {}),
                      **({"window": w.window} if w.window else {})}}
+    if keep:
+        return res, x, out
     del x, out
     torch.cuda.empty_cache()
     return res
@@ -338,34 +342,39 @@ def bench_fused_views(torch, da, name, steps, warmup):
             "ms_per_step_copy_then_dense": round(ms_copy, 5)}
 
 
-def cpu_baseline(torch, name, budget_s=12.0):
+def cpu_baseline(torch, name, x, out, budget_s=12.0):
     """The float64 oracle, as it stands, on the host cores: whole heads of the
-    workload (every query row of each sampled (b, h)) until ~budget_s seconds."""
+    workload (every query row of each (b, h), on the inputs the timed kernel
+    read, with the workload's own lambda and lambda_init) until ~budget_s
+    seconds, and the largest |GPU - oracle| over the output rows of those
+    heads that the timed kernel wrote."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
-    from workloads import WORKLOADS, make_workload
+    from workloads import WORKLOADS
 
     w = WORKLOADS[name]
-    x = make_workload(name, "cuda")
-    lam = 0.8
-    heads, t0 = 0, time.perf_counter()
+    li = w.lambda_init if w.lambda_init is not None else oracle.lambda_init_schedule(w.layer)
+    if "lam" in x:
+        lam = x["lam"].cpu().double().numpy()
+    else:
+        lam = oracle.reparam_lambda(x["lq1"].cpu(), x["lk1"].cpu(), x["lq2"].cpu(), x["lk2"].cpu(), li)
+    heads, worst, t0 = 0, 0.0, time.perf_counter()
     pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
     for (b, h) in pairs:
         sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
-        o = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], lam,
+        o = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], lam[h],
                                        w.causal, np.arange(w.T))
         if w.headnorm:
-            oracle.head_rmsnorm(o, 0.8, w.eps)
+            o = oracle.head_rmsnorm(o, li, w.eps)
         heads += 1
+        worst = max(worst, float(np.max(np.abs(out[b, h].float().cpu().numpy().astype(np.float64) - o))))
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     flops = prefill_flops(w) / (w.B * w.H) * heads
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    del x
-    torch.cuda.empty_cache()
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -374,8 +383,10 @@ def cpu_baseline(torch, name, budget_s=12.0):
         pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "cpu_model": model,
+            "max_abs_err": worst, "tolerance": 2e-2 if w.dtype == "bf16" else 1e-4,
             "sample": f"{heads} of {w.B * w.H} (b,h) heads of {name}, all {w.T} query rows, "
-                      f"float64 numpy, {dt:.1f} s wall, host os.cpu_count()={os.cpu_count()}"}
+                      f"float64 numpy (includes the per-head comparison with the timed kernel's "
+                      f"output), {dt:.1f} s wall, host os.cpu_count()={os.cpu_count()}"}
 
 
 def main():
@@ -415,7 +426,17 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
         return
     da.lib()
-    primary = bench_workload(torch, da, args.workload, args.steps, args.warmup)
+    w = WORKLOADS[args.workload]
+    want_cpu = not args.no_cpu_baseline and w.kind == "prefill"
+    if want_cpu:
+        primary, px, pout = bench_workload(torch, da, args.workload, args.steps, args.warmup, keep=True)
+        # the oracle runs after the other workloads; its inputs and the timed
+        # output move to host memory meanwhile
+        px = {k: v.cpu() for k, v in px.items() if isinstance(v, torch.Tensor)}
+        pout = pout.cpu()
+        torch.cuda.empty_cache()
+    else:
+        primary = bench_workload(torch, da, args.workload, args.steps, args.warmup)
     also = {}
     if not args.primary_only:
         for name in OTHERS + [PRIMARY]:
@@ -428,10 +449,9 @@ def main():
         also["fused_views_prefill_t4k_causal"] = bench_fused_views(
             torch, da, "prefill_t4k_causal", args.steps, args.warmup)
     cpu = None
-    w = WORKLOADS[args.workload]
-    if not args.no_cpu_baseline and w.kind == "prefill":
-        log("[bench] cpu baseline (float64 oracle)")
-        cpu = cpu_baseline(torch, args.workload)
+    if want_cpu:
+        log("[bench] cpu baseline (float64 oracle) and its comparison with the timed output")
+        cpu = cpu_baseline(torch, args.workload, px, pout)
     line = {
         "metric": METRIC, "value": primary["value"], "unit": primary["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": primary["ms_per_step"],

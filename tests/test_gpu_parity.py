@@ -317,7 +317,26 @@ def test_decode_split_invariance_and_last_row():
         assert (o - outs[0]).abs().max().item() <= 1e-5
 
 
-# ---- the named workloads at full size (sampled rows) --------------------------
+# ---- the named workloads at full size ------------------------------------------
+#
+# Every output row of the T=4096 workload; at T=32768 and at T=8192 (D=128)
+# one row of every 32-row wave slice of every (b, h) (so every workgroup,
+# every wave and the tile order the launch uses are covered), plus the first
+# and last rows, random rows and the needle rows; every (b, h) row of the
+# decode workload.  Each workload runs in the launch configuration
+# bench.py times.
+
+def _wave_rows(T, h, extra=(), rng=None, group=32):
+    """One row of every ``group``-row slice (its position varying with the
+    slice and the head), the first 24 and last 16 rows, 64 random rows and
+    ``extra``."""
+    rows = {group * g + (g * 37 + h * 11) % group for g in range((T + group - 1) // group)}
+    rows |= set(range(min(T, 24))) | set(range(max(0, T - 16), T))
+    if rng is not None:
+        rows |= set(rng.choice(T, size=min(T, 64), replace=False).tolist())
+    rows |= {r for r in extra if 0 <= r < T}
+    return np.array(sorted(r for r in rows if r < T))
+
 
 def _sample_rows(T, rng, extra=()):
     rows = set(range(min(T, 24))) | set(range(max(0, T - 16), T))
@@ -326,56 +345,85 @@ def _sample_rows(T, rng, extra=()):
     return np.array(sorted(rows))
 
 
-def _check_prefill_workload(name, heads):
+def _launch_workload(name):
+    """Inputs and output of the named prefill workload, launched as bench.py
+    launches it (lambda from its vectors inside the prefill launch when the
+    workload has vectors)."""
     w = WORKLOADS[name]
     x = make_workload(name, DEV)
-    if "lam" in x:
-        lam = x["lam"]
-        lam_ref = x["lam"].cpu().double().numpy()
-    else:
-        lam = da.diffattn_lambda(x["lq1"], x["lk1"], x["lq2"], x["lk2"], da.diffattn_lambda_init(w.layer))
-        lam_ref = oracle.reparam_lambda(x["lq1"].cpu(), x["lk1"].cpu(), x["lq2"].cpu(), x["lk2"].cpu(),
-                                        oracle.lambda_init_schedule(w.layer))
     li = w.lambda_init if w.lambda_init is not None else oracle.lambda_init_schedule(w.layer)
     say(f"workload {name}: launching")
-    out = da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, causal=w.causal,
-                          headnorm=w.headnorm, lambda_init=li, eps=w.eps)
+    if "lam" in x:
+        lam_ref = x["lam"].cpu().double().numpy()
+        out = da.diffattn_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lam"], causal=w.causal,
+                              headnorm=w.headnorm, lambda_init=li, eps=w.eps)
+    else:
+        lam_ref = oracle.reparam_lambda(x["lq1"].cpu(), x["lk1"].cpu(), x["lq2"].cpu(), x["lk2"].cpu(),
+                                        oracle.lambda_init_schedule(w.layer))
+        out = da.diffattn_fwd_reparam(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lq1"], x["lk1"],
+                                      x["lq2"], x["lk2"], da.diffattn_lambda_init(w.layer), causal=w.causal,
+                                      headnorm=w.headnorm, eps=w.eps)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    rng = np.random.default_rng(w.seed)
+    return w, x, out, lam_ref, li
+
+
+def _check_rows(w, x, out, lam_ref, li, b, h, rows):
+    sl = {k: x[k][b, h].double().cpu() for k in ("q1", "k1", "q2", "k2", "v")}  # exact upcast
+    ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], lam_ref[h],
+                                     w.causal, rows)
+    if w.headnorm:
+        ref = oracle.head_rmsnorm(ref, li, w.eps)
+    return maxerr(out[b, h, rows], ref)
+
+
+def test_workload_prefill_t4k_every_row():
+    w, x, out, lam_ref, li = _launch_workload("prefill_t4k_causal")
     worst = 0.0
-    for (b, h) in heads:
-        extra = []
-        if "needle_pos" in x:
-            for j in x["needle_pos"][b, h].tolist():
-                extra += [j, j + 1, j + 100]
-            # the query rows the needles copy: their maps peak on the needle
-            for i in x["needle_query"][b, h].tolist():
-                extra += [i - 1, i, i + 1]
-        rows = _sample_rows(w.T, rng, extra)
-        sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
-        ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"],
-                                         lam_ref[h], w.causal, rows)
-        if w.headnorm:
-            ref = oracle.head_rmsnorm(ref, li, w.eps)
-        err = maxerr(out[b, h, rows], ref)
-        worst = max(worst, err)
-    say(f"workload {name}: max err {worst:.3e} over {len(heads)} heads")
+    rows = np.arange(w.T)
+    for b in range(w.B):
+        for h in range(w.H):
+            worst = max(worst, _check_rows(w, x, out, lam_ref, li, b, h, rows))
+    say(f"workload prefill_t4k_causal: max err {worst:.3e} over all {w.B * w.H} heads x {w.T} rows")
     del x, out
     torch.cuda.empty_cache()
     assert worst <= TOL[w.dtype]
 
 
-def test_workload_prefill_t4k():
-    _check_prefill_workload("prefill_t4k_causal", [(0, 0), (0, 7), (1, 3), (1, 15)])
-
-
 def test_workload_prefill_t32k_needles():
-    _check_prefill_workload("prefill_t32k_needles", [(0, 0), (0, 5), (0, 15)])
+    w, x, out, lam_ref, li = _launch_workload("prefill_t32k_needles")
+    rng = np.random.default_rng(w.seed)
+    worst, n = 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            extra = []
+            for j in x["needle_pos"][b, h].tolist():
+                extra += [j, j + 1, j + 100]
+            # the query rows the needles copy: their maps peak on the needle
+            for i in x["needle_query"][b, h].tolist():
+                extra += [i - 1, i, i + 1]
+            rows = _wave_rows(w.T, h, extra, rng)
+            n += len(rows)
+            worst = max(worst, _check_rows(w, x, out, lam_ref, li, b, h, rows))
+    say(f"workload prefill_t32k_needles: max err {worst:.3e} over {n} rows of {w.B * w.H} heads")
+    del x, out
+    torch.cuda.empty_cache()
+    assert worst <= TOL[w.dtype]
 
 
 def test_workload_full_t8k_d128():
-    _check_prefill_workload("full_t8k_d128", [(0, 0), (1, 4), (3, 7)])
+    w, x, out, lam_ref, li = _launch_workload("full_t8k_d128")
+    rng = np.random.default_rng(w.seed)
+    worst, n = 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = _wave_rows(w.T, h, (), rng)
+            n += len(rows)
+            worst = max(worst, _check_rows(w, x, out, lam_ref, li, b, h, rows))
+    say(f"workload full_t8k_d128: max err {worst:.3e} over {n} rows of {w.B * w.H} heads")
+    del x, out
+    torch.cuda.empty_cache()
+    assert worst <= TOL[w.dtype]
 
 
 def test_workload_tiny_fp32():
@@ -389,7 +437,7 @@ def test_workload_tiny_fp32():
     assert maxerr(out, oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_ref, True)) <= 1e-4
 
 
-def test_workload_decode_l64k():
+def test_workload_decode_l64k_every_row():
     w = WORKLOADS["decode_l64k"]
     say("workload decode_l64k: generating 16 GiB cache")
     x = make_workload(w.name, DEV)
@@ -400,12 +448,13 @@ def test_workload_decode_l64k():
     torch.cuda.synchronize()
     lam_ref = oracle.lambda_init_schedule(w.layer)  # zero vectors: lambda = lambda_init
     worst = 0.0
-    for (b, h) in ((0, 0), (5, 3), (17, 9), (31, 15)):
-        ref = oracle.diff_attention_decode(x["q1"][b:b + 1, h:h + 1].cpu(), x["k1"][b:b + 1, h:h + 1].cpu(),
-                                           x["q2"][b:b + 1, h:h + 1].cpu(), x["k2"][b:b + 1, h:h + 1].cpu(),
-                                           x["v"][b:b + 1, h:h + 1].cpu(), lam_ref)
-        worst = max(worst, maxerr(out[b:b + 1, h:h + 1], ref))
-    say(f"workload decode_l64k: max err {worst:.3e}")
+    for b in range(w.B):
+        for h in range(w.H):
+            # one (b, h) slice at a time, upcast exactly on the device
+            sl = [x[k][b:b + 1, h:h + 1].double().cpu() for k in ("q1", "k1", "q2", "k2", "v")]
+            ref = oracle.diff_attention_decode(*sl, lam_ref)
+            worst = max(worst, maxerr(out[b:b + 1, h:h + 1], ref))
+        say(f"workload decode_l64k: sequences 0..{b} done, max err {worst:.3e}")
     del x
     torch.cuda.empty_cache()
     assert worst <= TOL["bf16"]
