@@ -2,28 +2,34 @@
 backward pass, through the C ABI, against the float64 oracle.
 
 Inputs are bf16 (the training dtype); both sides see the same rounded values.
-Tolerance for a gradient tensor G: max |G_gpu - G_ref| <= 2e-2 * max |G_ref|
-+ 1e-4.  The GPU rounds dOpre, the probabilities and dS to bf16 before their
-products (relative error 2^-9 each) and rounds G itself to bf16 (2^-9); the
-relative term leaves a margin of about ten such roundings at the tensor's
-scale.  The absolute term covers gradients that are exactly zero (one visible
-key: a constant softmax), where what remains is the fp32 rounding of
-dP - D (|dP| ~ sqrt(2D) ~ 11, times 2^-24, times the sum over D of |K| /
-sqrt(D)).  dlambda_h = -sum over (t, c) of dOpre O2 is a sum whose terms
-carry the forward's bf16 probability rounding in O2; its error scales with
-the root-sum-square of those terms, not with the sum (which can cancel to
-near zero), so each head gets the relative bound against
-max(|dlambda_ref|, rss of its terms, 1).
+Tolerance for a gradient tensor G, element by element:
 
-Known limit of the bound: dS_ij = p_ij dOpre_i . (v_j - o_i) is a
-difference of dot products, and in a row with one or two visible keys under
-the head norm with lambda > 1 it can be far smaller than its terms, so the
-2^-9 rounding of dOpre (stored in bf16 by design) and of the forward's
-bf16-weighted outputs can reach a few percent of max |dQ|.  The draw of the
-T = 2 causal head-norm case with seed 3065 shows dQ1 at 3.6% of its maximum
-(0.0045 of 0.126), with these kernels and with the earlier ones alike; the
-sweep's D = 64 draws are seeds 3000 + i, its D = 32 and D = 128 draws
-3032 + i and 3128 + i.
+    |G_gpu - G_ref| <= 2e-2 * max |G_ref| + 1e-4 + B
+
+The first two terms cover the roundings whose effect stays proportional to
+the tensor's scale (fp32 accumulation and the bf16 rounding of each gradient
+element, 2^-8; the absolute term covers gradients that are exactly zero, a
+row with one visible key).  B is derived, for sequences of up to 4 rows
+(tests/bwd_rounding.py): the first-order bound u sum_i |dG/de_i| of relative
+perturbations |e_i| <= u = 2^-8 at every value the kernels hold in bf16 (the
+score operands q log2(e)/sqrt(D) and k log2(e)/sqrt(D), the forward's
+probabilities that form the saved O1, O2, dOpre, dS, and P1 - lam P2) and at
+the forward's row sums.  Short rows need it: dS_ij = p_ij dOpre_i . (v_j -
+o_i) is then a small difference of large terms (with the head norm dOpre is
+moreover orthogonal to the pre-norm output), so 2^-8 roundings of its inputs
+become percents of max|G| -- for the T = 2, 3 causal head-norm draws with
+seeds 3000 .. 3199, about 4% of the gradient tensors miss 2% of their scale
+(worst 15%, seed 3146 at T = 2).  The bound is the derivative of the exact
+chain rule, so a wrong index, term or sign in a kernel is not absorbed by it
+on any draw where B is small against G; longer sequences (B = 0) are held to
+2% of the scale.  The sweep uses seeds 3000 + i for every case, and one test
+replays the draws with the largest errors.
+
+dlambda_h = -sum over (t, c) of dOpre O2 is a sum whose terms carry the
+forward's bf16 probability rounding in O2; its error scales with the
+root-sum-square of those terms, not with the sum (which can cancel to near
+zero), so each head gets the relative bound against max(|dlambda_ref|, rss
+of its terms, 1).
 """
 
 import numpy as np
@@ -32,6 +38,7 @@ import torch
 
 import differential_attention_forward_amd as da
 import oracle
+from tests import bwd_rounding
 from workloads import WORKLOADS, grad_output, make_workload, prefill_inputs
 
 pytestmark = pytest.mark.gpu
@@ -39,6 +46,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 REL = 2e-2
 ABS = 1e-4
+BOUND_MAX_T = 4
 NAMES = ("dq1", "dk1", "dq2", "dk2", "dv", "dlambda")
 
 
@@ -83,9 +91,9 @@ def dlambda_term_rss(x, lam, dout, causal, headnorm, lambda_init, eps):
     return np.sqrt(np.sum((dop * o2) ** 2, axis=(0, 2, 3)))
 
 
-def check_grads(got, ref, tag, dl_rss=None):
+def check_grads(got, ref, tag, dl_rss=None, bound=None):
     errs = {}
-    for name, g, r in zip(NAMES, got, ref):
+    for i, (name, g, r) in enumerate(zip(NAMES, got, ref)):
         if name == "dlambda":
             scale = np.maximum(np.maximum(np.abs(r), 1.0), 0.0 if dl_rss is None else dl_rss)
             err_h = np.abs(_np(g) - r)
@@ -94,14 +102,28 @@ def check_grads(got, ref, tag, dl_rss=None):
             errs[name] = (float(np.max(err_h / scale)), 1.0)
             continue
         scale = float(np.max(np.abs(r)))
-        err = float(np.max(np.abs(_np(g) - r)))
-        errs[name] = (err, scale)
+        err = np.abs(_np(g) - r)
+        tol = REL * scale + ABS + (0.0 if bound is None else bound[i])
+        errs[name] = (float(np.max(err)), scale)
         assert np.isfinite(_np(g)).all(), (tag, name)
-        assert err <= REL * scale + ABS, (tag, name, err, scale)
+        worst = np.unravel_index(np.argmax(err - tol), err.shape)
+        assert np.all(err <= tol), (tag, name, worst, float(err[worst]), float(np.broadcast_to(tol, err.shape)[worst]), scale)
     say(tag, " ".join(f"{n}={e / max(s, 1e-30):.2e}" for n, (e, s) in errs.items()))
 
 
 SWEEP_T = [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 257]
+
+
+def _bwd_case(T, D, causal, headnorm, seed, lam):
+    x = prefill_inputs(1, 2, T, D, "bf16", seed=seed)
+    dout = grad_output((1, 2, T, 2 * D), seed=seed + 100)
+    out, _, got = run_train(x, lam, dout, causal, headnorm, lambda_init=0.6)
+    ref = oracle.diff_attention_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, dout,
+                                         causal, headnorm, 0.6, 1e-5)
+    rss = dlambda_term_rss(x, lam.numpy(), dout, causal, headnorm, 0.6, 1e-5)
+    bound = (bwd_rounding.first_order_bound(x, lam.numpy(), dout, causal, headnorm, 0.6, 1e-5)
+             if T <= BOUND_MAX_T else None)
+    check_grads(got, ref, f"  T={T} seed={seed}", rss, bound)
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
@@ -111,14 +133,17 @@ def test_bwd_sweep(causal, headnorm, D):
     lam = torch.tensor([0.35, 1.3], dtype=torch.float32)
     for i, T in enumerate(SWEEP_T):
         say(f"bwd D={D} T={T} causal={causal} headnorm={headnorm}")
-        off = {32: 32, 64: 0, 128: 128}[D]
-        x = prefill_inputs(1, 2, T, D, "bf16", seed=3000 + i + off)
-        dout = grad_output((1, 2, T, 2 * D), seed=3100 + i + off)
-        out, _, got = run_train(x, lam, dout, causal, headnorm, lambda_init=0.6)
-        ref = oracle.diff_attention_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, dout,
-                                             causal, headnorm, 0.6, 1e-5)
-        rss = dlambda_term_rss(x, lam.numpy(), dout, causal, headnorm, 0.6, 1e-5)
-        check_grads(got, ref, f"  T={T}", rss)
+        _bwd_case(T, D, causal, headnorm, 3000 + i, lam)
+
+
+def test_bwd_short_rows_worst_draws():
+    """The draws of the T = 2 / T = 3 causal head-norm cases with the largest
+    errors relative to their gradients' scale (seeds 3000 .. 3199, D = 64),
+    and seed 3065, the draw first seen to exceed 2% of max |dQ1|."""
+    lam = torch.tensor([0.35, 1.3], dtype=torch.float32)
+    for T, seed in ((2, 3065), (2, 3146), (3, 3176), (3, 3031), (2, 3095)):
+        say(f"bwd short rows T={T} seed={seed}")
+        _bwd_case(T, 64, True, True, seed, lam)
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
@@ -155,18 +180,19 @@ def test_fwd_train_output_and_saved_state(D):
         diag2 = np.diagonal(a2, axis1=2, axis2=3)
         ref1 = (s1 - np.log(diag1)) / np.log(2.0)
         ref2 = (s2 - np.log(diag2)) / np.log(2.0)
-        # The forward sums bf16-rounded probabilities (relative error <= 2^-9
-        # each), so log2 of the sum is off by at most 2^-9 / ln 2 = 2.8e-3.
-        # Its scores use q * log2(e)/sqrt(D) rounded to bf16 (relative error
-        # <= 2^-9 + 2^-24 per element), which moves score s_ij by at most
-        # delta_ij = (2^-9 + 2^-24) log2(e)/sqrt(D) sum_d |q_id k_jd|, and the
+        # The forward's row sum is of fp32 probabilities or of their bf16
+        # roundings (unit roundoff 2^-8, 8 significant bits), so log2 of the
+        # sum is off by at most 2^-8 / ln 2 = 5.64e-3.  Its scores use
+        # q * log2(e)/sqrt(D) rounded to bf16 (relative error <= 2^-8 + 2^-24
+        # per element), which moves score s_ij by at most
+        # delta_ij = (2^-8 + 2^-24) log2(e)/sqrt(D) sum_d |q_id k_jd|, and the
         # log-sum-exp of row i by at most max_j delta_ij over its visible keys.
         for br, (qn, kn, ref) in enumerate((("q1", "k1", ref1), ("q2", "k2", ref2))):
             absqk = np.abs(x[qn].double().numpy()) @ np.abs(x[kn].double().numpy()).transpose(0, 1, 3, 2)
             if causal:
                 absqk = np.where(np.tril(np.ones((T, T), dtype=bool)), absqk, 0.0)
-            delta = (2.0 ** -9 + 2.0 ** -24) * (1.4426950408889634 / np.sqrt(D)) * absqk.max(axis=-1)
-            assert np.all(np.abs(_np(lse[:, :, br]) - ref) <= 3e-3 + delta)
+            delta = (2.0 ** -8 + 2.0 ** -24) * (1.4426950408889634 / np.sqrt(D)) * absqk.max(axis=-1)
+            assert np.all(np.abs(_np(lse[:, :, br]) - ref) <= 5.7e-3 + delta)
 
 
 def test_bwd_lambda_vectors():
