@@ -27,13 +27,14 @@ __all__ = [
     "diffattn_status_string", "diffattn_lambda_init", "diffattn_lambda", "diffattn_fwd",
     "diffattn_fwd_reparam", "diffattn_fwd_window", "diffattn_fwd_strided", "diffattn_attention_fwd",
     "diffattn_decode_default_splits", "diffattn_decode_workspace_bytes", "diffattn_decode",
-    "diffattn_decode_ragged",
+    "diffattn_decode_ragged", "diffattn_decode_noalloc", "DIFFATTN_NOALLOC_SCRATCH_BYTES",
     "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_bwd_workspace_bytes",
     "diffattn_bwd", "diffattn_v2_fwd", "diffattn_v2_decode_workspace_bytes", "diffattn_v2_decode",
 ]
 
 DIFFATTN_F32 = 0
 DIFFATTN_BF16 = 1
+DIFFATTN_NOALLOC_SCRATCH_BYTES = 32 << 20  # the header's macro of the same name
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libdiffattn.so"
@@ -62,6 +63,8 @@ _SIGS = {
                              _VP, ctypes.c_size_t, _VP, _VP]),
     "diffattn_decode_ragged": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F,
                                     _I, _VP, ctypes.c_size_t, _VP, _VP]),
+    "diffattn_decode_noalloc": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _F, _F,
+                                     _I, _VP, _VP]),
     "diffattn_train_saved_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "diffattn_fwd_train": (_I, [_I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _F, _F,
                                 _VP, _VP, ctypes.c_size_t, _VP]),
@@ -376,6 +379,35 @@ def diffattn_decode(q1, k1, q2, k2, v, lam, headnorm: bool = False, lambda_init:
                                  float(lambda_init), float(eps), int(num_splits),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _ptr(out), _stream(stream)))
+    return out
+
+
+@_streamed
+def diffattn_decode_noalloc(q1, k1, q2, k2, v, lam, headnorm: bool = False,
+                            lambda_init: float = 0.8, eps: float = 1e-5, num_splits: int = 0,
+                            out=None, stream=None):
+    """diffattn_decode without a workspace: the library's per-GPU scratch
+    array holds the partial states (calls that overlap on one GPU race).
+    Pass `out` and a tensor `lam` [H] to keep this call free of allocations."""
+    q1, k1, q2, k2, v = (_dev(t, n) for t, n in
+                         ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")))
+    if k1.dim() != 4:
+        raise ValueError("k1 must be [B, H, L, D]")
+    b, h, l, d = k1.shape
+    if q1.shape != (b, h, d) or q2.shape != (b, h, d):
+        raise ValueError("q1, q2 must be [B, H, D]")
+    if k2.shape != k1.shape or v.shape != (b, h, l, 2 * d):
+        raise ValueError("k2 must match k1 and v must be [B, H, L, 2D]")
+    for x in (q2, k1, k2, v):
+        if x.dtype != q1.dtype:
+            raise ValueError("all inputs must share one dtype")
+    lamv = _lambda_vec(lam, h, q1.device)
+    if out is None:
+        out = torch.empty((b, h, 2 * d), device=q1.device, dtype=q1.dtype)
+    _check(lib().diffattn_decode_noalloc(_dtype_code(q1), b, h, l, d, _ptr(q1), _ptr(k1), _ptr(q2),
+                                         _ptr(k2), _ptr(v), _ptr(lamv), int(bool(headnorm)),
+                                         float(lambda_init), float(eps), int(num_splits),
+                                         _ptr(out), _stream(stream)))
     return out
 
 

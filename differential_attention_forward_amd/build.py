@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
-KERNEL_SOURCES = ["prefill.hip", "decode.hip", "lambda.hip", "backward.hip"]
+KERNEL_SOURCES = ["prefill.hip", "decode.hip", "lambda.hip", "backward.hip", "scratch.hip"]
 HOST_SOURCES = ["abi.hip"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -495,7 +495,7 @@ diffattn_status decode_impl(int dtype, int B, int H, int L, int D, const void* q
                             const void* q2, const void* k2, const void* v, const float* lambda,
                             const int* lengths, int headnorm, float lambda_init, float eps,
                             int num_splits, void* workspace, size_t workspace_bytes, void* out,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool lib_scratch = false) {
   if (!q1 || !k1 || !q2 || !k2 || !v || !lambda || !out) return DIFFATTN_ERR_INVALID;
   if (B < 1 || H < 1 || L < 1) return DIFFATTN_ERR_INVALID;
   if (headnorm && !(eps > 0.0f)) return DIFFATTN_ERR_INVALID;
@@ -510,6 +510,12 @@ diffattn_status decode_impl(int dtype, int B, int H, int L, int D, const void* q
   if ((long long)B * H * S > 0x7fffffffLL || (long long)L * 2 * D > 0x7fffffffLL)
     return DIFFATTN_ERR_UNSUPPORTED;
   const size_t need = diffattn_decode_workspace_bytes(B, H, L, D, S);
+  if (lib_scratch) {
+    // the library's own array of the current device instead of a caller's
+    if (need > DIFFATTN_NOALLOC_SCRATCH_BYTES) return DIFFATTN_ERR_WORKSPACE;
+    if (diffattn::decode_scratch(&workspace) != hipSuccess) return DIFFATTN_ERR_HIP;
+    workspace_bytes = DIFFATTN_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return DIFFATTN_ERR_UNSUPPORTED;
   const size_t es = elem_bytes(dtype);
@@ -572,6 +578,15 @@ diffattn_status diffattn_decode_ragged(int dtype, int B, int H, int L, int D, co
   if (!lengths) return DIFFATTN_ERR_INVALID;
   return decode_impl(dtype, B, H, L, D, q1, k1, q2, k2, v, lambda, lengths, headnorm, lambda_init,
                      eps, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+diffattn_status diffattn_decode_noalloc(int dtype, int B, int H, int L, int D, const void* q1,
+                                        const void* k1, const void* q2, const void* k2,
+                                        const void* v, const float* lambda, int headnorm,
+                                        float lambda_init, float eps, int num_splits, void* out,
+                                        hipStream_t stream) {
+  return decode_impl(dtype, B, H, L, D, q1, k1, q2, k2, v, lambda, nullptr, headnorm, lambda_init,
+                     eps, num_splits, nullptr, 0, out, stream, true);
 }
 
 // ---- DIFF V2: two query heads per differential head, K/V shared per group ----

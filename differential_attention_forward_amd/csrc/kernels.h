@@ -106,6 +106,10 @@ struct BwdArgs {
 // dtype: 0 = fp32, 1 = bf16 (same codes as the public enum)
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool headnorm,
                       hipStream_t stream);
+// Device address of the library-held decode scratch of the current device
+// (DIFFATTN_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned), looked up on the
+// first call per device.
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, bool headnorm,
                          hipStream_t stream);
 // DIFF V2 decode, bf16: q1/q2 [B,H,D], k/v caches [B,Hkv,L,D], out [B,H,D];

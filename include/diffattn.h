@@ -13,7 +13,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers (HIP device memory) owned by the
  *     caller.  The library allocates nothing and keeps no state; every entry
- *     point is thread-safe.
+ *     point is thread-safe.  (One exception: diffattn_decode_noalloc works in
+ *     a device array the library holds per GPU; see there.)
  *   - Tensors are dense, contiguous and row-major in the shapes given.  Every
  *     tensor pointer must be 16-byte aligned.
  *   - Inputs are never written.  Outputs must not overlap any input.
@@ -250,6 +251,42 @@ diffattn_status diffattn_decode_ragged(int dtype, int B, int H, int L, int D, co
                                        int headnorm, float lambda_init, float eps, int num_splits,
                                        void* workspace, size_t workspace_bytes, void* out,
                                        hipStream_t stream);
+
+/*
+ * Size in bytes of the device array diffattn_decode_noalloc works in (one per
+ * GPU).
+ */
+#define DIFFATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * diffattn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * same kernels and the same result bit for bit, but no workspace argument.
+ * The split-K partial states go to a static device array of
+ * DIFFATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds, one copy per
+ * GPU, from its load until the process ends.  The copy of the current device
+ * (hipGetDevice) is used, so `stream` must belong to that device.  The first
+ * call on a device looks up the array's device address
+ * (hipGetSymbolAddress; to keep that lookup out of a graph capture, make one
+ * call on each device before capturing).  No call allocates or frees memory.
+ *
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * partial states: calls that can overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.  The array's contents on
+ * entry are ignored, so nothing needs to be cleared between calls.
+ *
+ *   arguments as for diffattn_decode, without workspace and workspace_bytes
+ * Errors: as diffattn_decode; ERR_WORKSPACE when
+ * diffattn_decode_workspace_bytes(B, H, L, D, num_splits) exceeds
+ * DIFFATTN_NOALLOC_SCRATCH_BYTES (fewer splits, or diffattn_decode with a
+ * workspace of the caller's, then fit); ERR_HIP when the array's address
+ * cannot be obtained (no device).
+ */
+diffattn_status diffattn_decode_noalloc(int dtype, int B, int H, int L, int D, const void* q1,
+                                        const void* k1, const void* q2, const void* k2,
+                                        const void* v, const float* lambda, int headnorm,
+                                        float lambda_init, float eps, int num_splits, void* out,
+                                        hipStream_t stream);
 
 /*
  * ---- DIFF V2 (the French lesson page "Attention différentielle (V2)",

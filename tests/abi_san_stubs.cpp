@@ -10,6 +10,7 @@ hipError_t launch_decode(const DecodeArgs&, int, int, bool, hipStream_t) { retur
 hipError_t launch_decode_v2(const DecodeArgs&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_attention(const FwdArgs&, int, bool, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_v2(const FwdArgs&, int, bool, hipStream_t) { return hipErrorNotSupported; }
+hipError_t decode_scratch(void**) { return hipErrorNotSupported; }
 hipError_t launch_bwd(const BwdArgs&, int, bool, bool, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_lambda(const float*, const float*, const float*, const float*, int, int, float, float*,
                          hipStream_t) {

@@ -7,6 +7,8 @@ returns before anything dereferences or launches.
 
 import ctypes
 import math
+import os
+import re
 
 import pytest
 
@@ -24,7 +26,7 @@ def L():
 
 def test_header_symbols_exported(L):
     names = da.header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     assert "diffattn_fwd_reparam" in names and "diffattn_attention_fwd" in names
     assert "diffattn_v2_fwd" in names and "diffattn_v2_decode" in names
     assert "diffattn_fwd_train" in names and "diffattn_bwd" in names
@@ -168,6 +170,37 @@ def test_decode_validation(L):
     assert dec(L, ws=P(8, 8)) == UNSUPPORTED
     # workspace overlapping the value cache
     assert dec(L, ws=P(4, 64)) == INVALID
+
+
+def dec_na(L, dtype=BF16, B=1, H=2, Lk=64, D=64, splits=0, ptrs=None):
+    p = ptrs or [P(i) for i in range(7)]
+    return L.diffattn_decode_noalloc(dtype, B, H, Lk, D, p[0], p[1], p[2], p[3], p[4], p[5], 0,
+                                     ctypes.c_float(0.8), ctypes.c_float(1e-5), splits, p[6], None)
+
+
+def test_decode_noalloc_validation(L):
+    """Argument errors, and a split count whose partial states would not fit
+    the library's array, are reported before the array is looked up."""
+    assert dec_na(L, Lk=0) == INVALID
+    assert dec_na(L, splits=-1) == INVALID
+    assert dec_na(L, Lk=10, splits=11) == INVALID
+    assert dec_na(L, D=80) == UNSUPPORTED
+    bad = [P(i) for i in range(7)]
+    bad[6] = P(4, 64)  # output inside the value cache
+    assert dec_na(L, ptrs=bad) != OK
+    nul = [P(i) for i in range(7)]
+    nul[0] = None
+    assert dec_na(L, ptrs=nul) == INVALID
+    cap = da.DIFFATTN_NOALLOC_SCRATCH_BYTES
+    assert da.diffattn_decode_workspace_bytes(1, 2, 8192, 128, 8192) > cap
+    assert dec_na(L, Lk=8192, D=128, splits=8192) == WORKSPACE
+    assert dec_na(L, B=4096, H=8, Lk=64, D=128, splits=1) == WORKSPACE
+
+
+def test_noalloc_scratch_size_matches_header():
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "diffattn.h")
+    m = re.search(r"#define DIFFATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(hdr).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == da.DIFFATTN_NOALLOC_SCRATCH_BYTES
 
 
 def fwin(L, dtype=BF16, window=4, ptrs=None, T=8, D=64):
