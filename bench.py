@@ -22,7 +22,11 @@ with standard softmax attention of the same size as the two causal workloads
 events around each launch on the launch stream) against the MI355X peak
 (bf16 dense MFMA 2.5 PFLOP/s, fp32 MFMA 157.3 TFLOP/s, HBM 8 TB/s).
 "cpu_baseline" times the float64 oracle on the host cores on a bounded sample
-of the primary workload.
+of the primary workload.  "micro" holds the measured ceilings of this GPU
+(differential_attention_forward_amd/micro.py: bf16 MFMA throughput and the
+shader clock it runs at, HBM read and copy, the global -> LDS DMA stream, LDS
+read rates, VALU issue beside an MFMA stream), and each roofline adds its
+bound's measured ceiling ("measured_peak", "frac_of_measured").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -274,6 +278,23 @@ def bench_workload(torch, da, name, steps, warmup, keep=False):
     return res
 
 
+def attach_measured_peak(res, measured):
+    """Adds the microbenchmarked ceiling of the workload's bound (bf16 MFMA
+    throughput at the clock it sustains, or streaming HBM read) to its
+    roofline, with the achieved rate as a fraction of it."""
+    roof = res.get("roofline") if isinstance(res, dict) else None
+    if not roof or "achieved" not in roof:
+        return
+    if roof["bound"] == "mfma" and roof["peak"] == PEAK["bf16_mfma_tflops"]:
+        m = measured["mfma_bf16"]["tflops"]
+    elif roof["bound"] == "hbm":
+        m = measured["hbm_read"]["gbs"]
+    else:
+        return
+    roof["measured_peak"] = round(m, 1)
+    roof["frac_of_measured"] = round(roof["achieved"] / m, 4)
+
+
 def bench_same_size_attention(torch, da, name, steps, warmup, diff_ms):
     """Standard softmax attention of the same size as the named causal
     differential workload (head width 2D, same B, H, T, same 8 T_eff T D B H
@@ -397,6 +418,10 @@ def main():
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--primary-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--micro", action="store_true",
+                    help="only run the microbenchmarks (measured MFMA, HBM, LDS-DMA, LDS and VALU "
+                         "ceilings and the shader clock under MFMA load) and print them")
+    ap.add_argument("--no-micro", action="store_true", help="skip the microbenchmarks")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -425,6 +450,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
         return
+    if args.micro:
+        from differential_attention_forward_amd import micro
+
+        print(json.dumps({"micro": micro.run_all(), "gpu": torch.cuda.get_device_name(0)}), flush=True)
+        return
     da.lib()
     w = WORKLOADS[args.workload]
     want_cpu = not args.no_cpu_baseline and w.kind == "prefill"
@@ -448,6 +478,14 @@ def main():
                 torch, da, name, args.steps, args.warmup, diff_ms)
         also["fused_views_prefill_t4k_causal"] = bench_fused_views(
             torch, da, "prefill_t4k_causal", args.steps, args.warmup)
+    measured = None
+    if not args.no_micro:
+        from differential_attention_forward_amd import micro
+
+        log("[bench] microbenchmarks (measured ceilings)")
+        measured = micro.run_all()
+        for res in [primary, *also.values()]:
+            attach_measured_peak(res, measured)
     cpu = None
     if want_cpu:
         log("[bench] cpu baseline (float64 oracle) and its comparison with the timed output")
@@ -459,6 +497,7 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": args.workload, **primary["shape"]},
         "roofline": primary["roofline"], "cpu_baseline": cpu,
+        "micro": measured,
         "also": also,
         "gpu": torch.cuda.get_device_name(0),
     }

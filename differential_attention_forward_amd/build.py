@@ -16,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
+MICRO_LIB = os.path.join(PKG, "libdiffattn_micro.so")
 
 KERNEL_SOURCES = ["prefill.hip", "decode.hip", "lambda.hip", "backward.hip", "scratch.hip"]
 HOST_SOURCES = ["abi.hip"]
@@ -44,19 +45,27 @@ def _compile(src: str, flags) -> str:
     return obj
 
 
-def build_library(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = [(s, KERNEL_FLAGS) for s in KERNEL_SOURCES] + [(s, []) for s in HOST_SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
-        objs = list(ex.map(lambda j: _compile(*j), jobs))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build_library(verbose: bool = True) -> str:
+    """libdiffattn.so (the attention library) and libdiffattn_micro.so (the
+    microbenchmarks bench.py reports measured ceilings from)."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = ([(s, KERNEL_FLAGS) for s in KERNEL_SOURCES + ["micro.hip"]] +
+            [(s, []) for s in HOST_SOURCES])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = dict(zip([j[0] for j in jobs], ex.map(lambda j: _compile(*j), jobs)))
+    _link([objs[s] for s in KERNEL_SOURCES + HOST_SOURCES], LIB)
+    _link([objs["micro.hip"]], MICRO_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {MICRO_LIB}")
     return LIB
 
 

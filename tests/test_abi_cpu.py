@@ -34,6 +34,18 @@ def test_header_symbols_exported(L):
         assert hasattr(L, n), n
 
 
+def test_micro_library_exports_its_header():
+    from differential_attention_forward_amd import micro
+
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                       "diffattn_micro.h")
+    names = re.findall(r"^int (diffattn_micro_\w+)\(", open(hdr).read(), re.M)
+    assert len(names) == 6 and set(names) == set(micro._SIGS)
+    handle = micro.lib()
+    for n in names:
+        getattr(handle, n)
+
+
 def test_status_strings(L):
     for s in range(5):
         assert da.diffattn_status_string(s)
