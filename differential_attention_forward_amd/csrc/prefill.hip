@@ -371,13 +371,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
       inv2 = 1.0f / l2;
     }
     const float* xrow = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
-    float o[C::CB][16];
+    // the output is formed in place in map 1's accumulators: a separate array
+    // of the same size would double the live registers (D = 128 spilled)
+    floatx16 (&o)[C::CB] = acc[0][qb];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         // t1 - lam * t2 with both maps rounded identically (no contraction)
-        const float t1 = acc[0][qb][cb][r] * inv1;
+        const float t1 = o[cb][r] * inv1;
         float t2;
         if constexpr (SPLIT) t2 = xrow[cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)];
         else t2 = acc[C::NBR - 1][qb][cb][r] * inv2;
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
         u32x4 raw = *(const u32x4*)(src + ks * 16 + hi * 8);
         raw = ok ? raw : u32x4{0u, 0u, 0u, 0u};
         // scores come out of the MFMA already in base-2 units: q * log2(e) / sqrt(D)
-        // rounded once to bf16 (relative error <= 2^-9 per element)
+        // rounded once to bf16 (relative error <= 2^-8 per element)
         const bf16x8 q = __builtin_bit_cast(bf16x8, raw);
         bf16x8 qs;
 #pragma unroll
@@ -825,8 +827,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
       if (kt + 3 < ntiles) step(kt + 3, std::integral_constant<int, 3>{});
   }
 
+  // The accumulators are normalised in place (acc * (1 / l), the same
+  // product every consumer used before): the saved map, the exchanged map and
+  // the output then read one set of registers.  Forming acc * inv separately
+  // for each consumer made the compiler keep a second full copy live across
+  // the training-forward branch (spills at D = 128).
+  auto normalise = [&](floatx16 (&ac)[C::CB], float inv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ac[cb][r] = ac[cb][r] * inv;
+  };
   // training forward: map br's normalised output and its log-sum-exp
-  auto save_map = [&](int br, int query, float m, float l, float inv, const floatx16 (&ac)[C::CB])
+  auto save_map = [&](int br, int query, float m, float l, const floatx16 (&ac)[C::CB])
       __attribute__((always_inline)) {
     if (a.save_o1 == nullptr || query >= T) return;
     float* dst = (br ? a.save_o2 : a.save_o1) + o_off + (size_t)query * C::DV;
@@ -834,8 +847,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const floatx4 t = {ac[cb][4 * g] * inv, ac[cb][4 * g + 1] * inv, ac[cb][4 * g + 2] * inv,
-                           ac[cb][4 * g + 3] * inv};
+        const floatx4 t = {ac[cb][4 * g], ac[cb][4 * g + 1], ac[cb][4 * g + 2], ac[cb][4 * g + 3]};
         *(floatx4*)(dst + cb * 32 + 8 * g + 4 * hi) = t;
       }
     if (hi == 0) a.save_lse[((size_t)bh * 2 + br) * T + query] = m + __log2f(l);
@@ -848,15 +860,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const float l2 = swap_halves_sum(lsum[0][qb]);
-        const float inv2 = 1.0f / l2;
-        save_map(1, q0 + qb * 32 + l32, mu[0][qb], l2, inv2, acc[0][qb]);
+        normalise(acc[0][qb], 1.0f / l2);
+        save_map(1, q0 + qb * 32 + l32, mu[0][qb], l2, acc[0][qb]);
         float* row = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const floatx4 t = {acc[0][qb][cb][4 * g] * inv2, acc[0][qb][cb][4 * g + 1] * inv2,
-                               acc[0][qb][cb][4 * g + 2] * inv2, acc[0][qb][cb][4 * g + 3] * inv2};
+            const floatx4 t = {acc[0][qb][cb][4 * g], acc[0][qb][cb][4 * g + 1], acc[0][qb][cb][4 * g + 2],
+                               acc[0][qb][cb][4 * g + 3]};
             *(floatx4*)(row + cb * 32 + 8 * g + 4 * hi) = t;
           }
       }
@@ -872,32 +884,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   for (int qb = 0; qb < NQB; ++qb) {
     const int query = q0 + qb * 32 + l32;
     const float l1 = swap_halves_sum(lsum[0][qb]);
-    const float inv1 = 1.0f / l1;
-    float inv2 = 0.0f;
-    if constexpr (MAPS == 2) save_map(0, query, mu[0][qb], l1, inv1, acc[0][qb]);
+    normalise(acc[0][qb], 1.0f / l1);
+    if constexpr (MAPS == 2) save_map(0, query, mu[0][qb], l1, acc[0][qb]);
     if constexpr (!SPLIT && MAPS == 2) {
       const float l2 = swap_halves_sum(lsum[1][qb]);
-      inv2 = 1.0f / l2;
-      save_map(1, query, mu[1][qb], l2, inv2, acc[1][qb]);
+      normalise(acc[1][qb], 1.0f / l2);
+      save_map(1, query, mu[1][qb], l2, acc[1][qb]);
     }
     const float* xrow = xch + (wq * C::QPW + qb * 32 + l32) * C::XP;
-    float o[C::CB][16];
+    // the output is formed in place in map 1's accumulators
+    floatx16 (&o)[C::CB] = acc[0][qb];
+    if constexpr (MAPS == 2) {
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
+      for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // t1 - lam * t2 with both maps rounded identically (no contraction)
-        const float t1 = acc[0][qb][cb][r] * inv1;
-        if constexpr (MAPS == 1) {
-          o[cb][r] = t1;
-        } else {
+        for (int r = 0; r < 16; ++r) {
+          // t1 - lam * t2 with both maps rounded identically (no contraction)
           float t2;
           if constexpr (SPLIT) t2 = xrow[cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)];
-          else t2 = acc[C::NBR - 1][qb][cb][r] * inv2;
+          else t2 = acc[C::NBR - 1][qb][cb][r];
           const float lt2 = lamv * t2;
-          o[cb][r] = t1 - lt2;
+          o[cb][r] = o[cb][r] - lt2;
         }
-      }
+    }
     if constexpr (HEADNORM) {
       float ss = 0.0f;
 #pragma unroll
@@ -1293,7 +1302,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (q0 >= T) return;
 
   // ---- epilogue: combine the maps, optional head norm, store -----------------
-  auto save_map = [&](int br, int query, float m, float l, float inv, const floatx16 (&ac)[C::CB])
+  // maps normalised in place (one product per element, read by the saved
+  // map and the output alike), as in fwd_bf16_kernel
+  auto save_map = [&](int br, int query, float m, float l, const floatx16 (&ac)[C::CB])
       __attribute__((always_inline)) {
     if (a.save_o1 == nullptr || query >= T) return;
     float* dst = (br ? a.save_o2 : a.save_o1) + o_off + (size_t)query * C::DV;
@@ -1301,8 +1312,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const floatx4 t = {ac[cb][4 * g] * inv, ac[cb][4 * g + 1] * inv, ac[cb][4 * g + 2] * inv,
-                           ac[cb][4 * g + 3] * inv};
+        const floatx4 t = {ac[cb][4 * g], ac[cb][4 * g + 1], ac[cb][4 * g + 2], ac[cb][4 * g + 3]};
         *(floatx4*)(dst + cb * 32 + 8 * g + 4 * hi) = t;
       }
     if (hi == 0) a.save_lse[((size_t)bh * 2 + br) * T + query] = m + __log2f(l);
@@ -1313,18 +1323,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float l2 = swap_halves_sum(lsum[1]);
   const float inv1 = 1.0f / l1;
   const float inv2 = 1.0f / l2;
-  save_map(0, query, mu[0], l1, inv1, acc[0]);
-  save_map(1, query, mu[1], l2, inv2, acc[1]);
-  float o[C::CB][16];
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[0][cb][r] = acc[0][cb][r] * inv1;
+      acc[1][cb][r] = acc[1][cb][r] * inv2;
+    }
+  save_map(0, query, mu[0], l1, acc[0]);
+  save_map(1, query, mu[1], l2, acc[1]);
+  floatx16 (&o)[C::CB] = acc[0];
 #pragma unroll
   for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       // t1 - lam * t2 with both maps rounded identically (no contraction)
-      const float t1 = acc[0][cb][r] * inv1;
-      const float t2 = acc[1][cb][r] * inv2;
-      const float lt2 = lamv * t2;
-      o[cb][r] = t1 - lt2;
+      const float lt2 = lamv * acc[1][cb][r];
+      o[cb][r] = o[cb][r] - lt2;
     }
   if constexpr (HEADNORM) {
     float ss = 0.0f;
