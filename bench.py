@@ -47,7 +47,8 @@ PRIMARY = "prefill_t4k_causal"
 OTHERS = ["prefill_t32k_needles", "full_t8k_d128", "decode_l64k", "v2_prefill_t4k", "v2_decode_l64k",
           "bwd_t4k_causal", "bwd_t4k_d128", "prefill_t32k_window4k", "decode_ragged_l64k"]
 CSRC = os.path.join(ROOT, "differential_attention_forward_amd", "csrc")
-KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip", "v2_decode": "decode.hip"}
+KERNEL_FILE = {"prefill": "prefill.hip", "decode": "decode.hip", "v2_decode": "decode.hip",
+               "backward": "backward.hip"}
 KERNEL_NAME = {"prefill": "fwd_bf16_kernel", "decode": "decode_partial_kernel",
                "v2_decode": "decode_v2_mma_kernel"}
 # which kernel dominates each workload kind (the backward has four of comparable weight)
@@ -67,14 +68,24 @@ def source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind, workload):
+def dominant_kernel(w):
+    """The kernel that does a workload's work: the launch choice of the
+    library's prefill dispatch (bf16, D = 64, causal, T > 4096 rows: the
+    ping-pong kernel; other prefill shapes: fwd_bf16_kernel)."""
+    kind = KIND_KERNEL[w.kind]
+    if kind == "prefill" and w.kind == "prefill" and w.dtype == "bf16" and w.D == 64 and w.causal and w.T > 4096:
+        return "fwd_pp_kernel"
+    return KERNEL_NAME[kind]
+
+
+def measured_traffic(kind, kernel, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; otherwise None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(f"{KERNEL_NAME[kind]}:{workload}")
+        rec = json.load(f).get(f"{kernel}:{workload}")
     if not rec or rec.get("source_hash") != source_hash(kind):
         return None
     return rec.get("bytes_per_launch")
@@ -250,8 +261,9 @@ def bench_workload(torch, da, name, steps, warmup, keep=False):
         peak = PEAK["bf16_mfma_tflops"] if w.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic("prefill", name) if w.kind in KIND_KERNEL else None,
-                "kernel": "bwd_prep + bwd_kv + bwd_q + bwd_lambda kernels" if w.kind == "bwd" else KERNEL_NAME["prefill"],
+                "traffic": (measured_traffic("prefill", dominant_kernel(w), name) if w.kind in KIND_KERNEL
+                            else measured_traffic("backward", "bwd_kernels", name)),
+                "kernel": "bwd_prep + bwd_kv + bwd_q + bwd_lambda kernels" if w.kind == "bwd" else dominant_kernel(w),
                 "algorithmic_per_launch": work}
         unit = "TFLOP/s"
     else:
@@ -260,8 +272,8 @@ def bench_workload(torch, da, name, steps, warmup, keep=False):
         achieved = work / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"],
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm_gbs"], 4),
-                "traffic": measured_traffic(KIND_KERNEL[w.kind], name),
-                "kernel": KERNEL_NAME[KIND_KERNEL[w.kind]],
+                "traffic": measured_traffic(KIND_KERNEL[w.kind], dominant_kernel(w), name),
+                "kernel": dominant_kernel(w),
                 "algorithmic_per_launch": work}
         unit = "GB/s"
     res = {"workload": name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
