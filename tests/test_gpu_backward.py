@@ -146,53 +146,66 @@ def test_bwd_short_rows_worst_draws():
         _bwd_case(T, 64, True, True, seed, lam)
 
 
+def _check_train_saved_state(x, lam, causal, headnorm, tag):
+    """The training forward's output equals the inference forward's bit for
+    bit; the saved per-map outputs and log-sum-exp match the oracle's maps."""
+    B, H, T, D = x["q1"].shape
+    d = {k: v.to(DEV) for k, v in x.items()}
+    say(f"fwd_train {tag} causal={causal} headnorm={headnorm}")
+    ref_out = da.diffattn_fwd(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam.to(DEV),
+                              causal=causal, headnorm=headnorm)
+    out, saved = da.diffattn_fwd_train(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam.to(DEV),
+                                       causal=causal, headnorm=headnorm)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    n = B * H * T * 2 * D
+    sv = saved.view(torch.float32)
+    o1 = sv[:n].view(B, H, T, 2 * D)
+    o2 = sv[n:2 * n].view(B, H, T, 2 * D)
+    lse = sv[2 * n:2 * n + 2 * B * H * T].view(B, H, 2, T)
+    a1, a2 = oracle.score_maps(x["q1"], x["k1"], x["q2"], x["k2"], causal)
+    v64 = x["v"].double().numpy()
+    assert np.max(np.abs(_np(o1) - a1 @ v64)) <= 2e-2
+    assert np.max(np.abs(_np(o2) - a2 @ v64)) <= 2e-2
+    # log2-domain log-sum-exp of the scaled scores, rebuilt from the maps:
+    # A = 2^(s log2(e)/sqrt(D) - lse) at any allowed entry, e.g. the
+    # diagonal (allowed under both masks)
+    s1 = np.einsum("bhtd,bhtd->bht", x["q1"].double().numpy(), x["k1"].double().numpy()) / np.sqrt(D)
+    s2 = np.einsum("bhtd,bhtd->bht", x["q2"].double().numpy(), x["k2"].double().numpy()) / np.sqrt(D)
+    diag1 = np.diagonal(a1, axis1=2, axis2=3)
+    diag2 = np.diagonal(a2, axis1=2, axis2=3)
+    ref1 = (s1 - np.log(diag1)) / np.log(2.0)
+    ref2 = (s2 - np.log(diag2)) / np.log(2.0)
+    # The forward's row sum is of fp32 probabilities or of their bf16
+    # roundings (unit roundoff 2^-8, 8 significant bits), so log2 of the
+    # sum is off by at most 2^-8 / ln 2 = 5.64e-3.  Its scores use
+    # q * log2(e)/sqrt(D) rounded to bf16 (relative error <= 2^-8 + 2^-24
+    # per element), which moves score s_ij by at most
+    # delta_ij = (2^-8 + 2^-24) log2(e)/sqrt(D) sum_d |q_id k_jd|, and the
+    # log-sum-exp of row i by at most max_j delta_ij over its visible keys.
+    for br, (qn, kn, ref) in enumerate((("q1", "k1", ref1), ("q2", "k2", ref2))):
+        absqk = np.abs(x[qn].double().numpy()) @ np.abs(x[kn].double().numpy()).transpose(0, 1, 3, 2)
+        if causal:
+            absqk = np.where(np.tril(np.ones((T, T), dtype=bool)), absqk, 0.0)
+        delta = (2.0 ** -8 + 2.0 ** -24) * (1.4426950408889634 / np.sqrt(D)) * absqk.max(axis=-1)
+        assert np.all(np.abs(_np(lse[:, :, br]) - ref) <= 5.7e-3 + delta)
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 def test_fwd_train_output_and_saved_state(D):
-    """The training forward's output is the inference forward's, bit for bit;
-    the saved per-map outputs and log-sum-exp match the oracle's maps."""
     B, H, T = 2, 2, 300
     x = prefill_inputs(B, H, T, D, "bf16", seed=3200 + D)
     lam = torch.tensor([0.5, 0.9], dtype=torch.float32)
-    d = {k: v.to(DEV) for k, v in x.items()}
     for causal, headnorm in ((True, False), (False, True)):
-        say(f"fwd_train causal={causal} headnorm={headnorm}")
-        ref_out = da.diffattn_fwd(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam.to(DEV),
-                                  causal=causal, headnorm=headnorm)
-        out, saved = da.diffattn_fwd_train(d["q1"], d["k1"], d["q2"], d["k2"], d["v"], lam.to(DEV),
-                                           causal=causal, headnorm=headnorm)
-        torch.cuda.synchronize()
-        assert torch.equal(out, ref_out)
-        n = B * H * T * 2 * D
-        sv = saved.view(torch.float32)
-        o1 = sv[:n].view(B, H, T, 2 * D)
-        o2 = sv[n:2 * n].view(B, H, T, 2 * D)
-        lse = sv[2 * n:2 * n + 2 * B * H * T].view(B, H, 2, T)
-        a1, a2 = oracle.score_maps(x["q1"], x["k1"], x["q2"], x["k2"], causal)
-        v64 = x["v"].double().numpy()
-        assert np.max(np.abs(_np(o1) - a1 @ v64)) <= 2e-2
-        assert np.max(np.abs(_np(o2) - a2 @ v64)) <= 2e-2
-        # log2-domain log-sum-exp of the scaled scores, rebuilt from the
-        # maps: A = 2^(s log2(e)/sqrt(D) - lse) at any allowed entry, e.g.
-        # the diagonal (allowed under both masks)
-        s1 = np.einsum("bhtd,bhtd->bht", x["q1"].double().numpy(), x["k1"].double().numpy()) / np.sqrt(D)
-        s2 = np.einsum("bhtd,bhtd->bht", x["q2"].double().numpy(), x["k2"].double().numpy()) / np.sqrt(D)
-        diag1 = np.diagonal(a1, axis1=2, axis2=3)
-        diag2 = np.diagonal(a2, axis1=2, axis2=3)
-        ref1 = (s1 - np.log(diag1)) / np.log(2.0)
-        ref2 = (s2 - np.log(diag2)) / np.log(2.0)
-        # The forward's row sum is of fp32 probabilities or of their bf16
-        # roundings (unit roundoff 2^-8, 8 significant bits), so log2 of the
-        # sum is off by at most 2^-8 / ln 2 = 5.64e-3.  Its scores use
-        # q * log2(e)/sqrt(D) rounded to bf16 (relative error <= 2^-8 + 2^-24
-        # per element), which moves score s_ij by at most
-        # delta_ij = (2^-8 + 2^-24) log2(e)/sqrt(D) sum_d |q_id k_jd|, and the
-        # log-sum-exp of row i by at most max_j delta_ij over its visible keys.
-        for br, (qn, kn, ref) in enumerate((("q1", "k1", ref1), ("q2", "k2", ref2))):
-            absqk = np.abs(x[qn].double().numpy()) @ np.abs(x[kn].double().numpy()).transpose(0, 1, 3, 2)
-            if causal:
-                absqk = np.where(np.tril(np.ones((T, T), dtype=bool)), absqk, 0.0)
-            delta = (2.0 ** -8 + 2.0 ** -24) * (1.4426950408889634 / np.sqrt(D)) * absqk.max(axis=-1)
-            assert np.all(np.abs(_np(lse[:, :, br]) - ref) <= 5.7e-3 + delta)
+        _check_train_saved_state(x, lam, causal, headnorm, f"D={D} T={T}")
+
+
+def test_fwd_train_long_causal_rows_saved_state():
+    """Causal D = 64 rows longer than 4096 take the two-wave ping-pong kernel,
+    whose training forward saves the maps from its own epilogue."""
+    x = prefill_inputs(1, 2, 4500, 64, "bf16", seed=3264)
+    lam = torch.tensor([0.6, 1.1], dtype=torch.float32)
+    _check_train_saved_state(x, lam, True, True, "D=64 T=4500")
 
 
 def test_bwd_lambda_vectors():
