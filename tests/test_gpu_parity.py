@@ -177,6 +177,31 @@ def test_value_offset_property_fp32():
     assert diff <= 1e-4, diff
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_output_rounding_is_nearest_even(D):
+    """The bf16 output is rounded to nearest, ties to even.  With one key (T = 1,
+    or a decode cache of one row) and V = 1 the fp32 result is exactly
+    1 - lambda; lambda = -2^-8 puts it halfway between bf16 1.0 (even) and
+    1.0078125, lambda = -3 2^-8 halfway between 1.0078125 and 1.015625
+    (even).  Nearest-even gives 1.0 and 1.015625; truncation gives 1.0 and
+    1.0078125, round-half-up 1.0078125 and 1.015625."""
+    lam = torch.tensor([-2.0 ** -8, -3.0 * 2.0 ** -8], dtype=torch.float32, device=DEV)
+    want = torch.tensor([1.0, 1.015625], dtype=torch.float32, device=DEV)
+    g = torch.Generator().manual_seed(77)
+    q = torch.randn((1, 2, 1, D), generator=g).bfloat16().to(DEV)
+    k = torch.randn((1, 2, 1, D), generator=g).bfloat16().to(DEV)
+    v = torch.ones((1, 2, 1, 2 * D), dtype=torch.bfloat16, device=DEV)
+    for causal in (True, False):
+        say(f"rounding D={D} causal={causal}")
+        out = da.diffattn_fwd(q, k, q, k, v, lam, causal=causal, headnorm=False)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0, :, 0].float(), want[:, None].expand(2, 2 * D)), out[0, :, 0, :4]
+    say(f"rounding decode D={D}")
+    out = da.diffattn_decode(q[:, :, 0], k, q[:, :, 0], k, v, lam, headnorm=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0].float(), want[:, None].expand(2, 2 * D)), out[0, :, :4]
+
+
 def test_repeatable_bitwise():
     x = to_dev(prefill_inputs(2, 4, 1500, 64, "bf16", seed=21))
     a = run_fwd(x, 0.7, True, True)
