@@ -880,6 +880,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
 
   // ---- epilogue: combine the maps, optional head norm, store -----------------
   bf16* __restrict__ O = (bf16*)a.out + (bb * a.sb[5] + h * a.sh[5]);
+  // rows staged through LDS for whole-row stores: split waves use their own
+  // exchange rows (already read by then), other shapes a slice of the free
+  // tile ring per wave, where that fits
+  constexpr int NCH = C::DV / 8;  // 16-byte columns per output row
+  constexpr bool STAGE_OUT = SPLIT ? (2 * C::DV <= 4 * C::XP) : (NW * NQB * 32 * 2 * C::DV <= C::SMEM);
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int query = q0 + qb * 32 + l32;
@@ -920,7 +925,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[cb][r] *= f;
     }
-    if (query < T) {
+    if constexpr (STAGE_OUT) {
+      // The lane layout holds 8 bytes of a row per 16-byte column, so direct
+      // stores touch 32 rows per instruction.  Instead the wave writes its
+      // 32 rows to its own LDS rows (16-byte columns XOR-swizzled by the row,
+      // conflict-free both ways), then stores whole rows: 16-byte lanes,
+      // NCH lanes per row.
+      char* stg = SPLIT ? (char*)(xch + (wq * C::QPW + qb * 32) * C::XP)
+                        : smem + (wave * NQB + qb) * 32 * (2 * C::DV);
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const bf16x4 v4 = {(bf16)o[cb][4 * g], (bf16)o[cb][4 * g + 1], (bf16)o[cb][4 * g + 2],
+                             (bf16)o[cb][4 * g + 3]};
+          const int col = (4 * cb + g) ^ (l32 & (NCH - 1));
+          *(bf16x4*)(stg + l32 * (2 * C::DV) + col * 16 + hi * 8) = v4;
+        }
+      constexpr int RPI = 64 / NCH;  // rows per store instruction
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / NCH;
+        const int c = lane % NCH;
+        const u32x4 w4 = *(const u32x4*)(stg + r * (2 * C::DV) + ((c ^ (r & (NCH - 1))) << 4));
+        const int row = q0 + qb * 32 + r;
+        if (row < T) *(u32x4*)(O + (size_t)row * a.sr[5] + c * 8) = w4;
+      }
+    } else if (query < T) {
       bf16* dst = O + (size_t)query * a.sr[5];
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb)
