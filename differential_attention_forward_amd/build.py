@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 MICRO_LIB = os.path.join(PKG, "libdiffattn_micro.so")
+# debug variant: every kernel fills its LDS with NaN patterns at entry
+# (DIFFATTN_LDS_POISON in csrc/common.h); tests compare it with LIB bit for bit
+POISON_LIB = os.path.join(PKG, "libdiffattn_poison.so")
 
 KERNEL_SOURCES = ["prefill.hip", "decode.hip", "lambda.hip", "backward.hip", "scratch.hip"]
 HOST_SOURCES = ["abi.hip"]
@@ -36,8 +39,8 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, flags) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, flags, tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     cmd = [hipcc(), *COMMON, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -55,17 +58,22 @@ def _link(objs, out: str) -> None:
 
 
 def build_library(verbose: bool = True) -> str:
-    """libdiffattn.so (the attention library) and libdiffattn_micro.so (the
-    microbenchmarks bench.py reports measured ceilings from)."""
+    """libdiffattn.so (the attention library), libdiffattn_poison.so (the same
+    with LDS poisoned at every kernel's entry, for tests) and
+    libdiffattn_micro.so (the microbenchmarks bench.py reports measured
+    ceilings from)."""
     os.makedirs(BUILD, exist_ok=True)
-    jobs = ([(s, KERNEL_FLAGS) for s in KERNEL_SOURCES + ["micro.hip"]] +
-            [(s, []) for s in HOST_SOURCES])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
-        objs = dict(zip([j[0] for j in jobs], ex.map(lambda j: _compile(*j), jobs)))
+    jobs = ([(s, KERNEL_FLAGS, "") for s in KERNEL_SOURCES + ["micro.hip"]] +
+            [(s, [], "") for s in HOST_SOURCES] +
+            [(s, KERNEL_FLAGS + ["-DDIFFATTN_LDS_POISON"], "_poison") for s in KERNEL_SOURCES])
+    workers = min(len(jobs), os.cpu_count() or 8)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = dict(zip([j[0] + j[2] for j in jobs], ex.map(lambda j: _compile(*j), jobs)))
     _link([objs[s] for s in KERNEL_SOURCES + HOST_SOURCES], LIB)
+    _link([objs[s + "_poison"] for s in KERNEL_SOURCES] + [objs[s] for s in HOST_SOURCES], POISON_LIB)
     _link([objs["micro.hip"]], MICRO_LIB)
     if verbose:
-        print(f"built {LIB} and {MICRO_LIB}")
+        print(f"built {LIB}, {POISON_LIB} and {MICRO_LIB}")
     return LIB
 
 

@@ -96,6 +96,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   constexpr int TPR = DV / 8;          // threads per row, 8 channels each
   constexpr int RPP = 256 / TPR;       // rows per pass
   __shared__ float red[4];
+  lds_poison(red, sizeof(red));
+  lds_poison_done();
   const int chunk = blockIdx.x % a.nchunk;
   const int bh = blockIdx.x / a.nchunk;
   const int h = bh % a.H;
@@ -545,6 +547,8 @@ __device__ __forceinline__ void kv_body(const BwdArgs& a, char* smem, int w) {
 template <int D, int NW, int NSTAGE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2))) void bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[CfgKV<D, NW, NSTAGE>::SMEM];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
   const int nkt = (a.T + CfgKV<D, NW, NSTAGE>::BK - 1) / CfgKV<D, NW, NSTAGE>::BK;
   const int w2 = xcd_remap(blockIdx.x, 2 * a.B * a.H * nkt);
   if (w2 & 1) kv_body<D, NW, NSTAGE, CAUSAL, kKvDv>(a, smem, w2 >> 1);
@@ -581,6 +585,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 12
   constexpr int DV = C::DV;
   constexpr int PD = NSTAGE - 1;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

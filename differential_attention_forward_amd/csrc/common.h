@@ -71,6 +71,27 @@ __device__ inline float reparam_lambda(const float* __restrict__ lq1, const floa
   return (e1 - e2) + lambda_init;
 }
 
+// Debug builds (-DDIFFATTN_LDS_POISON) fill every LDS array a kernel declares
+// with all-ones words (NaN as fp32 and as bf16) at entry, before anything else
+// touches LDS, so that reading LDS the kernel never wrote (a missing wait or
+// barrier, a stray index) changes the result instead of reusing a stale value
+// that happens to be right.  No-ops otherwise.  Every thread of the workgroup
+// calls both, poison first for each array, then done once.
+__device__ inline void lds_poison(void* p, size_t bytes) {
+#ifdef DIFFATTN_LDS_POISON
+  uint32_t* w = (uint32_t*)p;
+  for (size_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0xffffffffu;
+#else
+  (void)p;
+  (void)bytes;
+#endif
+}
+__device__ inline void lds_poison_done() {
+#ifdef DIFFATTN_LDS_POISON
+  __syncthreads();
+#endif
+}
+
 // bf16 <-> fp32 on raw 16-bit patterns (bf16 is the top half of an fp32).
 __device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -85,6 +85,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   __shared__ float2 sp[kSub];         // per key: (s1, s2) then (p1, p2)
   __shared__ float red[kWaves];
   __shared__ float accred[kWaves][2][DV];
+  __shared__ float lred[kWaves][2];
+  lds_poison(sp, sizeof(sp));
+  lds_poison(red, sizeof(red));
+  lds_poison(accred, sizeof(accred));
+  lds_poison(lred, sizeof(lred));
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int S = a.S;
@@ -229,7 +235,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
       accred[wave][1][vsub * EPC + e] = acc2[e];
     }
   }
-  __shared__ float lred[kWaves][2];
   if (lane == 0) {
     lred[wave][0] = l1;
     lred[wave][1] = l2;
@@ -266,6 +271,12 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   __shared__ float sm[2][kMaxSplitsLds];
   __shared__ float part[NG][4][DV];
   __shared__ float red[4];
+  __shared__ float mred[4][2];
+  lds_poison(sm, sizeof(sm));
+  lds_poison(part, sizeof(part));
+  lds_poison(red, sizeof(red));
+  lds_poison(mred, sizeof(mred));
+  lds_poison_done();
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
@@ -286,7 +297,6 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   }
   M1 = wave_max(M1);
   M2 = wave_max(M2);
-  __shared__ float mred[4][2];
   if ((tid & 63) == 0) {
     mred[tid >> 6][0] = M1;
     mred[tid >> 6][1] = M2;
@@ -391,6 +401,8 @@ void decode_v2_mma_kernel(DecodeArgs a) {
   constexpr int kPf = 2;              // blocks in flight per wave, in registers
   static_assert(NR <= 32, "query columns");
   __shared__ __attribute__((aligned(1024))) char smem[kWaves][2 * KB];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;

@@ -90,6 +90,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
   using C = Cfg<D, NQB, NW, BC, SPLIT>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::SMEM];
   float* const smem = (float*)smem_raw;
+  lds_poison(smem_raw, sizeof(smem_raw));
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -475,6 +477,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   constexpr int BC = C::BC;
   constexpr int PD = NSTAGE - 1;  // prefetch distance in tiles
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1002,6 +1006,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(2 * SEGW <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   __shared__ int simd_of[NW];
+  lds_poison(smem, sizeof(smem));
+  lds_poison(simd_of, sizeof(simd_of));
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
