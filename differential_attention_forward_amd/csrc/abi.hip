@@ -68,6 +68,7 @@ diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float*
   for (const void* p : ins)
     if (!aligned(p, 4)) return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(lambda_out, 4)) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!diffattn::grid_fits(H, 64)) return DIFFATTN_ERR_UNSUPPORTED;  // one 64-thread workgroup per head
   const size_t nin = (size_t)H * Dl * sizeof(float), nout = (size_t)H * sizeof(float);
   for (const void* p : ins)
     if (overlaps(lambda_out, nout, p, nin)) return DIFFATTN_ERR_INVALID;
@@ -90,8 +91,10 @@ diffattn_status check_fwd(int dtype, int B, int H, int T, int D, const void* q1,
   for (const void* p : ins)
     if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(out, 16)) return DIFFATTN_ERR_UNSUPPORTED;
-  // every (b, h) slice and every work index must fit the 32-bit index math
-  if ((long long)B * H > 0x7fffffffLL || (long long)T * 2 * D > 0x7fffffffLL)
+  // every (b, h) slice and every work index must fit the 32-bit index math,
+  // and the launch grid what one dispatch can express
+  if ((long long)B * H > 0x7fffffffLL || (long long)T * 2 * D > 0x7fffffffLL ||
+      !diffattn::row_grid_fits(B, H, T))
     return DIFFATTN_ERR_UNSUPPORTED;
   const size_t es = elem_bytes(dtype);
   const size_t nqk = (size_t)B * H * T * D * es;
@@ -214,7 +217,8 @@ diffattn_status diffattn_fwd_strided(int dtype, int B, int H, int T, int D, cons
       if (strides[3 * i + j] % 8) return DIFFATTN_ERR_UNSUPPORTED;
   }
   if (!aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
-  if ((long long)B * H > 0x7fffffffLL || (long long)T * 2 * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H > 0x7fffffffLL || (long long)T * 2 * D > 0x7fffffffLL || !diffattn::row_grid_fits(B, H, T))
+    return DIFFATTN_ERR_UNSUPPORTED;
   // K and V rows are fetched at 32-bit byte offsets from their (b, h) slice;
   // query and output row strides are ints
   for (int i = 0; i < 6; ++i) {
@@ -309,7 +313,8 @@ diffattn_status diffattn_attention_fwd(int dtype, int B, int H, int T, int D, co
   for (const void* p : ins)
     if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(out, 16)) return DIFFATTN_ERR_UNSUPPORTED;
-  if ((long long)B * H > 0x7fffffffLL || (long long)T * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H > 0x7fffffffLL || (long long)T * D > 0x7fffffffLL || !diffattn::row_grid_fits(B, H, T))
+    return DIFFATTN_ERR_UNSUPPORTED;
   const size_t n = (size_t)B * H * T * D * elem_bytes(dtype);
   for (const void* p : ins)
     if (overlaps(out, n, p, n)) return DIFFATTN_ERR_INVALID;
@@ -348,7 +353,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool train_sizes_ok(int B, int H, int T, int D) {
   if (B < 1 || H < 1 || T < 1 || (D != 32 && D != 64 && D != 128)) return false;
-  return (long long)B * H <= 0x7fffffffLL && (long long)T * 2 * D <= 0x7fffffffLL;
+  return (long long)B * H <= 0x7fffffffLL && (long long)T * 2 * D <= 0x7fffffffLL &&
+         diffattn::row_grid_fits(B, H, T);
 }
 
 }  // namespace
@@ -507,7 +513,9 @@ diffattn_status decode_impl(int dtype, int B, int H, int L, int D, const void* q
     if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(out, 16) || !aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
   const int S = num_splits ? num_splits : diffattn_decode_default_splits(B, H, L);
-  if ((long long)B * H * S > 0x7fffffffLL || (long long)L * 2 * D > 0x7fffffffLL)
+  // split-K grid of B H S workgroups, reduce grid of B H
+  if (!diffattn::grid_fits((long long)B * H * S, diffattn::kDecodeThreads) ||
+      !diffattn::grid_fits((long long)B * H, 256) || (long long)L * 2 * D > 0x7fffffffLL)
     return DIFFATTN_ERR_UNSUPPORTED;
   const size_t need = diffattn_decode_workspace_bytes(B, H, L, D, S);
   if (lib_scratch) {
@@ -602,7 +610,8 @@ diffattn_status diffattn_v2_fwd(int dtype, int B, int H, int Hkv, int T, int D, 
   for (const void* p : ins)
     if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(out, 16) || !aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
-  if ((long long)B * H > 0x7fffffffLL || (long long)T * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H > 0x7fffffffLL || (long long)T * D > 0x7fffffffLL || !diffattn::row_grid_fits(B, H, T))
+    return DIFFATTN_ERR_UNSUPPORTED;
   const size_t nq = (size_t)B * H * T * D * 2, nkv = (size_t)B * Hkv * T * D * 2;
   const size_t sizes[4] = {nq, nq, nkv, nkv};
   for (int i = 0; i < 4; ++i)
@@ -657,7 +666,10 @@ diffattn_status diffattn_v2_decode(int dtype, int B, int H, int Hkv, int L, int 
     if (!aligned(p, 16)) return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(out, 16) || !aligned(lambda, 4)) return DIFFATTN_ERR_UNSUPPORTED;
   const int S = num_splits ? num_splits : diffattn_decode_default_splits(B, Hkv, L);
-  if ((long long)B * H * S > 0x7fffffffLL || (long long)L * D > 0x7fffffffLL) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!diffattn::grid_fits((long long)B * Hkv * S, diffattn::kDecodeThreads) ||
+      !diffattn::grid_fits((long long)B * H, 256) || (long long)B * H * S > 0x7fffffffLL ||
+      (long long)L * D > 0x7fffffffLL)
+    return DIFFATTN_ERR_UNSUPPORTED;
   const size_t need = diffattn_v2_decode_workspace_bytes(B, H, Hkv, L, D, S);
   if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return DIFFATTN_ERR_UNSUPPORTED;

@@ -805,11 +805,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 12
 // ---- launchers --------------------------------------------------------------
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
-  const int gp = a.nchunk * a.B * a.H;
-  if (headnorm) bwd_prep_kernel<D, true><<<gp, 256, 0, stream>>>(a);
-  else bwd_prep_kernel<D, false><<<gp, 256, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // Four-wave workgroups with two LDS stages: two kv or q workgroups per CU
   // (the q pass takes 16% less time than with one eight-wave workgroup at
   // D = 64).  D = 128: a q wave holds 128 accumulators and 128 fragment
@@ -817,12 +812,21 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
   constexpr int KNW = 4, QNW = 4;
   constexpr int KST = 2;  // two stages: two kv workgroups per CU
   constexpr int QST = 2;
-  const int nkt = (a.T + 32 * KNW - 1) / (32 * KNW);
-  bwd_kv_kernel<D, KNW, KST, CAUSAL><<<2 * a.B * a.H * nkt, KNW * 64, 0, stream>>>(a);
+  const long long bh = (long long)a.B * a.H;
+  const long long gp = (long long)a.nchunk * bh;
+  const long long gkv = 2 * bh * ((a.T + 32 * KNW - 1) / (32 * KNW));
+  const long long gq = bh * ((a.T + 32 * QNW - 1) / (32 * QNW));
+  // every grid is checked before the first launch, so a refused shape runs nothing
+  if (!grid_fits(gp, 256) || !grid_fits(gkv, KNW * 64) || !grid_fits(gq, QNW * 64))
+    return hipErrorInvalidConfiguration;
+  if (headnorm) bwd_prep_kernel<D, true><<<dim3((unsigned)gp), dim3(256), 0, stream>>>(a);
+  else bwd_prep_kernel<D, false><<<dim3((unsigned)gp), dim3(256), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_kv_kernel<D, KNW, KST, CAUSAL><<<dim3((unsigned)gkv), dim3(KNW * 64), 0, stream>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nqt = (a.T + 32 * QNW - 1) / (32 * QNW);
-  bwd_q_kernel<D, QNW, QST, CAUSAL><<<a.B * a.H * nqt, QNW * 64, 0, stream>>>(a);
+  bwd_q_kernel<D, QNW, QST, CAUSAL><<<dim3((unsigned)gq), dim3(QNW * 64), 0, stream>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   bwd_lambda_kernel<<<a.H, 64, 0, stream>>>(a);

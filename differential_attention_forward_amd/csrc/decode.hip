@@ -34,7 +34,7 @@
 namespace diffattn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kDecodeThreads;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSub = 512;  // keys per sub-chunk (scores kept in LDS)
 constexpr int kUnroll = 8;
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 template <int D, bool F32>
 hipError_t launch_d(const DecodeArgs& a, bool headnorm, hipStream_t stream) {
   const long nblk = (long)a.B * a.H * a.S;
-  if (nblk > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(nblk, kThreads) || !grid_fits((long long)a.B * a.H, 256)) return hipErrorInvalidConfiguration;
   decode_partial_kernel<D, F32><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -610,7 +610,7 @@ void decode_v2_mma_kernel(DecodeArgs a) {
 template <int D, int G>
 hipError_t launch_v2_d(const DecodeArgs& a, hipStream_t stream) {
   const long nblk = (long)a.B * a.Hkv * a.S;
-  if (nblk > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(nblk, kThreads) || !grid_fits((long long)a.B * a.H, 256)) return hipErrorInvalidConfiguration;
   decode_v2_mma_kernel<D, G><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

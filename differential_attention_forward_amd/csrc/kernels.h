@@ -7,6 +7,26 @@
 
 namespace diffattn {
 
+// What one dispatch can express: at most 2^31 - 1 workgroups along x, and a
+// grid of at most 2^32 - 1 work-items (the dispatch packet holds the grid
+// size in work-items as a 32-bit value).  Every launcher checks its shape.
+inline bool grid_fits(long long blocks, long long threads) {
+  return blocks >= 1 && blocks <= 0x7fffffffLL && blocks * threads <= 0xffffffffLL;
+}
+
+// Threads of a decode split-K workgroup (decode_partial_kernel and
+// decode_v2_mma_kernel): the decode grid is B x H (x Hkv for V2) x S of them.
+constexpr int kDecodeThreads = 256;
+
+// Every prefill, training-forward and backward launch runs at most 4
+// work-items per query (or key) row of its padded row range, and pads each
+// head's T rows by at most 255, so 4 B H (T + 255) bounds their grids; the
+// entry points refuse larger shapes before any launch.  (Such shapes need
+// more than 2^30 rows, i.e. inputs far beyond one GPU's memory.)
+inline bool row_grid_fits(long long B, long long H, long long T) {
+  return 4 * B * H * (T + 255) <= 0xffffffffLL;
+}
+
 struct FwdArgs {
   const void* q1;
   const void* k1;

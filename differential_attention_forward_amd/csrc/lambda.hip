@@ -24,6 +24,7 @@ __global__ __launch_bounds__(64) void lambda_kernel(const float* __restrict__ lq
 
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
                          int H, int Dl, float lambda_init, float* out, hipStream_t stream) {
+  if (!grid_fits(H, 64)) return hipErrorInvalidConfiguration;
   lambda_kernel<<<dim3(H), dim3(64), 0, stream>>>(lq1, lk1, lq2, lk2, Dl, lambda_init, out);
   return hipGetLastError();
 }

@@ -1410,7 +1410,7 @@ hipError_t launch_pp(const FwdArgs& a, bool causal, bool headnorm, hipStream_t s
   using C = CfgB<D, 1, 8, 4, false>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
-  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(grid, C::NT)) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (causal) {
     if (headnorm) fwd_pp_kernel<D, true, true><<<g, b, 0, stream>>>(a);
@@ -1427,7 +1427,7 @@ hipError_t launch_bf16(const FwdArgs& a, bool causal, bool headnorm, hipStream_t
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
-  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(grid, C::NT)) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (causal) {
     if (headnorm) fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, true><<<g, b, 0, stream>>>(a);
@@ -1444,7 +1444,7 @@ hipError_t launch_window(const FwdArgs& a, bool headnorm, hipStream_t stream) {
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
-  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(grid, C::NT)) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (headnorm) fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, true, 2, false, true><<<g, b, 0, stream>>>(a);
   else fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, false, 2, false, true><<<g, b, 0, stream>>>(a);
@@ -1456,7 +1456,7 @@ hipError_t launch_v2_d(const FwdArgs& a, bool causal, hipStream_t stream) {
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, 2, true>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
-  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(grid, C::NT)) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (causal) fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, true, false, 2, true><<<g, b, 0, stream>>>(a);
   else fwd_bf16_kernel<D, NQB, NW, NSTAGE, SPLIT, false, false, 2, true><<<g, b, 0, stream>>>(a);
@@ -1468,7 +1468,7 @@ hipError_t launch_std(const FwdArgs& a, bool causal, hipStream_t stream) {
   using C = CfgB<D, NQB, NW, NSTAGE, false, 1>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
-  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(grid, C::NT)) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (causal) fwd_bf16_kernel<D, NQB, NW, NSTAGE, false, true, false, 1><<<g, b, 0, stream>>>(a);
   else fwd_bf16_kernel<D, NQB, NW, NSTAGE, false, false, false, 1><<<g, b, 0, stream>>>(a);
@@ -1480,7 +1480,7 @@ hipError_t launch_f32(const FwdArgs& a, bool causal, bool headnorm, hipStream_t 
   using C = Cfg<D, NQB, NW, BC, SPLIT>;
   const long nqt = (a.T + C::BR - 1) / C::BR;
   const long grid = (long)a.B * a.H * nqt;
-  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (!grid_fits(grid, C::NT)) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(C::NT);
   if (causal) {
     if (headnorm) fwd_f32_kernel<D, NQB, NW, BC, SPLIT, true, true><<<g, b, 0, stream>>>(a);

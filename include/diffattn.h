@@ -28,6 +28,16 @@
  *   - lambda is a per-head fp32 device array [H]; a per-layer scalar is the
  *     case of all heads equal.  It is not clamped: negative values and values
  *     above 1 are allowed (paperleet page, "Return requirements").
+ *   - Size limits ("grid size" below; beyond them ERR_UNSUPPORTED, nothing
+ *     launched).  Offsets between heads and batches are 64-bit, so tensors
+ *     may exceed 4 GiB; within one (b, h) slice, T x (row width) must stay
+ *     below 2^31 elements, and B x H below 2^31.  A dispatch holds at most
+ *     2^32 - 1 work-items: prefill, training forward and backward need
+ *     4 B H (T + 255) <= 2^32 - 1 (every one of their launches runs at most 4
+ *     work-items per row of its padded row range; this only binds beyond
+ *     2^30 rows, far past one GPU's memory); decode needs B H S <= 2^24 - 1
+ *     split-K workgroups of 256 threads (S the split count; V2: B Hkv S);
+ *     diffattn_lambda needs H <= 2^26 - 1 (one 64-thread workgroup per head).
  */
 #ifndef DIFFATTN_H
 #define DIFFATTN_H

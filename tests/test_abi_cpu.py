@@ -2,7 +2,10 @@
 and rejects invalid arguments before any HIP call (no GPU needed).
 
 Pointers passed here are fake addresses; validation only compares them and
-returns before anything dereferences or launches.
+returns before anything dereferences or launches.  The few checks that a
+valid call gets past validation make it only where no HIP device is visible
+(it then fails at the launch); with a device it would launch kernels on
+unmapped addresses, so there they are skipped.
 """
 
 import ctypes
@@ -22,6 +25,11 @@ F32, BF16 = da.DIFFATTN_F32, da.DIFFATTN_BF16
 @pytest.fixture(scope="module")
 def L():
     return da.lib()
+
+
+def _no_device():
+    import torch
+    return torch.cuda.device_count() == 0  # counts devices without initialising one
 
 
 def test_header_symbols_exported(L):
@@ -141,7 +149,8 @@ def test_fwd_reparam_validation(L):
     assert fwdr(L, vecs=[P(10), P(11), P(12), P(5, 8)]) == INVALID  # out over a vector
     # a valid call only fails at the launch: no GPU here, so it must not report
     # a validation error (OK or ERR_HIP)
-    assert fwdr(L, lam_out=P(20)) in (OK, 4)
+    if _no_device():
+        assert fwdr(L, lam_out=P(20)) in (OK, 4)
 
 
 def att(L, dtype=BF16, B=1, H=2, T=8, D=128, ptrs=None):
@@ -389,7 +398,8 @@ def test_fwd_train_validation(L):
     assert fwdt(L, ptrs=alias) == INVALID
     alias[7] = P(4)            # saved over v
     assert fwdt(L, ptrs=alias) == INVALID
-    assert fwdt(L) in (OK, 4)
+    if _no_device():
+        assert fwdt(L) in (OK, 4)
 
 
 def bwd(L, dtype=BF16, B=1, H=2, T=8, D=64, ins=None, outs=None, vecs=None, dvecs=None, Dl=16,
@@ -427,5 +437,44 @@ def test_bwd_validation(L):
     assert bwd(L, outs=[P(10), P(11), P(12), P(13), P(14), P(7, 16)]) == INVALID    # dlambda in saved
     assert bwd(L, ws=P(6)) == INVALID                                                # workspace over dout
     assert bwd(L, vecs=vecs, dvecs=[P(24), P(25), P(26), P(20)]) == INVALID          # dlk2 over lq1
-    assert bwd(L, vecs=vecs, dvecs=dvecs) in (OK, 4)
-    assert bwd(L) in (OK, 4)
+    if _no_device():
+        assert bwd(L, vecs=vecs, dvecs=dvecs) in (OK, 4)
+        assert bwd(L) in (OK, 4)
+
+
+# fake device addresses 2^40 bytes apart, for shapes whose tensors exceed 4 GiB
+def F(i):
+    return ctypes.c_void_p((1 << 40) * (i + 1))
+
+
+def test_grid_limits(L):
+    """Shapes whose launch grid one dispatch cannot express (more than 2^32 - 1
+    work-items) are refused with ERR_UNSUPPORTED before anything runs; the
+    largest accepted shapes get past validation."""
+    far = [F(i) for i in range(8)]
+    # prefill / training / backward: 4 B H (T + 255) <= 2^32 - 1
+    H = 1 << 20
+    assert 4 * H * (768 + 255) <= 2 ** 32 - 1 < 4 * H * (769 + 255)
+    assert fwd(L, B=1, H=H, T=769, D=32, ptrs=far[:7]) == UNSUPPORTED
+    assert att(L, B=1, H=H, T=769, D=64, ptrs=far[:4]) == UNSUPPORTED
+    assert fwdt(L, B=1, H=H, T=769, D=32, ptrs=far) == UNSUPPORTED
+    assert bwd(L, B=1, H=H, T=769, D=32, ins=far, outs=[F(10 + k) for k in range(6)],
+               ws=F(20)) == UNSUPPORTED
+    assert da.diffattn_train_saved_bytes(1, H, 769, 32) == 0
+    assert da.diffattn_bwd_workspace_bytes(1, H, 769, 32) == 0
+    assert da.diffattn_train_saved_bytes(1, H, 768, 32) > 0
+    # decode: B H S split-K workgroups of 256 threads
+    big_ws = 1 << 39
+    assert dec(L, B=1024, H=256, Lk=64, D=32, splits=64, ws=F(8), wsb=big_ws, ptrs=far[:7]) == UNSUPPORTED
+    assert v2d(L, B=1024, H=256, Hkv=256, Lk=64, D=64, splits=64, ws=F(8), wsb=big_ws,
+               ptrs=far[:6]) == UNSUPPORTED
+    # lambda: one 64-thread workgroup per head
+    p = [F(i) for i in range(5)]
+    assert L.diffattn_lambda(p[0], p[1], p[2], p[3], 1 << 26, 8, ctypes.c_float(0.2), p[4],
+                             None) == UNSUPPORTED
+    if _no_device():
+        assert fwd(L, B=1, H=H, T=768, D=32, ptrs=far[:7]) in (OK, 4)
+        assert dec(L, B=1024, H=255, Lk=64, D=32, splits=64, ws=F(8), wsb=big_ws,
+                   ptrs=far[:7]) in (OK, 4)
+        assert L.diffattn_lambda(p[0], p[1], p[2], p[3], (1 << 26) - 1, 8, ctypes.c_float(0.2),
+                                 p[4], None) in (OK, 4)
