@@ -476,6 +476,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   using C = CfgB<D, NQB, NW, NSTAGE, SPLIT, MAPS, SHKV>;
   constexpr int BC = C::BC;
   constexpr int PD = NSTAGE - 1;  // prefetch distance in tiles
+  // One-map waves at D <= 64 in eight-wave workgroups (two waves per SIMD,
+  // 256 registers each, about 170 used) read a block's LDS fragments ahead
+  // of their MFMAs: every K fragment before the first score MFMA, every V
+  // fragment right after the score MFMAs, in flight during the softmax.  Left
+  // to itself the compiler issues each read just before its MFMA and waits on
+  // it at once, about six LDS round trips per block and wave; the early
+  // reads take 204 registers and 3-5% off the T = 4096 causal prefill
+  // (bit-identical).  Other shapes have no registers to spare.
+  constexpr bool PREF = C::NBR * NQB == 1 && D <= 64 && !SHKV && NW == 8;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   lds_poison(smem, sizeof(smem));
   lds_poison_done();
@@ -663,6 +672,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
     }
   };
 
+  // The same products with the reads issued ahead (PREF): all K fragments of
+  // block kb, then the score MFMAs, the order pinned by a scheduling barrier.
+  auto qk_early = [&](int kb, const char* sb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
+    const char* Kb = sb + (SPLIT && wbr ? C::KBYTES : 0) + kb * 32 * (2 * D) + k_rd;
+    bf16x8 kfr[C::KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) kfr[ks] = *(const bf16x8*)(Kb + (((2 * ks + hi) ^ swk) << 4));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+      s[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks], qf[0][0][ks], ks > 0 ? s[0][0]
+                                                        : C::NEGMU_REGS ? negmu[0][0]
+                                                        : splat16(-mu[0][0]), 0, 0, 0);
+  };
+
   // -inf on the keys of block kb that a row may not see (causal: key > query;
   // full attention: keys past the ragged end), both maps
   auto mask_block = [&](int kt, int kb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
@@ -789,6 +813,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
       }
   };
 
+  // (PREF) the V fragments of block kb, read before the softmax, and the P.V
+  // MFMAs that use them after it
+  auto load_v = [&](int kb, const char* sb, bf16x8 (&vfr)[C::CB][2]) __attribute__((always_inline)) {
+    const char* Vb = sb + C::KT * C::KBYTES;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char* base = Vb + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) + (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
+        vfr[cb][ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+      }
+  };
+  auto pv_early = [&](const bf16x8 (&vfr)[C::CB][2], const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        acc[0][0][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[cb][ks], pk[0][0][ks], acc[0][0][cb], 0, 0, 0);
+  };
+
   if (PD < ntiles) wait_vm_barrier<C::SEGW_MIN * (PD - 1)>();
   else wait_vm_barrier<0>();
   // ---- main loop: tile kt computed while tiles kt+1 .. kt+PD load ------------
@@ -807,11 +853,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
       floatx16 s[C::NBR][NQB];
       bf16x8 pk[C::NBR][NQB][2];
       float bs[C::NBR][NQB];
-      qk(kb, sb, s);
-      if (masked) mask_block(kt, kb, s);
-      expo(s, pk, bs);
-      settle(kt == 0 && kb == 0, s, pk, bs);
-      pv(kb, sb, pk);
+      if constexpr (PREF) {
+        bf16x8 vfr[C::CB][2];
+        qk_early(kb, sb, s);
+        load_v(kb, sb, vfr);
+        __builtin_amdgcn_sched_barrier(0);
+        if (masked) mask_block(kt, kb, s);
+        expo(s, pk, bs);
+        settle(kt == 0 && kb == 0, s, pk, bs);
+        pv_early(vfr, pk);
+      } else {
+        qk(kb, sb, s);
+        if (masked) mask_block(kt, kb, s);
+        expo(s, pk, bs);
+        settle(kt == 0 && kb == 0, s, pk, bs);
+        pv(kb, sb, pk);
+      }
     }
   };
   // unrolled by NSTAGE so that every stage offset is a compile-time constant
