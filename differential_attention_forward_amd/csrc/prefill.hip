@@ -485,6 +485,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // reads take 204 registers and 3-5% off the T = 4096 causal prefill
   // (bit-identical).  Other shapes have no registers to spare.
   constexpr bool PREF = C::NBR * NQB == 1 && D <= 64 && !SHKV && NW == 8;
+  // One-map waves at D = 128 have no registers for that (248-255 in the
+  // two-map-pair shapes): there each fragment read is issued one MFMA ahead
+  // instead (PIPE), into a second 4-register buffer.  Left to itself the
+  // compiler waits on every read at once (lgkmcnt(0) before each of the 24
+  // MFMAs of a block); one read in flight behind each MFMA takes 2.7% off
+  // the D = 128 full prefill and 1.2% off the D = 128 V2 prefill
+  // (bit-identical).
+  constexpr bool PIPE = C::NBR * NQB == 1 && D == 128;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   lds_poison(smem, sizeof(smem));
   lds_poison_done();
@@ -687,6 +695,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
                                                         : splat16(-mu[0][0]), 0, 0, 0);
   };
 
+  // (PIPE) the score product with each K fragment read one MFMA ahead
+  auto qk_pipe = [&](int kb, const char* sb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
+    const char* Kb = sb + (SPLIT && wbr && !SHKV ? C::KBYTES : 0) + kb * 32 * (2 * D) + k_rd;
+    bf16x8 cur = *(const bf16x8*)(Kb + ((hi ^ swk) << 4));
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      bf16x8 nxt;
+      if (ks + 1 < C::KSTEPS) nxt = *(const bf16x8*)(Kb + (((2 * (ks + 1) + hi) ^ swk) << 4));
+      __builtin_amdgcn_sched_barrier(0);
+      s[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[0][0][ks], ks > 0 ? s[0][0]
+                                                        : C::NEGMU_REGS ? negmu[0][0]
+                                                        : splat16(-mu[0][0]), 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < C::KSTEPS) cur = nxt;
+    }
+  };
+
   // -inf on the keys of block kb that a row may not see (causal: key > query;
   // full attention: keys past the ragged end), both maps
   auto mask_block = [&](int kt, int kb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
@@ -827,6 +852,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
         vfr[cb][ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
       }
   };
+  // (PIPE) one V fragment of block kb: 16 keys of output columns 32 cb ..
+  auto vread = [&](int kb, const char* sb, int cb, int ks) __attribute__((always_inline)) {
+    const char* base = sb + C::KT * C::KBYTES + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) +
+                       (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+  };
+  // (PIPE) the P.V product with each V fragment read one MFMA ahead
+  auto pv_pipe = [&](int kb, const char* sb, const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
+    bf16x8 cur = vread(kb, sb, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::CB; ++i) {
+      bf16x8 nxt;
+      if (i + 1 < 2 * C::CB) nxt = vread(kb, sb, (i + 1) / 2, (i + 1) % 2);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[0][0][i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pk[0][0][i % 2], acc[0][0][i / 2], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < 2 * C::CB) cur = nxt;
+    }
+  };
   auto pv_early = [&](const bf16x8 (&vfr)[C::CB][2], const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
@@ -862,6 +908,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
         expo(s, pk, bs);
         settle(kt == 0 && kb == 0, s, pk, bs);
         pv_early(vfr, pk);
+      } else if constexpr (PIPE) {
+        qk_pipe(kb, sb, s);
+        if (masked) mask_block(kt, kb, s);
+        expo(s, pk, bs);
+        settle(kt == 0 && kb == 0, s, pk, bs);
+        pv_pipe(kb, sb, pk);
       } else {
         qk(kb, sb, s);
         if (masked) mask_block(kt, kb, s);
