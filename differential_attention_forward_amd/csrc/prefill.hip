@@ -485,13 +485,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // reads take 204 registers and 3-5% off the T = 4096 causal prefill
   // (bit-identical).  Other shapes have no registers to spare.
   constexpr bool PREF = C::NBR * NQB == 1 && D <= 64 && !SHKV && NW == 8;
-  // One-map waves at D = 128 have no registers for that (248-255 in the
-  // two-map-pair shapes): there each fragment read is issued one MFMA ahead
+  // One-map waves at D = 128 have no registers for that in the split shape
+  // (250-255 used): there each fragment read is issued one MFMA ahead
   // instead (PIPE), into a second 4-register buffer.  Left to itself the
   // compiler waits on every read at once (lgkmcnt(0) before each of the 24
   // MFMAs of a block); one read in flight behind each MFMA takes 2.7% off
   // the D = 128 full prefill and 1.2% off the D = 128 V2 prefill
-  // (bit-identical).
+  // (bit-identical).  The V2 form has the registers for all of a block's K
+  // reads up front (176 used) but gains nothing more from them.
   constexpr bool PIPE = C::NBR * NQB == 1 && D == 128;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   lds_poison(smem, sizeof(smem));
