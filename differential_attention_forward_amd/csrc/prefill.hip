@@ -820,17 +820,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
       for (int qb = 0; qb < NQB; ++qb) lsum[br][qb] += bsum[br][qb];
   };
 
+  // One V fragment of block kb (A operand of the P.V product): keys
+  // 16 ks .. 16 ks + 15 of output columns 32 cb .. 32 cb + 31, read with two
+  // transposing LDS reads from the row-major V tile
+  auto vread = [&](int kb, const char* sb, int cb, int ks) __attribute__((always_inline)) {
+    const char* base = sb + C::KT * C::KBYTES + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) +
+                       (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
+    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+  };
   // acc += P^T-weighted V rows of block kb; each V fragment serves both maps
   auto pv = [&](int kb, const char* sb, const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
-    const char* Vb = sb + C::KT * C::KBYTES;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const char* base = Vb + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) + (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
-        const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        const bf16x8 av = vread(kb, sb, cb, ks);
 #pragma unroll
         for (int br = 0; br < C::NBR; ++br)
 #pragma unroll
@@ -842,24 +848,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // (PREF) the V fragments of block kb, read before the softmax, and the P.V
   // MFMAs that use them after it
   auto load_v = [&](int kb, const char* sb, bf16x8 (&vfr)[C::CB][2]) __attribute__((always_inline)) {
-    const char* Vb = sb + C::KT * C::KBYTES;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const char* base = Vb + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) + (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
-        vfr[cb][ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-      }
-  };
-  // (PIPE) one V fragment of block kb: 16 keys of output columns 32 cb ..
-  auto vread = [&](int kb, const char* sb, int cb, int ks) __attribute__((always_inline)) {
-    const char* base = sb + C::KT * C::KBYTES + (kb * 32 + 16 * ks + v_row) * (2 * C::DV) +
-                       (((4 * cb + v_chunk) ^ v_sw) << 4) + v_byte;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)base);
-    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * (2 * C::DV)));
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+      for (int ks = 0; ks < 2; ++ks) vfr[cb][ks] = vread(kb, sb, cb, ks);
   };
   // (PIPE) the P.V product with each V fragment read one MFMA ahead
   auto pv_pipe = [&](int kb, const char* sb, const bf16x8 (&pk)[C::NBR][NQB][2]) __attribute__((always_inline)) {
