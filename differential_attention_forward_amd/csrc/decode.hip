@@ -535,7 +535,9 @@ void decode_v2_mma_kernel(DecodeArgs a) {
       for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
       m = swap_halves_max(m);
       const float delta = started ? fmaxf(m, 0.0f) : m;  // the first block always has a visible key
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      // the first block finds the state empty: no scaling (2^-delta could
+      // overflow for a block max far below zero, and 0 x inf is NaN)
+      const float alpha = started ? __builtin_amdgcn_exp2f(-delta) : 1.0f;
       mu += delta;
       lsum *= alpha;
 #pragma unroll

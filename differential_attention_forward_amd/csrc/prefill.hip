@@ -799,7 +799,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
           const bool had = WIN ? seen[br][qb] : !first;
           if constexpr (WIN) seen[br][qb] = had || m != kNegInf;
           const float delta = had ? fmaxf(m, 0.0f) : (m == kNegInf ? 0.0f : m);
-          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          // before the row's first visible key its state is empty (nothing to
+          // scale): 2^-delta could overflow there (delta = the block max, which
+          // may lie far below zero) and 0 x inf would be NaN; afterwards
+          // delta >= 0 and the factor is at most 1
+          const float alpha = had ? __builtin_amdgcn_exp2f(-delta) : 1.0f;
           mu[br][qb] += delta;
           lsum[br][qb] *= alpha;
 #pragma unroll
@@ -1289,7 +1293,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 1; r < 16; ++r) m = fmaxf(m, s[br][r]);
         m = swap_halves_max(m);
         const float delta = first ? (m == kNegInf ? 0.0f : m) : fmaxf(m, 0.0f);
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        // the first block finds the state empty: no scaling (2^-delta could
+        // overflow for a block max far below zero, and 0 x inf is NaN)
+        const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-delta);
         mu[br] += delta;
         lsum[br] *= alpha;
 #pragma unroll

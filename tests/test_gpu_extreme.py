@@ -1,0 +1,185 @@
+"""Parity on rows whose scores are all far below zero.
+
+Queries and keys are drawn as c u + 0.2 z and -c u + 0.2 z' (u a fixed unit
+vector, z, z' standard normal), so every score q.k / sqrt(D) sits near
+-c^2 / sqrt(D) with a spread of a few units: around -300 in the base-2 units
+the kernels work in.  Softmax is invariant to a shift shared by a row
+(paperleet "Differential Transformer Attention": each map is a row softmax),
+so the maps, and the output, are those of ordinary scores; the float64 oracle
+computes them exactly.  A kernel that scaled its running state by 2^(-m) with
+the row's first block maximum m would overflow here (2^300 is beyond fp32)
+and turn the empty accumulators into NaN."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import differential_attention_forward_amd as da
+import oracle
+from workloads import decode_inputs, prefill_inputs, v2_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+SCORE = 300.0  # target |score| in base-2 units
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _shift(q, k, D, dtype):
+    """q, k (any leading shape, last dim D) moved to scores near -SCORE."""
+    c = math.sqrt(SCORE * math.sqrt(D) / math.log2(math.e))
+    u = torch.ones(D, dtype=torch.float32) / math.sqrt(D)
+    qs = (c * u + 0.2 * q.float())
+    ks = (-c * u + 0.2 * k.float())
+    td = {"fp32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    return qs.to(td), ks.to(td)
+
+
+def _extreme_prefill(B, H, T, D, dtype, seed):
+    x = prefill_inputs(B, H, T, D, dtype, seed=seed)
+    x["q1"], x["k1"] = _shift(x["q1"], x["k1"], D, dtype)
+    x["q2"], x["k2"] = _shift(x["q2"], x["k2"], D, dtype)
+    return x
+
+
+def _err(gpu, ref):
+    g = gpu.double().cpu().numpy()
+    assert np.isfinite(g).all(), "non-finite output"
+    return float(np.max(np.abs(g - ref)))
+
+
+def _dev(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+@pytest.mark.parametrize("dtype,D,causal,headnorm", [
+    ("bf16", 64, True, True),     # one-map waves, early fragment reads
+    ("bf16", 64, True, False),
+    ("bf16", 64, False, True),    # 64-row waves
+    ("bf16", 32, True, True),     # two maps per wave
+    ("bf16", 128, False, True),   # D = 128, reads one MFMA ahead
+    ("fp32", 64, True, True),
+])
+def test_prefill_very_negative_scores(dtype, D, causal, headnorm):
+    x = _extreme_prefill(1, 2, 300, D, dtype, seed=7300 + D)
+    lam = torch.tensor([0.3, 1.2], dtype=torch.float32)
+    say(f"extreme prefill {dtype} D={D} causal={causal} headnorm={headnorm}")
+    xd = _dev(x)
+    out = da.diffattn_fwd(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV), causal=causal,
+                          headnorm=headnorm, lambda_init=0.8, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam.numpy(), causal)
+    if headnorm:
+        ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+    err = _err(out, ref)
+    say(f"  max err {err:.3e}")
+    assert err <= TOL[dtype], err
+
+
+def test_long_causal_rows_very_negative_scores():
+    # T > 4096: the ping-pong kernel; sampled rows against the oracle
+    T = 4097
+    x = _extreme_prefill(1, 2, T, 64, "bf16", seed=7310)
+    lam = torch.tensor([0.5, -0.2], dtype=torch.float32)
+    say("extreme prefill, ping-pong kernel, T=4097")
+    xd = _dev(x)
+    out = da.diffattn_fwd(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(T - 40, T),
+                                     np.random.default_rng(7310).choice(T, 100, replace=False)]))
+    for h in range(2):
+        ref = oracle.diff_attention_rows(x["q1"][0, h], x["k1"][0, h], x["q2"][0, h], x["k2"][0, h],
+                                         x["v"][0, h], float(lam[h]), True, rows)
+        err = _err(out[0, h, rows], ref)
+        say(f"  h={h} max err {err:.3e}")
+        assert err <= TOL["bf16"], (h, err)
+
+
+def test_window_and_attention_very_negative_scores():
+    x = _extreme_prefill(1, 2, 1000, 64, "bf16", seed=7320)
+    lam = torch.tensor([0.6, 0.9], dtype=torch.float32)
+    xd = _dev(x)
+    say("extreme window prefill, W=256")
+    out = da.diffattn_fwd_window(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV), 256,
+                                 headnorm=True, lambda_init=0.8, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.head_rmsnorm(
+        oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam.numpy(), True, window=256),
+        0.8, 1e-5)
+    err = _err(out, ref)
+    say(f"  max err {err:.3e}")
+    assert err <= TOL["bf16"], err
+    for D in (64, 128):
+        say(f"extreme standard attention D={D}")
+        y = _extreme_prefill(1, 2, 300, D, "bf16", seed=7330 + D)
+        # values of the usual scale (the shifted queries are ~5 in size)
+        v = y["v"][..., :D].contiguous()
+        yd = _dev(y)
+        out = da.diffattn_attention_fwd(yd["q1"], yd["k1"], v.to(DEV), causal=True)
+        torch.cuda.synchronize()
+        err = _err(out, oracle.attention(y["q1"], y["k1"], v, True))
+        say(f"  max err {err:.3e}")
+        assert err <= TOL["bf16"], (D, err)
+
+
+def test_training_forward_very_negative_scores():
+    x = _extreme_prefill(1, 2, 300, 64, "bf16", seed=7340)
+    lam = torch.tensor([0.4, 1.1], dtype=torch.float32)
+    xd = _dev(x)
+    say("extreme training forward")
+    out, saved = da.diffattn_fwd_train(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV),
+                                       causal=True, headnorm=True, lambda_init=0.8, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.head_rmsnorm(
+        oracle.diff_attention(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam.numpy(), True), 0.8, 1e-5)
+    err = _err(out, ref)
+    say(f"  max err {err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_very_negative_scores(dtype):
+    B, H, L, D = 2, 3, 3000, 64
+    x = decode_inputs(B, H, L, D, dtype, seed=7350)
+    x["q1"], x["k1"] = _shift(x["q1"], x["k1"], D, dtype)
+    x["q2"], x["k2"] = _shift(x["q2"], x["k2"], D, dtype)
+    lam = torch.tensor([0.2, 0.7, 1.3], dtype=torch.float32)
+    xd = _dev(x)
+    say(f"extreme decode {dtype}")
+    out = da.diffattn_decode(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV), num_splits=7)
+    torch.cuda.synchronize()
+    err = _err(out, oracle.diff_attention_decode(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam.numpy()))
+    say(f"  max err {err:.3e}")
+    assert err <= TOL[dtype], err
+
+
+def test_v2_very_negative_scores():
+    D = 128
+    x = v2_inputs(1, 8, 2, 300, D, "bf16", seed=7360, lam_uniform=(0.2, 0.8))
+    x["q1"], k = _shift(x["q1"], x["k"], D, "bf16")
+    x["q2"], _ = _shift(x["q2"], x["k"], D, "bf16")
+    x["k"] = k
+    xd = _dev(x)
+    say("extreme V2 prefill")
+    out = da.diffattn_v2_fwd(xd["q1"], xd["q2"], xd["k"], xd["v"], xd["lam"], causal=True)
+    torch.cuda.synchronize()
+    err = _err(out, oracle.diff_attention_v2(x["q1"], x["q2"], x["k"], x["v"], x["lam"].numpy(), True))
+    say(f"  max err {err:.3e}")
+    assert err <= TOL["bf16"], err
+    y = v2_inputs(2, 8, 2, 3000, D, "bf16", seed=7361, decode=True, lam_uniform=(0.2, 0.8))
+    y["q1"], k = _shift(y["q1"], y["k"], D, "bf16")
+    y["q2"], _ = _shift(y["q2"], y["k"], D, "bf16")
+    y["k"] = k
+    yd = _dev(y)
+    say("extreme V2 decode")
+    out = da.diffattn_v2_decode(yd["q1"], yd["q2"], yd["k"], yd["v"], yd["lam"])
+    torch.cuda.synchronize()
+    err = _err(out, oracle.diff_attention_v2_decode(y["q1"], y["q2"], y["k"], y["v"], y["lam"].numpy()))
+    say(f"  max err {err:.3e}")
+    assert err <= TOL["bf16"], err
