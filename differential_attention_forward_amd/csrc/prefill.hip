@@ -1638,9 +1638,9 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
       case 64: {
         // Every row sees up to `window` keys, so workgroups carry nearly equal
         // work: with enough 256-row workgroups to fill the chip twice, both
-        // maps per wave (each V fragment feeds two P.V products) win, 6.7%
-        // at T = 32768, W = 4096, 16 heads; with few, the finer one-map
-        // 128-row workgroups.
+        // maps per wave (each V fragment feeds two P.V products) win, 1.1%
+        // at T = 32768, W = 4096, 16 heads over the one-map shape with its
+        // early reads; with few, the finer one-map 128-row workgroups.
         const long wg256 = (long)a.B * a.H * ((a.T + 255) / 256);
         if (wg256 >= 2 * compute_units()) return launch_window<64, 1, 8, 3, false>(a, headnorm, stream);
         return launch_window<64, 1, 8, 3, true>(a, headnorm, stream);
