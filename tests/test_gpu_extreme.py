@@ -202,3 +202,31 @@ def test_v2_extreme_scores(sign):
     err = _err(out, oracle.diff_attention_v2_decode(y["q1"], y["q2"], y["k"], y["v"], y["lam"].numpy()))
     say(f"  max err {err:.3e}")
     assert err <= TOL["bf16"], err
+
+
+def test_backward_extreme_scores(sign):
+    # The backward forms probabilities from the saved log-sum-exp.  K's large
+    # shared component (|c u| ~ 41) multiplies the bf16 rounding of dS, whose
+    # rows cancel only in exact arithmetic, so dQ is held to the backward
+    # tests' derived first-order rounding bound (tests/bwd_rounding.py),
+    # which needs short sequences: T = 4 (the second half, rows 2 and 3,
+    # carrying the positive side's step).
+    from tests import bwd_rounding
+    from tests.test_gpu_backward import check_grads, dlambda_term_rss
+    from workloads import grad_output
+    T = 4
+    x = _extreme_prefill(1, 2, T, 64, "bf16", seed=7370, sign=sign)
+    lam = torch.tensor([0.4, 1.1], dtype=torch.float32)
+    dout = grad_output((1, 2, T, 128), seed=7371)
+    xd = _dev(x)
+    say(f"extreme backward sign={sign:+.0f}")
+    out, saved = da.diffattn_fwd_train(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV),
+                                       causal=True, headnorm=True, lambda_init=0.8, eps=1e-5)
+    g = da.diffattn_bwd(xd["q1"], xd["k1"], xd["q2"], xd["k2"], xd["v"], lam.to(DEV), dout.to(DEV), saved,
+                        causal=True, headnorm=True, lambda_init=0.8, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.diff_attention_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam.numpy(), dout,
+                                         True, True, 0.8, 1e-5)
+    rss = dlambda_term_rss(x, lam.numpy(), dout, True, True, 0.8, 1e-5)
+    bound = bwd_rounding.first_order_bound(x, lam.numpy(), dout, True, True, 0.8, 1e-5)
+    check_grads(g, ref, f"  extreme T={T} sign={sign:+.0f}", rss, bound)
