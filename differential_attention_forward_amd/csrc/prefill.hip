@@ -31,9 +31,9 @@
 //
 // bf16 (fwd_bf16_kernel): K1, K2, V tiles of 64 keys go global -> LDS
 // directly (asynchronous DMA, NSTAGE-deep ring), v_mfma_f32_32x32x16_bf16,
-// probabilities rounded to bf16 for the P.V product and summed as rounded.
-// fp32 (fwd_f32_kernel): tiles of 32 keys staged global -> VGPR -> LDS,
-// double buffered, v_mfma_f32_32x32x2_f32, fp32 probabilities.
+// probabilities rounded to bf16 for the P.V product.
+// fp32 (fwd_f32_kernel): tiles of 32 to 128 keys staged global -> VGPR ->
+// LDS, double buffered, v_mfma_f32_32x32x2_f32, fp32 probabilities.
 #include "common.h"
 #include "kernels.h"
 
@@ -1672,9 +1672,17 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
       case 128: return launch_bf16<128, 1, 8, 2, true>(a, causal, headnorm, stream);
     }
   } else {  // fp32
+    // Eight waves (two per SIMD) wherever their registers fit in 256: with
+    // one wave per SIMD nothing hides a wave's LDS reads and softmax behind
+    // another wave's MFMAs.  One map per wave except for D = 32 full
+    // attention, whose 256-row two-map workgroups carry equal work and read
+    // each K/V tile once for both maps; D = 128 needs one wave per SIMD
+    // (its accumulators and Q fragments alone take 192 registers).
     switch (D) {
-      case 32: return launch_f32<32, 1, 4, 32, false>(a, causal, headnorm, stream);
-      case 64: return launch_f32<64, 1, 4, 32, false>(a, causal, headnorm, stream);
+      case 32:
+        if (causal) return launch_f32<32, 1, 8, 128, true>(a, causal, headnorm, stream);
+        return launch_f32<32, 1, 8, 64, false>(a, causal, headnorm, stream);
+      case 64: return launch_f32<64, 1, 8, 64, true>(a, causal, headnorm, stream);
       case 128: return launch_f32<128, 1, 4, 32, true>(a, causal, headnorm, stream);
     }
   }
