@@ -117,6 +117,32 @@ def test_fwd_causal_many_heads(headnorm):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("headnorm", [False, True])
+def test_fwd_d32_long_causal_rows(headnorm):
+    # D=32 causal rows beyond 2048 keys run one map per wave: 128-row
+    # workgroups for few heads, 192-row ones once 128-row workgroups would
+    # exceed four per compute unit (B2 H32 T2100: 1088); shorter rows keep
+    # both maps per wave (the sweep above).  Sampled heads and rows, full
+    # key range, ragged against both row counts.
+    rng = np.random.default_rng(47)
+    for B, H, T, seed, pairs in ((1, 2, 2049, 45, ((0, 0), (0, 1))), (1, 2, 3001, 46, ((0, 0), (0, 1))),
+                                 (2, 32, 2100, 47, ((0, 0), (1, 17), (1, 31)))):
+        x = prefill_inputs(B, H, T, 32, "bf16", seed=seed, device=DEV)
+        lam = torch.linspace(-0.3, 1.1, H, dtype=torch.float32, device=DEV)
+        say(f"fwd bf16 D=32 B={B} H={H} T={T} causal headnorm={headnorm}")
+        out = run_fwd(x, lam, True, headnorm)
+        for b, h in pairs:
+            rows = np.unique(np.concatenate([np.arange(32), np.arange(T - 32, T), rng.choice(T, 96, replace=False)]))
+            sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
+            ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], float(lam[h]), True,
+                                             rows)
+            if headnorm:
+                ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+            assert maxerr(out[b, h, rows], ref) <= TOL["bf16"], (T, b, h)
+        del x, out
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("D", [64, 128])
 def test_standard_attention(D, causal):
