@@ -1614,8 +1614,18 @@ long compute_units() {
 
 hipError_t launch_v2(const FwdArgs& a, int D, bool causal, hipStream_t stream) {
   switch (D) {
-    // both maps per wave: K and V fragments each serve two MFMAs
-    case 64: return launch_v2_d<64, 1, 8, 3, false>(a, causal, stream);
+    case 64:
+      // Short causal rows: one map per wave, with the first version's rule
+      // for 128- or 192-row workgroups (B2 H16 T4096: 0.223 -> 0.164 ms;
+      // B4 H32 T1024: 0.076 -> 0.068 ms).  Otherwise both maps per wave: K
+      // and V fragments each serve two MFMAs.
+      if (causal && a.T <= 4096) {
+        const long wg128 = (long)a.B * a.H * ((a.T + 127) / 128);
+        const long cus = compute_units();
+        if (wg128 <= cus || (a.T > 2048 && wg128 <= 4 * cus)) return launch_v2_d<64, 1, 8, 3, true>(a, causal, stream);
+        return launch_v2_d<64, 1, 12, 3, true>(a, causal, stream);
+      }
+      return launch_v2_d<64, 1, 8, 3, false>(a, causal, stream);
     // one map per wave (registers: the accumulators alone take 64 VGPRs per map)
     case 128: return launch_v2_d<128, 1, 8, 3, true>(a, causal, stream);
   }

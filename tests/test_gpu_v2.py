@@ -52,6 +52,31 @@ def test_v2_fwd_sweep(D, causal):
             assert err <= TOL, (H, Hkv, T, err)
 
 
+def test_v2_fwd_d64_causal_shapes():
+    # D=64 causal rows up to 4096 keys run one map per wave: 128-row
+    # workgroups for few heads (B1 H4 T2500), 192-row ones once 128-row
+    # workgroups exceed one per compute unit at T <= 2048 (B2 H32 T1100: 576).
+    # Sampled query heads and rows, full key range, ragged row counts.
+    rng = np.random.default_rng(53)
+    for B, H, Hkv, T, seed, pairs in ((1, 4, 2, 2500, 51, ((0, 0), (0, 3))),
+                                      (2, 32, 8, 1100, 52, ((0, 0), (1, 9), (1, 31)))):
+        x = v2_inputs(B, H, Hkv, T, 64, "bf16", seed=seed, device=DEV)
+        lam = torch.linspace(-0.3, 1.2, H, device=DEV)
+        say(f"v2 fwd D=64 B={B} H={H} Hkv={Hkv} T={T} causal")
+        out = da.diffattn_v2_fwd(x["q1"], x["q2"], x["k"], x["v"], lam, causal=True)
+        torch.cuda.synchronize()
+        grp = H // Hkv
+        for b, p in pairs:
+            rows = np.unique(np.concatenate([np.arange(32), np.arange(T - 32, T), rng.choice(T, 96, replace=False)]))
+            g = p // grp
+            k, v = x["k"][b, g].cpu(), x["v"][b, g].cpu()
+            ref = oracle.diff_attention_rows(x["q1"][b, p].cpu(), k, x["q2"][b, p].cpu(), k, v, float(lam[p]),
+                                             True, rows)
+            assert maxerr(out[b, p, rows], ref) <= TOL, (T, b, p)
+        del x, out
+        torch.cuda.empty_cache()
+
+
 def test_v2_identical_maps_cancel():
     # q1 = q2 and lambda = 1: both maps are the same, the output is exactly 0
     x = v2_inputs(1, 4, 2, 200, 64, "bf16", seed=77)
