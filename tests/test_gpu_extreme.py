@@ -80,7 +80,7 @@ def _dev(x):
 @pytest.mark.parametrize("dtype,D,causal,headnorm", [
     ("bf16", 64, True, True),     # one-map waves, early fragment reads
     ("bf16", 64, True, False),
-    ("bf16", 64, False, True),    # 64-row waves
+    ("bf16", 64, False, True),    # full attention, two maps per wave
     ("bf16", 32, True, True),     # two maps per wave
     ("bf16", 128, False, True),   # D = 128, reads one MFMA ahead
     ("fp32", 64, True, True),

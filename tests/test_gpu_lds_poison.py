@@ -8,8 +8,8 @@ first (a missing wait or barrier, a stray index) would pick up NaN or another
 value there and change its output; one that does not is bit-identical, since
 the poison adds only the fill and a barrier at entry.  The cases cover each
 launch shape: split and non-split prefill, the ping-pong kernel, the
-three-waves-per-SIMD split, full attention with 64-row waves, D = 32 / 128,
-fp32, sliding window, standard attention, DIFF V2 prefill and decode, decode,
+three-waves-per-SIMD split, full attention, D = 32 / 128, the fp32 shapes,
+sliding window, standard attention, DIFF V2 prefill and decode, decode,
 ragged decode, the allocation-free decode, the training forward and the
 backward."""
 
@@ -79,10 +79,14 @@ PREFILL = [
     (1, 2, 300, 64, "bf16", True, True),     # split, 8 waves
     (1, 2, 4500, 64, "bf16", True, False),   # ping-pong kernel
     (4, 16, 2048, 64, "bf16", True, True),   # split, 12 waves
-    (1, 2, 300, 64, "bf16", False, True),    # full: split, 64-row waves
+    (1, 2, 300, 64, "bf16", False, True),    # full: non-split
     (1, 2, 300, 128, "bf16", False, True),   # D = 128 split
     (1, 2, 300, 32, "bf16", True, False),    # D = 32 non-split
-    (1, 2, 200, 64, "fp32", True, True),     # fp32
+    (1, 2, 2100, 32, "bf16", True, True),    # D = 32 causal beyond 2048 keys: split
+    (1, 2, 200, 64, "fp32", True, True),     # fp32: one map per wave, 64-key tiles
+    (1, 2, 300, 32, "fp32", True, False),    # fp32 D = 32 causal: 128-key tiles
+    (1, 2, 300, 32, "fp32", False, True),    # fp32 D = 32 full: both maps per wave
+    (1, 2, 200, 128, "fp32", False, False),  # fp32 D = 128: four waves
 ]
 
 
@@ -109,9 +113,11 @@ def test_window_attention_v2_poisoned_same_bits(libs):
         a, b = run_both(libs, lambda: da.diffattn_attention_fwd(y["q1"], y["k1"], y["q1"], causal=True))
         assert_same(a, b, f"attention D={D}")
     say("poison V2 prefill and decode")
-    v2 = dev(v2_inputs(1, 8, 2, 500, 128, "bf16", seed=5103, lam_uniform=(0.2, 0.8)))
-    a, b = run_both(libs, lambda: da.diffattn_v2_fwd(v2["q1"], v2["q2"], v2["k"], v2["v"], v2["lam"], causal=True))
-    assert_same(a, b, "v2 prefill")
+    for D, causal in ((128, True), (64, True), (64, False)):
+        v2 = dev(v2_inputs(1, 8, 2, 500, D, "bf16", seed=5103 + D, lam_uniform=(0.2, 0.8)))
+        a, b = run_both(libs, lambda: da.diffattn_v2_fwd(v2["q1"], v2["q2"], v2["k"], v2["v"], v2["lam"],
+                                                         causal=causal))
+        assert_same(a, b, f"v2 prefill D={D} causal={causal}")
     v2d = dev(v2_inputs(2, 8, 2, 3000, 128, "bf16", seed=5104, decode=True, lam_uniform=(0.2, 0.8)))
     a, b = run_both(libs, lambda: da.diffattn_v2_decode(v2d["q1"], v2d["q2"], v2d["k"], v2d["v"], v2d["lam"]))
     assert_same(a, b, "v2 decode")
