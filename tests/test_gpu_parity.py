@@ -550,18 +550,21 @@ def test_fwd_window_long_rows():
                 assert maxerr(out[b, h, rows], ref) <= TOL["bf16"], (T, W, b, h)
 
 
-def test_fwd_window_many_heads():
-    # enough 256-row workgroups (4 x 32 x 4 = 512) for the two-maps-per-wave
-    # window configuration: whole heads against the oracle, a ragged T
-    B, H, T, W = 4, 32, 1000, 300
-    x = prefill_inputs(B, H, T, 64, "bf16", seed=43)
+@pytest.mark.parametrize("D,H", [(64, 32), (32, 64)])
+def test_fwd_window_many_heads(D, H):
+    # D=64: enough 256-row workgroups (4 x 32 x 4 = 512) for the
+    # two-maps-per-wave window configuration; D=32: enough 192-row ones
+    # (4 x 64 x 6 = 1536) for one map per wave at three waves per SIMD.
+    # Whole heads against the oracle, a ragged T
+    B, T, W = 4, 1000, 300
+    x = prefill_inputs(B, H, T, D, "bf16", seed=43 + D)
     lam = torch.linspace(-0.2, 1.2, H)
-    say(f"fwd window bf16 D=64 B={B} H={H} T={T} W={W}")
+    say(f"fwd window bf16 D={D} B={B} H={H} T={T} W={W}")
     for headnorm in (False, True):
         out = da.diffattn_fwd_window(*(to_dev(x)[k] for k in ("q1", "k1", "q2", "k2", "v")), lam.to(DEV), W,
                                      headnorm=headnorm, lambda_init=0.8, eps=1e-5)
         torch.cuda.synchronize()
-        for (b, h) in ((0, 0), (1, 17), (3, 31)):
+        for (b, h) in ((0, 0), (1, 17), (3, H - 1)):
             ref = oracle.diff_attention_rows(x["q1"][b, h], x["k1"][b, h], x["q2"][b, h], x["k2"][b, h],
                                              x["v"][b, h], float(lam[h]), True, np.arange(T), window=W)
             if headnorm:
