@@ -538,11 +538,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   const bool wave_active = q0 < T;
   const int k_end = CAUSAL ? min(T, q_tile0 + C::BR) : T;
   // sliding window (causal only): row i sees keys i - W < j <= i.  Key tiles
-  // below the workgroup's first row's window are never loaded; kt below
-  // counts tiles from kt0.
+  // below the workgroup's first row's window are never loaded: the
+  // workgroup's tiles are kt0 .. kt0 + ntiles - 1, and the loop's step kt
+  // names one of them through ptile.
   const int W = CAUSAL && WIN ? a.window : 0;
   const int kt0 = W > 0 ? max(0, q_tile0 - W + 1) / BC : 0;
   const int ntiles = (k_end + BC - 1) / BC - kt0;
+  // With a window, step kt visits tile kt0 + ((kt - kt0) mod ntiles): the
+  // workgroups of consecutive query tiles, which run side by side on one XCD,
+  // then read the same key tile at the same step (their windows overlap in
+  // all but a few tiles), so each tile is fetched into that XCD's L2 about
+  // once rather than once per workgroup (T = 32768, W = 4096: 1.50 -> 0.51 GB
+  // fetched per launch, 2% less time).  The online softmax takes the tiles
+  // in any order.  Without a window kt0 = 0 and the order is the natural one.
+  const int krot = W > 0 ? (ntiles - kt0 % ntiles) % ntiles : 0;
+  auto ptile = [&](int kt) __attribute__((always_inline)) {
+    const int r = kt + krot;
+    return kt0 + (r >= ntiles ? r - ntiles : r);
+  };
   const float sc = a.score_scale;
   float lamv = 0.0f;
   if constexpr (MAPS == 2) {
@@ -559,7 +572,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   constexpr int CK = D / 8, RK = 64 / CK, CV = C::DV / 8, RV = 64 / CV;
   const int rl_k = lane / CK, rl_v = lane / CV;
   auto issue_rt = [&](int kt, char* sb) __attribute__((always_inline)) {
-    const int key0 = (kt0 + kt) * BC;
+    const int key0 = ptile(kt) * BC;
 #pragma unroll
     for (int i = 0; i < C::SEGW; ++i) {
       const int seg = wave + i * NW;
@@ -656,7 +669,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // A 32-key block kb of tile kt takes part only if it holds a key this wave
   // may attend to.
   auto kb_live = [&](int kt, int kb) __attribute__((always_inline)) {
-    const int key0 = (kt0 + kt) * BC + kb * 32;
+    const int key0 = ptile(kt) * BC + kb * 32;
     return key0 < T && (!CAUSAL || key0 <= q_last) && (W == 0 || key0 + 31 > q0 - W);
   };
 
@@ -716,7 +729,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // -inf on the keys of block kb that a row may not see (causal: key > query;
   // full attention: keys past the ragged end), both maps
   auto mask_block = [&](int kt, int kb, floatx16 (&s)[C::NBR][NQB]) __attribute__((always_inline)) {
-    const int key0 = (kt0 + kt) * BC + kb * 32;
+    const int key0 = ptile(kt) * BC + kb * 32;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int query = q0 + qb * 32 + l32;
@@ -884,7 +897,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {
     // whether any block of this tile crosses the causal diagonal (or the
     // ragged end) for this wave's rows
-    const int tk0 = (kt0 + kt) * BC;
+    const int tk0 = ptile(kt) * BC;
     const bool masked = CAUSAL ? (tk0 + BC - 1 > q0 || (W > 0 && tk0 <= q_last - W)) : (tk0 + BC > T);
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
