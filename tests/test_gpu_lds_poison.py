@@ -114,10 +114,10 @@ def test_window_attention_v2_poisoned_same_bits(libs):
                                                          headnorm=False))
     assert_same(a, b, "window D=32")
     say("poison standard attention")
-    for D in (64, 128):
+    for D, causal in ((64, True), (128, True), (128, False)):
         y = dev(prefill_inputs(1, 2, 300, D, "bf16", seed=5102 + D))
-        a, b = run_both(libs, lambda: da.diffattn_attention_fwd(y["q1"], y["k1"], y["q1"], causal=True))
-        assert_same(a, b, f"attention D={D}")
+        a, b = run_both(libs, lambda: da.diffattn_attention_fwd(y["q1"], y["k1"], y["q1"], causal=causal))
+        assert_same(a, b, f"attention D={D} causal={causal}")
     say("poison V2 prefill and decode")
     for D, causal in ((128, True), (64, True), (64, False)):
         v2 = dev(v2_inputs(1, 8, 2, 500, D, "bf16", seed=5103 + D, lam_uniform=(0.2, 0.8)))

@@ -159,6 +159,17 @@ def test_standard_attention(D, causal):
     say(f"  worst {worst:.3e}")
 
 
+def test_standard_attention_long_causal_rows():
+    # head width 128, causal rows beyond 4096 keys: 256-row workgroups
+    # (shorter rows take 128-row ones, as in the test above)
+    T = 4500
+    x = attention_inputs(1, 2, T, 128, seed=931)
+    say(f"attention bf16 D=128 T={T} causal")
+    out = da.diffattn_attention_fwd(*(x[k].to(DEV) for k in ("q", "k", "v")), causal=True)
+    torch.cuda.synchronize()
+    assert maxerr(out, oracle.attention(x["q"], x["k"], x["v"], True)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_lambda_range(dtype):
     # lambda is not clamped: negative and > 1 values included
