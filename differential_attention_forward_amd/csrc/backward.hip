@@ -541,11 +541,18 @@ __device__ __forceinline__ void kv_body(const BwdArgs& a, char* smem, int w) {
   }
 }
 
+// Waves per SIMD the kv and q kernels are compiled for (the register budget
+// follows): D = 128 holds 128 accumulators and 128 fragment registers per
+// wave, one wave; D = 64 two; D = 32 fits three in 168 registers, which at
+// B2 H16 T4096 full attention takes 3.7% and at B4 H32 T1024 causal 10.5%
+// off the backward (bit-identical).
+constexpr int bwd_waves(int D) { return D >= 128 ? 1 : D <= 32 ? 3 : 2; }
+
 // dK and dV workgroups side by side: the key block w of head bh becomes
 // workgroups 2w (dK1, dK2) and 2w + 1 (dV), on the same XCD (they stage the
 // same query tiles).
 template <int D, int NW, int NSTAGE, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2))) void bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(bwd_waves(D), bwd_waves(D)))) void bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[CfgKV<D, NW, NSTAGE>::SMEM];
   lds_poison(smem, sizeof(smem));
   lds_poison_done();
@@ -579,7 +586,7 @@ struct CfgQ {
 };
 
 template <int D, int NW, int NSTAGE, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2))) void bwd_q_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(bwd_waves(D), bwd_waves(D)))) void bwd_q_kernel(BwdArgs a) {
   using C = CfgQ<D, NW, NSTAGE>;
   constexpr int BC = C::BC;
   constexpr int DV = C::DV;
@@ -806,11 +813,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 12
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(const BwdArgs& a, bool headnorm, hipStream_t stream) {
   // Four-wave workgroups with two LDS stages: two kv or q workgroups per CU
-  // (the q pass takes 16% less time than with one eight-wave workgroup at
-  // D = 64).  D = 128: a q wave holds 128 accumulators and 128 fragment
-  // registers, one wave per SIMD; LDS stages of 64-65 KiB.
+  // at D = 64 (the q pass takes 16% less time than with one eight-wave
+  // workgroup), three at D = 32 (bwd_waves).  D = 128: a q wave holds 128
+  // accumulators and 128 fragment registers, one wave per SIMD; LDS stages
+  // of 64-65 KiB.
   constexpr int KNW = 4, QNW = 4;
-  constexpr int KST = 2;  // two stages: two kv workgroups per CU
+  constexpr int KST = 2;  // two stages: two (D = 32: three) kv workgroups per CU
   constexpr int QST = 2;
   const long long bh = (long long)a.B * a.H;
   const long long gp = (long long)a.nchunk * bh;
