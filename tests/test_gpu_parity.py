@@ -159,6 +159,31 @@ def test_standard_attention(D, causal):
     say(f"  worst {worst:.3e}")
 
 
+def test_fwd_fp32_many_heads():
+    # fp32 launch shapes over many workgroups (XCD remap, heaviest-first
+    # order, ragged last tiles): D=64 one map per wave on 64-key tiles, D=32
+    # causal one map per wave on 128-key tiles, D=32 full both maps per wave,
+    # D=128 four waves.  Sampled heads and rows, full key range
+    rng = np.random.default_rng(61)
+    for B, H, T, D, causal, headnorm, seed in ((2, 16, 2500, 64, True, True, 62), (1, 12, 3001, 32, True, False, 63),
+                                               (1, 8, 3000, 32, False, True, 64),
+                                               (1, 8, 1100, 128, False, False, 65)):
+        x = prefill_inputs(B, H, T, D, "fp32", seed=seed, device=DEV)
+        lam = torch.linspace(-0.4, 1.3, H, dtype=torch.float32, device=DEV)
+        say(f"fwd fp32 D={D} B={B} H={H} T={T} causal={causal} headnorm={headnorm}")
+        out = run_fwd(x, lam, causal, headnorm)
+        for b, h in ((0, 0), (B - 1, H // 2), (B - 1, H - 1)):
+            rows = np.unique(np.concatenate([np.arange(16), np.arange(T - 16, T), rng.choice(T, 48, replace=False)]))
+            sl = {k: x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")}
+            ref = oracle.diff_attention_rows(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], float(lam[h]), causal,
+                                             rows)
+            if headnorm:
+                ref = oracle.head_rmsnorm(ref, 0.8, 1e-5)
+            assert maxerr(out[b, h, rows], ref) <= TOL["fp32"], (D, T, b, h)
+        del x, out
+        torch.cuda.empty_cache()
+
+
 def test_standard_attention_long_causal_rows():
     # head width 128, causal rows beyond 4096 keys: 256-row workgroups
     # (shorter rows take 128-row ones, as in the test above)
