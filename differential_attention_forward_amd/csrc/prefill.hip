@@ -1628,10 +1628,10 @@ long compute_units() {
 hipError_t launch_v2(const FwdArgs& a, int D, bool causal, hipStream_t stream) {
   switch (D) {
     case 64:
-      // Short causal rows: one map per wave, with the first version's rule
-      // for 128- or 192-row workgroups (B2 H16 T4096: 0.223 -> 0.164 ms;
-      // B4 H32 T1024: 0.076 -> 0.068 ms).  Otherwise both maps per wave: K
-      // and V fragments each serve two MFMAs.
+      // Short causal rows: one map per wave, in 128- or 192-row workgroups
+      // by the rule launch_fwd applies to D = 64 causal rows (B2 H16 T4096:
+      // 0.223 -> 0.164 ms; B4 H32 T1024: 0.076 -> 0.068 ms).  Otherwise both
+      // maps per wave: K and V fragments each serve two MFMAs.
       if (causal && a.T <= 4096) {
         const long wg128 = (long)a.B * a.H * ((a.T + 127) / 128);
         const long cus = compute_units();
