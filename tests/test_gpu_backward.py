@@ -262,15 +262,16 @@ def test_bwd_key_gradient_identity_long(D, T):
             assert err <= REL * float(np.max(np.abs(ref))), (h, err)
 
 
-def test_workload_bwd_t4k_causal():
-    """The bench's backward workload (B2 H16 T4096 D64, causal, head norm,
-    lambda_init 0.8) in its launch configuration: dQ1, dQ2 against the oracle
-    on every head, one row of every 128-row q-pass workgroup plus the first
-    and last rows, and the per-map key-gradient identity (sum over keys of
-    dK = 0) on every head."""
-    w = WORKLOADS["bwd_t4k_causal"]
-    x = make_workload("bwd_t4k_causal", DEV)
-    say("workload bwd_t4k_causal: launching")
+@pytest.mark.parametrize("name", ["bwd_t4k_causal", "bwd_t4k_d128"])
+def test_workload_bwd(name):
+    """The bench's backward workloads (B2 H16 T4096 D64 and B2 H8 T4096
+    D128, causal, head norm, lambda_init 0.8) in their launch configuration:
+    dQ1, dQ2 against the oracle on every head, one row of every 128-row
+    q-pass workgroup plus the first and last rows, and the per-map
+    key-gradient identity (sum over keys of dK = 0) on every head."""
+    w = WORKLOADS[name]
+    x = make_workload(name, DEV)
+    say(f"workload {name}: launching")
     _, saved = da.diffattn_fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lam"], causal=True,
                                      headnorm=True, lambda_init=w.lambda_init, eps=w.eps)
     g = da.diffattn_bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lam"], x["dout"], saved, causal=True,
@@ -295,6 +296,6 @@ def test_workload_bwd_t4k_causal():
             for got, ref in ((g[0][b, h, rows], r1), (g[2][b, h, rows], r2)):
                 err = float(np.max(np.abs(_np(got) - ref)))
                 assert err <= REL * float(np.max(np.abs(ref))) + ABS, (b, h, err)
-        say(f"workload bwd_t4k_causal: batch row {b} done")
+        say(f"workload {name}: batch row {b} done")
     del x, g, saved
     torch.cuda.empty_cache()
