@@ -1672,13 +1672,13 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool causal, bool head
         return launch_window<32, 1, 8, 3, false>(a, headnorm, stream);
       }
       case 64: {
-        // Every row sees up to `window` keys, so workgroups carry nearly equal
-        // work: with enough 256-row workgroups to fill the chip twice, both
-        // maps per wave (each V fragment feeds two P.V products) win, 1.1%
-        // at T = 32768, W = 4096, 16 heads over the one-map shape with its
-        // early reads; with few, the finer one-map 128-row workgroups.
-        const long wg256 = (long)a.B * a.H * ((a.T + 255) / 256);
-        if (wg256 >= 2 * compute_units()) return launch_window<64, 1, 8, 3, false>(a, headnorm, stream);
+        // One map per wave.  With at least two 192-row workgroups per compute
+        // unit, three waves per SIMD hide more latency than two (T = 32768,
+        // W = 4096, 16 heads: 1.57 -> 1.50 ms, also 4.9% ahead of both maps
+        // per wave in 256-row workgroups there; T = 8192, W = 1024, 32 heads:
+        // 4.8%); with fewer, the 128-row workgroups with early reads.
+        const long wg192 = (long)a.B * a.H * ((a.T + 191) / 192);
+        if (wg192 >= 2 * compute_units()) return launch_window<64, 1, 12, 3, true>(a, headnorm, stream);
         return launch_window<64, 1, 8, 3, true>(a, headnorm, stream);
       }
       case 128: return launch_window<128, 1, 8, 2, true>(a, headnorm, stream);

@@ -107,12 +107,14 @@ def test_window_attention_v2_poisoned_same_bits(libs):
     a, b = run_both(libs, lambda: da.diffattn_fwd_window(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, 256,
                                                          headnorm=True))
     assert_same(a, b, "window")
-    # D = 32 with enough 192-row workgroups for one map per wave, 12 waves
-    y = dev(prefill_inputs(2, 96, 1100, 32, "bf16", seed=5105))
-    lam96 = torch.full((96,), 0.6, dtype=torch.float32, device=DEV)
-    a, b = run_both(libs, lambda: da.diffattn_fwd_window(y["q1"], y["k1"], y["q2"], y["k2"], y["v"], lam96, 300,
-                                                         headnorm=False))
-    assert_same(a, b, "window D=32")
+    # enough 192-row workgroups for one map per wave, 12 waves (D = 32: four
+    # per compute unit, D = 64: two)
+    for D, H in ((32, 96), (64, 48)):
+        y = dev(prefill_inputs(2, H, 1100, D, "bf16", seed=5105 + D))
+        lamh = torch.full((H,), 0.6, dtype=torch.float32, device=DEV)
+        a, b = run_both(libs, lambda: da.diffattn_fwd_window(y["q1"], y["k1"], y["q2"], y["k2"], y["v"], lamh, 300,
+                                                             headnorm=False))
+        assert_same(a, b, f"window D={D} 12 waves")
     say("poison standard attention")
     for D, causal in ((64, True), (128, True), (128, False)):
         y = dev(prefill_inputs(1, 2, 300, D, "bf16", seed=5102 + D))

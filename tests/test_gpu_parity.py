@@ -568,8 +568,8 @@ def test_fwd_window_sweep(D, headnorm):
 
 
 def test_fwd_window_long_rows():
-    # rows longer than 4096 take the two-maps-per-wave configuration; short
-    # rows over many heads the 192-row one: sampled rows, every key in range
+    # long rows and few heads (the 128-row one-map configuration with early
+    # reads), windows wider than a tile: sampled rows, every key in range
     lam = torch.tensor([0.8, 0.3, -0.1, 1.1], dtype=torch.float32)
     for (B, H, T, W, seed) in ((1, 2, 5000, 700, 41), (2, 4, 3000, 1024, 42)):
         x = prefill_inputs(B, H, T, 64, "bf16", seed=seed)
@@ -588,10 +588,10 @@ def test_fwd_window_long_rows():
 
 @pytest.mark.parametrize("D,H", [(64, 32), (32, 64)])
 def test_fwd_window_many_heads(D, H):
-    # D=64: enough 256-row workgroups (4 x 32 x 4 = 512) for the
-    # two-maps-per-wave window configuration; D=32: enough 192-row ones
-    # (4 x 64 x 6 = 1536) for one map per wave at three waves per SIMD.
-    # Whole heads against the oracle, a ragged T
+    # enough 192-row workgroups for one map per wave at three waves per
+    # SIMD (D=64: 4 x 32 x 6 = 768, at least two per compute unit; D=32:
+    # 4 x 64 x 6 = 1536, at least four).  Whole heads against the oracle, a
+    # ragged T
     B, T, W = 4, 1000, 300
     x = prefill_inputs(B, H, T, D, "bf16", seed=43 + D)
     lam = torch.linspace(-0.2, 1.2, H)
