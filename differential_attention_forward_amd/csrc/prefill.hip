@@ -1651,8 +1651,11 @@ hipError_t launch_attention(const FwdArgs& a, int D, bool causal, hipStream_t st
     case 128:
       // Short causal rows: 128-row workgroups of four waves, two LDS stages
       // (two workgroups per CU) even out the causal triangle (B2 H16 T4096:
-      // 0.189 -> 0.170 ms); longer rows and full attention keep 256 rows.
+      // 0.189 -> 0.170 ms); longer causal rows: 384-row workgroups at three
+      // waves per SIMD (168 registers, 16 bytes of spills; B1 H16 T32768:
+      // 3.92 -> 3.79 ms); full attention: 256 rows, two waves per SIMD.
       if (causal && a.T <= 4096) return launch_std<128, 1, 4, 2>(a, causal, stream);
+      if (causal) return launch_std<128, 1, 12, 3>(a, causal, stream);
       return launch_std<128, 1, 8, 3>(a, causal, stream);
   }
   return hipErrorInvalidValue;

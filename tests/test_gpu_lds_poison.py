@@ -116,10 +116,10 @@ def test_window_attention_v2_poisoned_same_bits(libs):
                                                              headnorm=False))
         assert_same(a, b, f"window D={D} 12 waves")
     say("poison standard attention")
-    for D, causal in ((64, True), (128, True), (128, False)):
-        y = dev(prefill_inputs(1, 2, 300, D, "bf16", seed=5102 + D))
+    for D, causal, T in ((64, True, 300), (128, True, 300), (128, False, 300), (128, True, 4500)):
+        y = dev(prefill_inputs(1, 2, T, D, "bf16", seed=5102 + D))
         a, b = run_both(libs, lambda: da.diffattn_attention_fwd(y["q1"], y["k1"], y["q1"], causal=causal))
-        assert_same(a, b, f"attention D={D} causal={causal}")
+        assert_same(a, b, f"attention D={D} causal={causal} T={T}")
     say("poison V2 prefill and decode")
     for D, causal in ((128, True), (64, True), (64, False)):
         v2 = dev(v2_inputs(1, 8, 2, 500, D, "bf16", seed=5103 + D, lam_uniform=(0.2, 0.8)))

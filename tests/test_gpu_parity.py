@@ -185,8 +185,9 @@ def test_fwd_fp32_many_heads():
 
 
 def test_standard_attention_long_causal_rows():
-    # head width 128, causal rows beyond 4096 keys: 256-row workgroups
-    # (shorter rows take 128-row ones, as in the test above)
+    # head width 128, causal rows beyond 4096 keys: 384-row workgroups at
+    # three waves per SIMD (shorter rows take 128-row ones, as in the test
+    # above)
     T = 4500
     x = attention_inputs(1, 2, T, 128, seed=931)
     say(f"attention bf16 D=128 T={T} causal")
