@@ -169,7 +169,9 @@ __global__ __launch_bounds__(kThreads) void lds_read_kernel(int iters, float* si
 
 // VALU next to an MFMA stream.  Waves 4..7 run `iters` rounds of 32
 // independent VALU operations (KIND 0: fp32 add, 1: v_dot2c_f32_bf16, 2:
-// v_exp_f32); waves 0..3, each on the SIMD of one of them, stream MFMAs for
+// v_exp_f32, 3: v_exp_f32 alternating with fp32 adds, 4: v_exp_f32
+// alternating with v_cvt_pk_bf16_f32: whether the transcendental unit lets
+// ordinary VALU work issue beside it); waves 0..3, each on the SIMD of one of them, stream MFMAs for
 // mfma_iters rounds when mfma_iters > 0 and exit at once otherwise.  One
 // block per CU (96 KiB of LDS declared).  The clock records of waves 4..7
 // give the VALU op's issue interval with and without the MFMA neighbour.
@@ -196,8 +198,16 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(int iters, int mfma_iter
           x[i] = x[i] + y;
         } else if constexpr (KIND == 1) {
           x[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[(i + 7) & 31]), ones, x[i], false);
-        } else {
+        } else if constexpr (KIND == 2) {
           x[i] = __builtin_amdgcn_exp2f(x[i]);
+        } else if constexpr (KIND == 3) {
+          // v_exp_f32 and an independent fp32 add, alternating in issue order
+          if (i % 2 == 0)
+            asm volatile("v_exp_f32 %0, %0\n\tv_add_f32 %1, %1, %2" : "+v"(x[i]), "+v"(x[i + 1]) : "v"(y));
+        } else {
+          // v_exp_f32 and an independent bf16 pair conversion, alternating
+          if (i % 2 == 0)
+            asm volatile("v_exp_f32 %0, %0\n\tv_cvt_pk_bf16_f32 %1, %1, %2" : "+v"(x[i]), "+v"(x[i + 1]) : "v"(y));
         }
       }
       asm volatile("" : "+v"(x[0]), "+v"(x[8]), "+v"(x[16]), "+v"(x[24]));
@@ -273,11 +283,13 @@ int diffattn_micro_lds_read(int transposing, int blocks, int iters, float* sink,
 
 int diffattn_micro_valu(int kind, int mfma_iters, int blocks, int iters, float* sink, size_t sink_elems,
                         unsigned long long* clk, size_t clk_elems, hipStream_t stream) {
-  if (!clk || iters < 1 || mfma_iters < 0 || kind < 0 || kind > 2) return (int)hipErrorInvalidValue;
+  if (!clk || iters < 1 || mfma_iters < 0 || kind < 0 || kind > 4) return (int)hipErrorInvalidValue;
   if (int e = check_out(sink, sink_elems, blocks, kThreads, clk, clk_elems)) return e;
   if (kind == 0) valu_kernel<0><<<blocks, kThreads, 0, stream>>>(iters, mfma_iters, sink, clk);
   if (kind == 1) valu_kernel<1><<<blocks, kThreads, 0, stream>>>(iters, mfma_iters, sink, clk);
   if (kind == 2) valu_kernel<2><<<blocks, kThreads, 0, stream>>>(iters, mfma_iters, sink, clk);
+  if (kind == 3) valu_kernel<3><<<blocks, kThreads, 0, stream>>>(iters, mfma_iters, sink, clk);
+  if (kind == 4) valu_kernel<4><<<blocks, kThreads, 0, stream>>>(iters, mfma_iters, sink, clk);
   return launched();
 }
 

@@ -186,7 +186,8 @@ def lds_read(transposing: bool, iters: int = 20000, reps: int = 3) -> dict:
 
 def valu(kind: int, with_mfma: bool, iters: int = 4000) -> float:
     """Shader clocks per instruction of a VALU wave (kind 0 add, 1 v_dot2c,
-    2 v_exp), alone on its SIMD or next to an MFMA-streaming wave."""
+    2 v_exp, 3 v_exp alternating with adds, 4 v_exp alternating with bf16
+    pair conversions), alone on its SIMD or next to an MFMA-streaming wave."""
     blocks = _cus()
     sink, clk = _bufs(blocks)
     L = lib()
@@ -206,7 +207,7 @@ def run_all() -> dict:
     """Every microbenchmark once (about two seconds on one MI355X)."""
     out = {"mfma_bf16": mfma(), "hbm_read": hbm_read(), "hbm_copy": hbm_copy(), "lds_dma": lds_dma(),
            "lds_read_b128": lds_read(False), "lds_read_tr16": lds_read(True)}
-    names = ("add_f32", "dot2c_f32_bf16", "exp_f32")
+    names = ("add_f32", "dot2c_f32_bf16", "exp_f32", "exp_f32_with_add_f32", "exp_f32_with_cvt_pk_bf16")
     out["valu_clocks_per_op"] = {n: {"alone": valu(k, False), "beside_mfma": valu(k, True)}
                                  for k, n in enumerate(names)}
     torch.cuda.empty_cache()

@@ -60,7 +60,9 @@ int diffattn_micro_lds_read(int transposing, int blocks, int iters, float* sink,
 
 /* VALU issue next to an MFMA stream, one block of 512 threads per CU: waves
  * 4..7 run `iters` rounds of 32 independent operations of kind 0 (fp32 add),
- * 1 (v_dot2c_f32_bf16) or 2 (v_exp_f32); waves 0..3, each sharing a SIMD with
+ * 1 (v_dot2c_f32_bf16), 2 (v_exp_f32), 3 (v_exp_f32 alternating with fp32
+ * adds) or 4 (v_exp_f32 alternating with v_cvt_pk_bf16_f32); kind outside
+ * 0..4 is hipErrorInvalidValue; waves 0..3, each sharing a SIMD with
  * one of them, run the MFMA stream above for mfma_iters rounds (0: they exit
  * at once).  Only waves 4..7 are timed.
  * sink >= blocks*512 floats, clk >= blocks*32 records. */
