@@ -604,8 +604,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(bwd_wav
 
   const int nqt = (T + C::BR - 1) / C::BR;
   const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
-  const int bh = w / nqt;
-  const int qi = w % nqt;
+  int bh, qi;
+  if (CAUSAL) causal_order(w, a.B * a.H * nqt, nqt, bh, qi);
+  else bh = w / nqt, qi = w % nqt;
   const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
   const int h = bh % a.H;
 

@@ -36,6 +36,25 @@ __device__ inline int xcd_remap(int bid, int n) {
   return x * base + (x < rem ? x : rem) + j;
 }
 
+// Causal work order.  Each XCD takes a contiguous range of the logical
+// workgroup ids (xcd_remap); when that range holds whole heads, its query
+// tiles go heaviest first across all of those heads (every head's last tile,
+// then every head's second to last, ...), so that the XCD's compute units
+// start the long causal rows first and finish together.  Otherwise each
+// head's tiles go heaviest first, head after head.
+__device__ inline void causal_order(int w, int n, int nqt, int& bh, int& qi) {
+  const int per = n / kNumXcd;
+  if (n % kNumXcd == 0 && per % nqt == 0) {
+    const int hpx = per / nqt;
+    const int x = w / per, j = w % per;
+    bh = x * hpx + j % hpx;
+    qi = j / hpx;
+  } else {
+    bh = w / nqt;
+    qi = w % nqt;
+  }
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

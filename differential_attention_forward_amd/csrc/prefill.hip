@@ -102,8 +102,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 8
 
   const int nqt = (T + C::BR - 1) / C::BR;
   const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
-  const int bh = w / nqt;
-  const int qi = w % nqt;
+  int bh, qi;
+  if (CAUSAL) causal_order(w, a.B * a.H * nqt, nqt, bh, qi);
+  else bh = w / nqt, qi = w % nqt;
   const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
   const int h = bh % a.H;
 
@@ -509,8 +510,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW < 8 
   // the division by nqt runs on the VALU: say that the results are uniform so
   // that every loop bound and branch derived from them stays scalar
   const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
-  const int bh = __builtin_amdgcn_readfirstlane(w / nqt);
-  const int qi = __builtin_amdgcn_readfirstlane(w % nqt);
+  int bh_, qi_;
+  if (CAUSAL) causal_order(w, a.B * a.H * nqt, nqt, bh_, qi_);
+  else bh_ = w / nqt, qi_ = w % nqt;
+  const int bh = __builtin_amdgcn_readfirstlane(bh_);
+  const int qi = __builtin_amdgcn_readfirstlane(qi_);
   const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
   const int h = bh % a.H;
 
@@ -1138,8 +1142,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int nqt = (T + C::BR - 1) / C::BR;
   const int w = xcd_remap(blockIdx.x, a.B * a.H * nqt);
-  const int bh = __builtin_amdgcn_readfirstlane(w / nqt);
-  const int qi = __builtin_amdgcn_readfirstlane(w % nqt);
+  int bh_, qi_;
+  if (CAUSAL) causal_order(w, a.B * a.H * nqt, nqt, bh_, qi_);
+  else bh_ = w / nqt, qi_ = w % nqt;
+  const int bh = __builtin_amdgcn_readfirstlane(bh_);
+  const int qi = __builtin_amdgcn_readfirstlane(qi_);
   const int qt = CAUSAL ? (nqt - 1 - qi) : qi;  // heaviest causal tiles first
   const int h = bh % a.H;
   const int bb = bh / a.H;
