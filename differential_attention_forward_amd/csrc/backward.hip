@@ -283,8 +283,11 @@ __device__ __forceinline__ void kv_body(const BwdArgs& a, char* smem, int w) {
   const int T = a.T;
 
   const int nkt = (T + C::BK - 1) / C::BK;
-  const int bh = w / nkt;
-  const int kt = w % nkt;  // causal: low key blocks see the most queries, issued first
+  // causal: low key blocks see the most queries, issued first (across all
+  // heads of an XCD's range, as the query-tile passes do)
+  int bh, kt;
+  if (CAUSAL) causal_order(w, a.B * a.H * nkt, nkt, bh, kt);
+  else bh = w / nkt, kt = w % nkt;
   const int h = bh % a.H;
 
   const size_t qk_off = (size_t)bh * T * D;
